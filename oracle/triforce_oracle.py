@@ -1,0 +1,335 @@
+"""fp64 CPU oracle for TriForce's decode-step attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import or run this module.  The product
+path never does: it shares no code with the HIP kernels and imports nothing
+from them, and this module imports nothing from the product package.
+
+Everything is plain numpy in float64, one (sequence, head) at a time.  16-bit
+inputs arrive as raw uint16 bit patterns and are widened exactly here.
+
+Sources (web pages, cited by title and section):
+  [blog]  aifetchly, "TriForce: Hierarchical Speculative Decoding for LLMs":
+          "1. The Three Forces of TriForce" (Force 1 streaming drafter with
+          sinks + W = 256 recent tokens; Force 2 retrieval of the top-k KV
+          blocks by key-query similarity under a token budget; Force 3 full
+          cache verification) and "2. Dual Rejection Sampling: Mathematical
+          Losslessness" (acceptance alpha = min(1, p/q) >= u, residual
+          max(0, p - q) / sum max(0, p - q)).
+  [abs]   mlsanity / fugumt pages for arXiv 2404.11912, "Abstract": the whole
+          KV cache is loaded for every generated token; a dynamic sparse KV
+          cache via retrieval serves as draft; robustness across temperatures.
+
+Readings where the pages are silent (each one repeated at its function):
+  chunk keys are the arithmetic mean of a chunk's keys; scores are unscaled
+  dot products summed over the query heads of a KV group; selection is per
+  (sequence, KV head) with ties to the lowest chunk index, output ascending,
+  -1 padded; a row with no visible key yields o = 0 and lse = -inf; verify
+  rows are bottom-right aligned (row i of Q sees keys j <= n - Q + i); the
+  accept test is alpha = min(1, p/q) >= u with p(x) = 0 always rejecting,
+  residual or bonus drawn by inverse CDF with one extra uniform; T = 0 is
+  greedy (one-hot at the lowest-index argmax).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ---------------------------------------------------------------------------
+# Widening of stored values
+# ---------------------------------------------------------------------------
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """uint16 bit patterns of fp16 / bf16 -> exact float64 values."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "fp32":
+        return np.asarray(bits).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def round_f64_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values once, to nearest with ties to even, to fp16 / bf16
+    and return the uint16 bit patterns.  States what a stored chunk key must
+    be.  bf16: keep 8 significant bits of the frexp mantissa with np.rint
+    (round half to even); values stay in the normal range here."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)  # numpy rounds f64 -> f16 directly
+    if dtype == "bf16":
+        m, e = np.frexp(x)
+        r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # exactly a bf16 value
+        return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# a1  Chunk-mean keys
+# ---------------------------------------------------------------------------
+
+def chunk_keys(K: np.ndarray, n: int, chunk_size: int) -> np.ndarray:
+    """Per-chunk mean of the keys: one summary key per block of `chunk_size`
+    consecutive positions, the last block averaged over the positions present.
+
+    [blog] "1. The Three Forces of TriForce", Force 2: retrieval works on KV
+    blocks matched by key-query similarity.  Reading: a block is summarised by
+    the arithmetic mean of its keys.
+    K: float64 [>= n][d].  Returns float64 [ceil(n / chunk_size)][d]."""
+    C = -(-n // chunk_size) if n > 0 else 0
+    out = np.zeros((C, K.shape[1]), np.float64)
+    for c in range(C):
+        lo, hi = c * chunk_size, min(n, (c + 1) * chunk_size)
+        out[c] = K[lo:hi].sum(axis=0) / (hi - lo)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a2  Query-to-chunk scores
+# ---------------------------------------------------------------------------
+
+def chunk_scores(q_group: np.ndarray, ck: np.ndarray) -> np.ndarray:
+    """s_c = sum over the query heads h of the group of q_h . kbar_c.
+
+    [blog] Force 2: "Key-Query similarity matching".  Reading: the plain dot
+    product, unscaled (no 1/sqrt(d): it would only rescale the ranking), summed
+    over the query heads that share the KV head (with one head per KV head this
+    is just q . kbar).  q_group: float64 [G][d]; ck: float64 [C][d]."""
+    C = ck.shape[0]
+    s = np.zeros(C, np.float64)
+    for h in range(q_group.shape[0]):
+        s += ck @ q_group[h]
+    return s
+
+
+# ---------------------------------------------------------------------------
+# a3  Top-k chunk selection under a token budget
+# ---------------------------------------------------------------------------
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """The k highest-scoring chunks of one (sequence, KV head) row.
+
+    [blog] Force 2: a small subset of the most critical KV blocks is chosen
+    ("top k = 2,048 tokens out of 128k").  Readings: k = budget // chunk_size
+    chunks; ties go to the lower chunk index; NaN counts as -inf and -0.0 as
+    +0.0; the result is sorted ascending and padded with -1 when the row has
+    fewer than k chunks.  Returns int64 [k]."""
+    s = np.array(scores, dtype=np.float64)
+    s[np.isnan(s)] = NEG_INF
+    s = s + 0.0  # -0.0 -> +0.0
+    C = s.shape[0]
+    order = np.lexsort((np.arange(C), -s))  # by score descending, then index
+    take = np.sort(order[:min(k, C)])
+    out = np.full(k, -1, np.int64)
+    out[:take.shape[0]] = take
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Attention over a set of keys: the plain definition
+# ---------------------------------------------------------------------------
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> Tuple[np.ndarray, float]:
+    """o = sum_t softmax_t(q . K_t / sqrt(d)) V_t and lse = log sum_t exp(q . K_t / sqrt(d)).
+
+    Scaled dot-product attention of one query over the given key/value rows.
+    Reading: with no keys, o = 0 and lse = -inf.  q: [d]; K, V: [m][d]."""
+    d = q.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros(d, np.float64), NEG_INF
+    logits = (K @ q) / math.sqrt(d)
+    m = logits.max()
+    w = np.exp(logits - m)
+    z = w.sum()
+    return (w @ V) / z, float(m + math.log(z))
+
+
+# ---------------------------------------------------------------------------
+# a4  Attention over the gathered chunks
+# ---------------------------------------------------------------------------
+
+def sparse_token_positions(idx: Sequence[int], chunk_size: int, n: int) -> np.ndarray:
+    """Positions covered by the selected chunks (index -1 skipped, positions
+    at or beyond n dropped)."""
+    pos: List[int] = []
+    for c in idx:
+        c = int(c)
+        if c < 0:
+            continue
+        pos.extend(t for t in range(c * chunk_size, (c + 1) * chunk_size) if t < n)
+    return np.asarray(pos, np.int64)
+
+
+def sparse_attn(q: np.ndarray, K: np.ndarray, V: np.ndarray, n: int,
+                idx: Sequence[int], chunk_size: int) -> Tuple[np.ndarray, float]:
+    """Attention of the draft query over the retrieved blocks only.
+
+    [blog] Force 2: the target model runs on a retrieval-sparse KV cache made
+    of the selected blocks; [abs]: dynamic sparse KV cache via retrieval as a
+    draft.  Reading: only the gathered positions are attended (no extra
+    recent-token tail)."""
+    pos = sparse_token_positions(idx, chunk_size, n)
+    return attention(q, K[pos], V[pos])
+
+
+# ---------------------------------------------------------------------------
+# a5  Sink + window streaming attention
+# ---------------------------------------------------------------------------
+
+def stream_positions(n: int, n_sink: int, window: int) -> np.ndarray:
+    """Visible positions of a streaming cache after n tokens: the first
+    n_sink positions and the most recent `window` ones (which include n - 1).
+
+    [blog] Force 1: the drafter keeps the initial prompt sinks plus the most
+    recent W tokens (W = 256), as in StreamingLLM."""
+    sinks = list(range(min(n_sink, n)))
+    recent = list(range(max(n_sink, n - window), n))
+    return np.asarray(sinks + recent, np.int64)
+
+
+def stream_attn_masked(q: np.ndarray, K_log: np.ndarray, V_log: np.ndarray, n: int,
+                       n_sink: int, window: int) -> Tuple[np.ndarray, float]:
+    """Streaming attention as full attention over the logical sequence with a
+    sink/window mask."""
+    pos = stream_positions(n, n_sink, window)
+    return attention(q, K_log[pos], V_log[pos])
+
+
+def stream_attn_ring(q: np.ndarray, K_log: np.ndarray, V_log: np.ndarray, n: int,
+                     n_sink: int, window: int) -> Tuple[np.ndarray, float]:
+    """The same quantity computed the other way: replay the n appends into a
+    cache of n_sink sink slots plus a window of `window` slots that evicts
+    its oldest entry, then attend over whatever the cache holds."""
+    sink_rows: List[int] = []
+    ring: List[int] = []
+    for p in range(n):
+        if len(sink_rows) < n_sink:
+            sink_rows.append(p)
+        else:
+            ring.append(p)
+            if len(ring) > window:
+                ring.pop(0)
+    held = np.asarray(sink_rows + ring, np.int64)
+    return attention(q, K_log[held], V_log[held])
+
+
+# ---------------------------------------------------------------------------
+# a6  Full-cache multi-query verification
+# ---------------------------------------------------------------------------
+
+def verify_attn(qs: np.ndarray, K: np.ndarray, V: np.ndarray, n: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of the Q = gamma + 1 verification queries over the full cache.
+
+    [blog] Force 3: the target with the complete cache checks all candidates
+    in one parallel pass; [abs]: the whole KV cache is loaded for every
+    generated token.  Reading (chain form): the last Q cache rows are the
+    draft positions themselves, so query row i sees keys j <= n - Q + i.
+    qs: [Q][d]; K, V: [>= n][d].  Returns o [Q][d], lse [Q]."""
+    Q, d = qs.shape
+    o = np.zeros((Q, d), np.float64)
+    lse = np.zeros(Q, np.float64)
+    for i in range(Q):
+        vis = n - Q + i + 1
+        vis = max(0, min(vis, n))
+        o[i], lse[i] = attention(qs[i], K[:vis], V[:vis])
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# a7  Lossless accept / reject
+# ---------------------------------------------------------------------------
+
+def distribution(logits: np.ndarray, temperature: float, probs: bool = False) -> np.ndarray:
+    """Token distribution of one row: softmax(logits / T) for T > 0; for T = 0
+    a one-hot at the lowest-index argmax (greedy).  With probs=True the row
+    already holds probabilities and is used as given.
+
+    [abs]: speedups hold across sampling temperatures.  Reading: temperature
+    divides the logits before the softmax."""
+    x = np.asarray(logits, dtype=np.float64)
+    if probs:
+        return x.copy()
+    if temperature == 0.0:
+        out = np.zeros_like(x)
+        out[int(np.argmax(x))] = 1.0  # np.argmax returns the first maximum
+        return out
+    z = x / float(temperature)
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+def inverse_cdf(r: np.ndarray, u: float) -> int:
+    """Draw from the (unnormalised, non-negative) weights r with one uniform:
+    the smallest t whose running sum exceeds u * sum(r), strictly; clamped to
+    the last t with r_t > 0 (guards the rounding of the running sum)."""
+    total = float(r.sum())
+    target = u * total
+    run = 0.0
+    last_pos = -1
+    for t in range(r.shape[0]):
+        if r[t] > 0.0:
+            last_pos = t
+        run += r[t]
+        if run > target:
+            return t
+    return last_pos
+
+
+def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniforms: Sequence[float],
+           temperature: float, probs: bool = False) -> Tuple[int, int, float]:
+    """One sequence's speculative accept/reject over gamma drafted tokens.
+
+    [blog] "2. Dual Rejection Sampling": a drafted token x is kept when
+    alpha = min(1, p(x) / q(x)) >= u, u ~ U(0, 1); at the first rejection the
+    next token is drawn from max(0, p - q) / sum_v max(0, p(v) - q(v)).
+    Readings: p(x) = 0 always rejects (and q(x) = 0 < p(x) accepts, alpha = 1);
+    if every draft is kept a bonus token is drawn from the target row gamma;
+    the draw is by inverse CDF with the extra uniform u[gamma]; a residual
+    that sums to 0 (only through rounding) falls back to p.
+
+    target: [gamma+1][V] logits (or probabilities), draft: [gamma][V],
+    tokens: [gamma], uniforms: [gamma+1].  Returns (n_accepted, next_token,
+    margin) where margin is the smallest distance of any decision taken to its
+    threshold (used by tests to skip rounding-level ties)."""
+    gamma = len(tokens)
+    margin = math.inf
+    j = gamma
+    for i in range(gamma):
+        p = distribution(target[i], temperature, probs)
+        q = distribution(draft[i], temperature, probs)
+        x = int(tokens[i])
+        px, qx = float(p[x]), float(q[x])
+        if px > 0.0:
+            alpha = 1.0 if qx == 0.0 else min(1.0, px / qx)
+            margin = min(margin, abs(alpha - float(uniforms[i])))
+            if alpha >= float(uniforms[i]):
+                continue
+        j = i
+        break
+    if j < gamma:
+        p = distribution(target[j], temperature, probs)
+        q = distribution(draft[j], temperature, probs)
+        r = np.maximum(0.0, p - q)
+        if r.sum() == 0.0:
+            r = p
+    else:
+        r = distribution(target[gamma], temperature, probs)
+    u = float(uniforms[gamma])
+    nxt = inverse_cdf(r, u)
+    # Margin of the inverse-CDF decision: distance of u*Z to the running sums
+    # that bracket the chosen token.
+    cs = np.cumsum(r)
+    tgt = u * float(r.sum())
+    if nxt >= 0:
+        lo = cs[nxt - 1] if nxt > 0 else 0.0
+        margin = min(margin, abs(cs[nxt] - tgt), abs(tgt - lo))
+    return j, nxt, margin

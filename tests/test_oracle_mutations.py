@@ -1,0 +1,108 @@
+"""The pins must catch plausible mistakes.  Each case plants one mistake in a
+copy of an oracle function (CPU only), runs the pin that should notice it,
+and expects that pin to fail."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.triforce_oracle as T
+import tests.test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(T, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def verify_off_by_one(qs, K, V, n):
+    Q, d = qs.shape
+    o, lse = np.zeros((Q, d)), np.zeros(Q)
+    for i in range(Q):
+        vis = max(0, min(n - Q + i, n))        # mistake: drops the + 1
+        o[i], lse[i] = T.attention(qs[i], K[:vis], V[:vis])
+    return o, lse
+
+
+def attention_unscaled(q, K, V):
+    if K.shape[0] == 0:
+        return np.zeros(q.shape[0]), -math.inf
+    logits = K @ q                              # mistake: no 1/sqrt(d)
+    w = np.exp(logits - logits.max())
+    return (w @ V) / w.sum(), float(logits.max() + math.log(w.sum()))
+
+
+def chunk_keys_fixed_divisor(K, n, cs):
+    C = -(-n // cs) if n > 0 else 0
+    out = np.zeros((C, K.shape[1]))
+    for c in range(C):
+        lo, hi = c * cs, min(n, (c + 1) * cs)
+        out[c] = K[lo:hi].sum(axis=0) / cs     # mistake: partial chunk divided by cs
+    return out
+
+
+def topk_ties_high_index(scores, k):
+    s = np.array(scores, np.float64)
+    s[np.isnan(s)] = -np.inf
+    C = len(s)
+    order = np.lexsort((-np.arange(C), -s))   # mistake: ties to the higher index
+    take = np.sort(order[:min(k, C)])
+    out = np.full(k, -1, np.int64)
+    out[:len(take)] = take
+    return out
+
+
+def stream_positions_short(n, S, W):
+    return np.asarray(list(range(min(S, n))) + list(range(max(S, n - W + 1), n)), np.int64)  # mistake: W - 1 recent
+
+
+def accept_flipped_residual(target, draft, tokens, uniforms, temperature, probs=False):
+    gamma = len(tokens)
+    j = gamma
+    for i in range(gamma):
+        p = T.distribution(target[i], temperature, probs)
+        q = T.distribution(draft[i], temperature, probs)
+        x = int(tokens[i])
+        if p[x] > 0 and (q[x] == 0 or min(1.0, p[x] / q[x]) >= uniforms[i]):
+            continue
+        j = i
+        break
+    if j < gamma:
+        r = np.maximum(0.0, T.distribution(draft[j], temperature, probs) - T.distribution(target[j], temperature, probs))  # mistake: q - p
+        if r.sum() == 0:
+            r = T.distribution(target[j], temperature, probs)
+    else:
+        r = T.distribution(target[gamma], temperature, probs)
+    return j, T.inverse_cdf(r, float(uniforms[gamma])), 1.0
+
+
+def accept_no_bonus(target, draft, tokens, uniforms, temperature, probs=False):
+    j, nxt, m = T.accept.__wrapped__(target, draft, tokens, uniforms, temperature, probs) \
+        if hasattr(T.accept, "__wrapped__") else ORIG_ACCEPT(target, draft, tokens, uniforms, temperature, probs)
+    if j == len(tokens):
+        nxt = int(np.argmax(T.distribution(draft[-1], temperature, probs)))  # mistake: bonus from the draft row
+    return j, nxt, m
+
+
+ORIG_ACCEPT = T.accept
+
+
+CASES = [
+    ("verify_attn", verify_off_by_one, pins.test_verify_rows_are_prefix_attention),
+    ("verify_attn", verify_off_by_one, pins.test_verify_alignment_closed_form),
+    ("attention", attention_unscaled, pins.test_attention_matches_library_sdpa_and_logsumexp),
+    ("chunk_keys", chunk_keys_fixed_divisor, lambda: pins.test_chunk_keys_ramp_closed_form(67, 8)),
+    ("select_topk", topk_ties_high_index, pins.test_topk_exhaustive_tie_patterns),
+    ("stream_positions", stream_positions_short, lambda: pins.test_stream_ring_equals_mask_and_library(1000, 4, 252)),
+    ("accept", accept_flipped_residual, pins.test_accept_hand_examples),
+    ("accept", accept_no_bonus, pins.test_accept_hand_examples),
+]
+
+
+@pytest.mark.parametrize("name,bad,pin", CASES, ids=[f"{c[0]}-{c[1].__name__}" for c in CASES])
+def test_pin_catches_planted_mistake(monkeypatch, name, bad, pin):
+    _patch(monkeypatch, name, bad)
+    with pytest.raises(AssertionError):
+        pin()
