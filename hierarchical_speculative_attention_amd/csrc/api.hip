@@ -1,0 +1,354 @@
+// C ABI of libtfattn (declared in include/tf_attn.h): host-side validation,
+// split planning and kernel launches.  Nothing is enqueued unless every
+// argument check passes.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "tf_internal.h"
+
+#define TF_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_detail[0] = '\0';
+  return TF_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is16(int dt) { return dt == TF_DTYPE_FP16 || dt == TF_DTYPE_BF16; }
+
+// Checks shared by every cache descriptor.
+int check_desc(const tf_kv_desc* kv, const char* name, bool allow_fp32) {
+  if (!kv) return fail(TF_ERR_INVALID_ARG, "%s is NULL", name);
+  if (kv->B < 0 || kv->H < 1 || kv->max_len < 0)
+    return fail(TF_ERR_INVALID_ARG, "%s: B=%d H=%d max_len=%d out of range", name, kv->B, kv->H, kv->max_len);
+  if (kv->d != tfk::kHeadDim) return fail(TF_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", name, kv->d);
+  if (!(is16(kv->dtype) || (allow_fp32 && kv->dtype == TF_DTYPE_FP32)))
+    return fail(allow_fp32 ? TF_ERR_INVALID_ARG : TF_ERR_UNSUPPORTED, "%s: dtype %d not supported", name, kv->dtype);
+  if (kv->B > 0 && (!kv->seq_base || !kv->seq_cap || !kv->seq_len))
+    return fail(TF_ERR_INVALID_ARG, "%s: seq_base/seq_cap/seq_len must be device arrays", name);
+  if (kv->B > 65535 || kv->H > 65535) return fail(TF_ERR_UNSUPPORTED, "%s: B or H above 65535", name);
+  return TF_OK;
+}
+
+int check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(TF_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(TF_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return TF_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return TF_OK;
+  if (!ws) return fail(TF_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(ws, 256)) return fail(TF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (have < need) return fail(TF_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return TF_OK;
+}
+
+#define TRY(x)              \
+  do {                      \
+    const int _s = (x);     \
+    if (_s != TF_OK) return _s; \
+  } while (0)
+
+// Target number of workgroups per launch: a few per compute unit.
+constexpr int kVerifyTargetWgs = 1024;
+constexpr int kSparseTargetWgs = 1024;
+
+void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, const tf_kv_desc* kv, int Hq, int Qn,
+                 float* out, float* lse) {
+  a.q = (const uint16_t*)q;
+  a.K = (const uint16_t*)K;
+  a.V = (const uint16_t*)V;
+  a.seq_base = kv->seq_base;
+  a.seq_cap = kv->seq_cap;
+  a.seq_len = kv->seq_len;
+  a.max_len = kv->max_len;
+  a.B = kv->B;
+  a.Hq = Hq;
+  a.Hkv = kv->H;
+  a.G = Hq / kv->H;
+  a.Qn = Qn;
+  a.rows = a.G * Qn;
+  a.idx = nullptr;
+  a.k = 0;
+  a.cs = 1;
+  a.n_sink = 0;
+  a.window = 0;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.counters = nullptr;
+  a.scale_ln = 1.0f / std::sqrt((float)tfk::kHeadDim);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)tfk::kHeadDim));
+}
+
+void fill_plan(tfk::AttnArgs& a, const tfk::SplitPlan& p, void* ws) {
+  a.tpw = p.tpw;
+  a.nsplit = p.nsplit;
+  a.rows_pad = p.rows_pad;
+  if (p.total_bytes) {
+    char* w = (char*)ws;
+    a.counters = (int32_t*)w;
+    a.part_ml = (float*)(w + p.counter_bytes);
+    a.part_o = (float*)(w + p.counter_bytes + p.part_ml_bytes);
+  }
+}
+
+}  // namespace
+
+TF_EXPORT const char* tf_status_string(int status) {
+  switch (status) {
+    case TF_OK: return "TF_OK";
+    case TF_ERR_INVALID_ARG: return "TF_ERR_INVALID_ARG";
+    case TF_ERR_UNSUPPORTED: return "TF_ERR_UNSUPPORTED";
+    case TF_ERR_WORKSPACE: return "TF_ERR_WORKSPACE";
+    case TF_ERR_HIP: return "TF_ERR_HIP";
+  }
+  return "TF_ERR_UNKNOWN";
+}
+
+TF_EXPORT const char* tf_last_error_detail(void) { return g_detail; }
+
+TF_EXPORT int tf_workspace_clear(void* ws, size_t ws_bytes, tf_stream_t stream) {
+  if (ws_bytes == 0) return ok();
+  TRY(check_ptr(ws, "ws", 16));
+  return check_hip(tfk::launch_clear(ws, ws_bytes, (hipStream_t)stream), "tf_workspace_clear");
+}
+
+// ---------------------------------------------------------------------------
+// a1
+// ---------------------------------------------------------------------------
+TF_EXPORT int tf_build_chunk_keys(const void* K, const tf_kv_desc* kv, int32_t chunk_size,
+                                  const int32_t* chunk_begin, int32_t max_chunks, void* ck,
+                                  const tf_kv_desc* ckd, tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  TRY(check_desc(ckd, "ckd", true));
+  if (ckd->B != kv->B || ckd->H != kv->H) return fail(TF_ERR_INVALID_ARG, "ckd B/H differ from kv");
+  if (ckd->dtype != TF_DTYPE_FP32 && ckd->dtype != kv->dtype)
+    return fail(TF_ERR_INVALID_ARG, "chunk keys are stored in the K dtype or fp32");
+  if (chunk_size < 1 || chunk_size > 4096) return fail(TF_ERR_INVALID_ARG, "chunk_size %d out of [1, 4096]", chunk_size);
+  if (max_chunks < 1) return fail(TF_ERR_INVALID_ARG, "max_chunks must be >= 1");
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(ck, "ck", 16));
+  if (chunk_begin) TRY(check_ptr(chunk_begin, "chunk_begin", 4));
+  if ((max_chunks + 15) / 16 > 0x7fffffff) return fail(TF_ERR_UNSUPPORTED, "max_chunks too large");
+  return check_hip(tfk::launch_chunk_keys((const uint16_t*)K, *kv, chunk_size, chunk_begin, max_chunks, ck, *ckd,
+                                          (hipStream_t)stream),
+                   "tf_build_chunk_keys");
+}
+
+// ---------------------------------------------------------------------------
+// a2
+// ---------------------------------------------------------------------------
+TF_EXPORT int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq, const void* ck, const tf_kv_desc* ckd,
+                              float* scores, int32_t c_max, tf_stream_t stream) {
+  TRY(check_desc(ckd, "ckd", true));
+  if (!is16(q_dtype)) return fail(TF_ERR_UNSUPPORTED, "q dtype %d not supported", q_dtype);
+  if (ckd->dtype != TF_DTYPE_FP32 && ckd->dtype != q_dtype)
+    return fail(TF_ERR_INVALID_ARG, "16-bit chunk keys must share the query dtype");
+  if (Hq < 1 || Hq % ckd->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, ckd->H);
+  if (c_max < 1) return fail(TF_ERR_INVALID_ARG, "c_max must be >= 1");
+  if (ckd->max_len > c_max) return fail(TF_ERR_INVALID_ARG, "ckd->max_len %d exceeds c_max %d", ckd->max_len, c_max);
+  if (ckd->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(ck, "ck", 16));
+  TRY(check_ptr(scores, "scores", 4));
+  return check_hip(tfk::launch_scores((const uint16_t*)q, q_dtype, Hq, ck, *ckd, scores, c_max, (hipStream_t)stream),
+                   "tf_score_chunks");
+}
+
+// ---------------------------------------------------------------------------
+// a3
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_select_topk_workspace_size(int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+TF_EXPORT int tf_select_topk(const float* scores, int32_t B, int32_t rows_per_seq, int32_t c_max,
+                             const int32_t* n_chunks, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                             tf_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (B < 0 || rows_per_seq < 1 || c_max < 1 || k < 1)
+    return fail(TF_ERR_INVALID_ARG, "B=%d rows=%d c_max=%d k=%d out of range", B, rows_per_seq, c_max, k);
+  if (c_max > (1 << 20)) return fail(TF_ERR_UNSUPPORTED, "c_max %d above 1<<20", c_max);
+  if (B > 65535) return fail(TF_ERR_UNSUPPORTED, "B above 65535");
+  if (B == 0) return ok();
+  TRY(check_ptr(scores, "scores", 4));
+  TRY(check_ptr(n_chunks, "n_chunks", 4));
+  TRY(check_ptr(idx, "idx", 4));
+  return check_hip(tfk::launch_topk(scores, B, rows_per_seq, c_max, n_chunks, k, idx, (hipStream_t)stream),
+                   "tf_select_topk");
+}
+
+// ---------------------------------------------------------------------------
+// a4
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_sparse_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t k, int32_t chunk_size) {
+  if (B < 1 || H < 1 || Hq < 1 || k < 1 || chunk_size < 1) return 0;
+  const long virt = (long)k * chunk_size;
+  if (virt > 0x7fffffffL) return 0;
+  return tfk::plan_splits(B, H, Hq / H, (int32_t)virt, kSparseTargetWgs).total_bytes;
+}
+
+TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const void* V, const tf_kv_desc* kv,
+                             const int32_t* idx, int32_t k, int32_t chunk_size, float* out, float* lse, void* ws,
+                             size_t ws_bytes, tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (Hq < 1 || Hq % kv->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, kv->H);
+  if (Hq / kv->H > tfk::kMaxRows) return fail(TF_ERR_UNSUPPORTED, "more than %d query heads per KV head", tfk::kMaxRows);
+  if (k < 1 || chunk_size < 1 || chunk_size > 4096) return fail(TF_ERR_INVALID_ARG, "k=%d chunk_size=%d", k, chunk_size);
+  if ((long)k * chunk_size > 0x7fffffffL) return fail(TF_ERR_UNSUPPORTED, "k * chunk_size too large");
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  TRY(check_ptr(idx, "idx", 4));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, Hq / kv->H, k * chunk_size, kSparseTargetWgs);
+  TRY(check_ws(ws, ws_bytes, plan.total_bytes));
+  tfk::AttnArgs a;
+  fill_common(a, q, K, V, kv, Hq, 1, out, lse);
+  a.idx = idx;
+  a.k = k;
+  a.cs = chunk_size;
+  fill_plan(a, plan, ws);
+  return check_hip(tfk::launch_attn(kv->dtype, tfk::kSparse, a, (hipStream_t)stream), "tf_sparse_attn");
+}
+
+// ---------------------------------------------------------------------------
+// a5
+// ---------------------------------------------------------------------------
+TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const void* Vs, const tf_kv_desc* sd,
+                             int32_t n_sink, int32_t window, float* out, float* lse, tf_stream_t stream) {
+  TRY(check_desc(sd, "sd", false));
+  if (Hq < 1 || Hq % sd->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, sd->H);
+  if (Hq / sd->H > tfk::kMaxRows) return fail(TF_ERR_UNSUPPORTED, "more than %d query heads per KV head", tfk::kMaxRows);
+  if (n_sink < 0 || window < 0 || (long)n_sink + window > (1L << 24))
+    return fail(TF_ERR_INVALID_ARG, "n_sink=%d window=%d out of range", n_sink, window);
+  if (sd->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(Ks, "Ks", 16));
+  TRY(check_ptr(Vs, "Vs", 16));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  tfk::AttnArgs a;
+  fill_common(a, q, Ks, Vs, sd, Hq, 1, out, lse);
+  a.n_sink = n_sink;
+  a.window = window;
+  // One workgroup per (sequence, head): every visible position in one split.
+  tfk::SplitPlan plan;
+  plan.tpw = ((n_sink + window + 127) / 128) * 128;
+  if (plan.tpw < 128) plan.tpw = 128;
+  plan.nsplit = 1;
+  plan.rows_pad = ((a.rows + 15) / 16) * 16;
+  plan.part_o_bytes = plan.part_ml_bytes = plan.counter_bytes = plan.total_bytes = 0;
+  fill_plan(a, plan, nullptr);
+  return check_hip(tfk::launch_attn(sd->dtype, tfk::kStream, a, (hipStream_t)stream), "tf_stream_attn");
+}
+
+// ---------------------------------------------------------------------------
+// a6
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len) {
+  if (B < 1 || H < 1 || Hq < 1 || Q < 1 || max_len < 0) return 0;
+  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs).total_bytes;
+}
+
+TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                             const tf_kv_desc* kv, float* out, float* lse, void* ws, size_t ws_bytes,
+                             tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (Hq < 1 || Hq % kv->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, kv->H);
+  if (Q < 1) return fail(TF_ERR_INVALID_ARG, "Q must be >= 1");
+  if ((long)(Hq / kv->H) * Q > tfk::kMaxRows)
+    return fail(TF_ERR_UNSUPPORTED, "G*Q = %ld query rows per KV head (at most %d)", (long)(Hq / kv->H) * Q,
+                tfk::kMaxRows);
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs);
+  TRY(check_ws(ws, ws_bytes, plan.total_bytes));
+  tfk::AttnArgs a;
+  fill_common(a, q, K, V, kv, Hq, Q, out, lse);
+  fill_plan(a, plan, ws);
+  return check_hip(tfk::launch_attn(kv->dtype, tfk::kVerify, a, (hipStream_t)stream), "tf_verify_attn");
+}
+
+// ---------------------------------------------------------------------------
+// a7
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_accept_workspace_size(int32_t B, int32_t gamma, int32_t V) {
+  return tfk::accept_ws_bytes(B, gamma, V);
+}
+
+TF_EXPORT int tf_accept(const float* target, const float* draft, const int32_t* draft_tokens,
+                        const double* uniforms, int32_t B, int32_t gamma, int32_t V, float temperature,
+                        int32_t flags, int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes,
+                        tf_stream_t stream) {
+  if (B < 0 || gamma < 0 || V < 1) return fail(TF_ERR_INVALID_ARG, "B=%d gamma=%d V=%d out of range", B, gamma, V);
+  if (!(temperature >= 0.f) || std::isinf(temperature))
+    return fail(TF_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (flags & ~TF_ACCEPT_PROBS) return fail(TF_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B > 0x7fffffff / 2) return fail(TF_ERR_UNSUPPORTED, "B too large");
+  if (B == 0) return ok();
+  TRY(check_ptr(target, "target", 4));
+  if (gamma > 0) {
+    TRY(check_ptr(draft, "draft", 4));
+    TRY(check_ptr(draft_tokens, "draft_tokens", 4));
+  }
+  TRY(check_ptr(uniforms, "uniforms", 8));
+  TRY(check_ptr(n_accepted, "n_accepted", 4));
+  TRY(check_ptr(next_token, "next_token", 4));
+  TRY(check_ws(ws, ws_bytes, tfk::accept_ws_bytes(B, gamma, V)));
+  return check_hip(tfk::launch_accept(target, draft, draft_tokens, uniforms, B, gamma, V, temperature, flags,
+                                      n_accepted, next_token, ws, (hipStream_t)stream),
+                   "tf_accept");
+}
+
+// ---------------------------------------------------------------------------
+// workspace clear: a fill kernel (no memset node, safe under graph capture)
+// ---------------------------------------------------------------------------
+namespace tfk {
+
+__global__ void clear_kernel(uint32_t* p, size_t n_words, unsigned char* tail, size_t n_tail) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t j = i; j < n_words; j += stride) p[j] = 0u;
+  if (i < n_tail) tail[i] = 0;
+}
+
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4, tail = bytes % 4;
+  size_t blocks = (words + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t*)ws, words,
+                     (unsigned char*)ws + words * 4, tail);
+  return hipGetLastError();
+}
+
+}  // namespace tfk

@@ -1,0 +1,184 @@
+// Chunk-mean keys and query-to-chunk scores: the retrieval side of Force 2
+// in the TriForce blog ("1. The Three Forces of TriForce": the target picks
+// the most critical KV blocks by key-query similarity).  A block is
+// summarised by the mean of its keys; the score of a block is the dot product
+// of that mean with the draft query (summed over the query heads sharing the
+// KV head).  Both kernels stream HBM once with 16-byte loads: 16 lanes cover
+// one 256-byte row of 128 16-bit values.
+#include "tf_internal.h"
+
+namespace tfk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void widen8(int dtype, u32x4 x, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned w = x[i];
+    if (dtype == TF_DTYPE_BF16) {
+      f[2 * i] = __uint_as_float(w << 16);
+      f[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      f[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned pack2(int dtype, float lo, float hi) {
+  unsigned short a, b;
+  if (dtype == TF_DTYPE_BF16) {
+    a = __builtin_bit_cast(unsigned short, (__bf16)lo);
+    b = __builtin_bit_cast(unsigned short, (__bf16)hi);
+  } else {
+    a = __builtin_bit_cast(unsigned short, (_Float16)lo);
+    b = __builtin_bit_cast(unsigned short, (_Float16)hi);
+  }
+  return (unsigned)a | ((unsigned)b << 16);
+}
+
+// ---------------------------------------------------------------------------
+// a1: grid (ceil(max_chunks / 16), H, B); 16 lanes per chunk, 8 dims per lane.
+// ---------------------------------------------------------------------------
+template <int IN_DT>
+__global__ __launch_bounds__(256) void chunk_keys_kernel(
+    const uint16_t* __restrict__ K, const int64_t* __restrict__ kbase, const int32_t* __restrict__ kcap,
+    const int32_t* __restrict__ klen, int32_t max_len, int32_t cs, const int32_t* __restrict__ chunk_begin,
+    int32_t max_chunks, void* __restrict__ ck, const int64_t* __restrict__ cbase,
+    const int32_t* __restrict__ ccap, int32_t out_dtype) {
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int cap = kcap[b];
+  const int n = min(max(klen[b], 0), min(cap, max_len));
+  const int C = (n + cs - 1) / cs;
+  const long cb = chunk_begin ? max(chunk_begin[b], 0) : 0;
+  const long c_end = min((long)C, cb + max_chunks);
+  const long cl = cb + (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  if (cl >= c_end || cl >= ccap[b]) return;
+  const int c = (int)cl;
+  const int lo = c * cs, hi = min(n, lo + cs);
+  const uint16_t* src = K + kbase[b] + ((size_t)g * cap + lo) * kHeadDim + 8 * part;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < hi - lo; ++t) {
+    float f[8];
+    widen8(IN_DT, *(const u32x4*)(src + (size_t)t * kHeadDim), f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] += f[j];
+  }
+  const float cnt = (float)(hi - lo);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = s[j] / cnt;
+  const size_t orow = (size_t)cbase[b] + ((size_t)g * ccap[b] + c) * kHeadDim + 8 * part;
+  if (out_dtype == TF_DTYPE_FP32) {
+    float* dst = (float*)ck + orow;
+    *(f32x4*)dst = f32x4{s[0], s[1], s[2], s[3]};
+    *(f32x4*)(dst + 4) = f32x4{s[4], s[5], s[6], s[7]};
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack2(out_dtype, s[2 * i], s[2 * i + 1]);
+    *(u32x4*)((uint16_t*)ck + orow) = o;
+  }
+}
+
+hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs,
+                             const int32_t* chunk_begin, int32_t max_chunks,
+                             void* ck, const tf_kv_desc& ckd, hipStream_t stream) {
+  const dim3 grid((max_chunks + 15) / 16, kv.H, kv.B), block(256);
+  if (kv.dtype == TF_DTYPE_BF16)
+    hipLaunchKernelGGL(chunk_keys_kernel<TF_DTYPE_BF16>, grid, block, 0, stream, K, kv.seq_base, kv.seq_cap,
+                       kv.seq_len, kv.max_len, cs, chunk_begin, max_chunks, ck, ckd.seq_base, ckd.seq_cap, ckd.dtype);
+  else
+    hipLaunchKernelGGL(chunk_keys_kernel<TF_DTYPE_FP16>, grid, block, 0, stream, K, kv.seq_base, kv.seq_cap,
+                       kv.seq_len, kv.max_len, cs, chunk_begin, max_chunks, ck, ckd.seq_base, ckd.seq_cap, ckd.dtype);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a2: grid (ceil(c_max / (16 * CPL)), H, B).  Each 16-lane group scores CPL
+// chunks (loads issued together), then reduces its 16 partial sums.
+// ---------------------------------------------------------------------------
+constexpr int kCPL = 4;
+
+template <int CK_DT>
+__global__ __launch_bounds__(256) void score_kernel(
+    const uint16_t* __restrict__ q, int32_t q_dtype, int32_t Hq, int32_t H, const void* __restrict__ ck,
+    const int64_t* __restrict__ cbase, const int32_t* __restrict__ ccap, const int32_t* __restrict__ clen,
+    int32_t c_max_len, float* __restrict__ scores, int32_t c_max) {
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int G = Hq / H;
+  const int part = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;  // 16 groups per block
+  const int cap = ccap[b];
+  const int C = min(max(clen[b], 0), min(cap, c_max_len));
+  // Group query: the sum of the G query heads' vectors (8 dims of it per lane).
+  float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < G; ++h) {
+    float f[8];
+    widen8(q_dtype, *(const u32x4*)(q + ((size_t)b * Hq + (size_t)g * G + h) * kHeadDim + 8 * part), f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qs[j] += f[j];
+  }
+  const int c0 = (blockIdx.x * 16 + grp) * kCPL;
+  float dot[kCPL];
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i) {
+    const int c = c0 + i;
+    float acc = 0.f;
+    if (c < C) {
+      const size_t row = (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
+      float f[8];
+      if (CK_DT == TF_DTYPE_FP32) {
+        const f32x4 x0 = *(const f32x4*)((const float*)ck + row);
+        const f32x4 x1 = *(const f32x4*)((const float*)ck + row + 4);
+        f[0] = x0[0]; f[1] = x0[1]; f[2] = x0[2]; f[3] = x0[3];
+        f[4] = x1[0]; f[5] = x1[1]; f[6] = x1[2]; f[7] = x1[3];
+      } else {
+        widen8(CK_DT, *(const u32x4*)((const uint16_t*)ck + row), f);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf(qs[j], f[j], acc);
+    }
+    dot[i] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i) {
+    float v = dot[i];
+    v += __shfl_xor(v, 8, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 1, 16);
+    dot[i] = v;
+  }
+  if (part < kCPL) {
+    const int c = c0 + part;
+    float v = dot[0];
+#pragma unroll
+    for (int i = 1; i < kCPL; ++i)
+      if (part == i) v = dot[i];
+    if (c < c_max) scores[((size_t)b * H + g) * c_max + c] = (c < C) ? v : -__builtin_huge_valf();
+  }
+}
+
+hipError_t launch_scores(const uint16_t* q, int32_t q_dtype, int32_t Hq, const void* ck,
+                         const tf_kv_desc& ckd, float* scores, int32_t c_max, hipStream_t stream) {
+  const dim3 grid((c_max + 16 * kCPL - 1) / (16 * kCPL), ckd.H, ckd.B), block(256);
+  switch (ckd.dtype) {
+    case TF_DTYPE_BF16:
+      hipLaunchKernelGGL(score_kernel<TF_DTYPE_BF16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
+                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
+      break;
+    case TF_DTYPE_FP16:
+      hipLaunchKernelGGL(score_kernel<TF_DTYPE_FP16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
+                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
+      break;
+    default:
+      hipLaunchKernelGGL(score_kernel<TF_DTYPE_FP32>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
+                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tfk

@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libtfattn.
+// Nothing here is part of the public C ABI (include/tf_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tf_attn.h"
+
+namespace tfk {
+
+constexpr int kHeadDim = 128;
+constexpr int kThreads = 256;          // 4 waves of 64 lanes
+constexpr int kTile = 32;              // virtual tokens per wave iteration
+constexpr int kMaxRows = 64;           // query rows per KV head (4 MFMA query tiles)
+
+enum AttnMode { kVerify = 0, kSparse = 1, kStream = 2 };
+
+struct AttnArgs {
+  const uint16_t* q;        // [B][Hq][Qn][d]
+  const uint16_t* K;
+  const uint16_t* V;
+  const int64_t* seq_base;
+  const int32_t* seq_cap;
+  const int32_t* seq_len;
+  int32_t max_len;
+  int32_t B, Hq, Hkv, G, Qn, rows;  // rows = G * Qn query rows per KV head
+  // sparse
+  const int32_t* idx;       // [B][Hkv][k]
+  int32_t k, cs;
+  // stream
+  int32_t n_sink, window;
+  // split-K
+  int32_t tpw;              // virtual tokens per workgroup (multiple of 128)
+  int32_t nsplit;           // gridDim.x
+  int32_t rows_pad;         // 16 * query tiles
+  float* out;               // [B][Hq][Qn][d]
+  float* lse;               // [B][Hq][Qn] or null
+  float* part_o;            // [B][Hkv][nsplit][rows_pad][d]
+  float* part_ml;           // [B][Hkv][nsplit][rows_pad][2]
+  int32_t* counters;        // [B][Hkv]
+  float scale_log2;         // log2(e) / sqrt(d)
+  float scale_ln;           // 1 / sqrt(d)
+};
+
+// Split plan shared by the workspace-size functions and the launches.
+struct SplitPlan {
+  int32_t tpw;
+  int32_t nsplit;
+  int32_t rows_pad;
+  size_t part_o_bytes, part_ml_bytes, counter_bytes, total_bytes;
+};
+
+SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs);
+
+hipError_t launch_attn(int dtype, int mode, const AttnArgs& a, hipStream_t stream);
+
+// chunk keys / scores
+hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs,
+                             const int32_t* chunk_begin, int32_t max_chunks,
+                             void* ck, const tf_kv_desc& ckd, hipStream_t stream);
+hipError_t launch_scores(const uint16_t* q, int32_t q_dtype, int32_t Hq, const void* ck,
+                         const tf_kv_desc& ckd, float* scores, int32_t c_max, hipStream_t stream);
+// top-k
+hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_max,
+                       const int32_t* n_chunks, int32_t k, int32_t* idx, hipStream_t stream);
+// accept
+size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V);
+hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens,
+                         const double* uniforms, int32_t B, int32_t gamma, int32_t V,
+                         float temperature, int32_t flags, int32_t* n_acc, int32_t* next,
+                         void* ws, hipStream_t stream);
+// workspace
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);
+
+}  // namespace tfk

@@ -1,0 +1,215 @@
+/*
+ * tf_attn.h - C ABI of the MI355X (gfx950) decode-step attention library of
+ * hierarchical speculative decoding (TriForce).
+ *
+ * The operations come from two web pages:
+ *   [blog] aifetchly, "TriForce: Hierarchical Speculative Decoding for LLMs",
+ *          section "1. The Three Forces of TriForce" (Force 1: a drafter on a
+ *          streaming cache of initial sinks plus the most recent W tokens;
+ *          Force 2: the target on a retrieval-sparse cache of the top-k KV
+ *          blocks chosen by key-query similarity; Force 3: the target on the
+ *          full cache verifying the candidates in one pass) and section
+ *          "2. Dual Rejection Sampling: Mathematical Losslessness" (accept x
+ *          when min(1, p(x)/q(x)) >= u, else draw from the normalised
+ *          max(0, p - q)).
+ *   [abs]  mlsanity / fugumt pages on arXiv 2404.11912, "Abstract": the whole
+ *          KV cache is read for every generated token; a retrieval-based
+ *          sparse KV cache acts as draft; robust across temperatures.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function returns a tf_status.  Arguments are validated on the host
+ *    before anything is enqueued; on any error nothing is launched and the
+ *    outputs are untouched.  tf_last_error_detail() then describes the error
+ *    (thread-local, valid until the next call on that thread).
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronises; scratch memory is a caller-owned
+ *    workspace whose size the matching *_workspace_size() function returns.
+ *  - Work is enqueued asynchronously on the caller's stream (0 = null stream).
+ *  - Results are deterministic: split counts and combine order depend only on
+ *    the arguments, so repeated calls give bitwise identical outputs.
+ *  - Head dimension d must be 128.  K/V storage is fp16 or bf16; all
+ *    attention arithmetic accumulates in fp32 and outputs are fp32.
+ *  - Pointers must be 16-byte aligned, and every row offset a descriptor
+ *    implies (seq_base[b] and seq_cap[b] * d) a multiple of 8 elements.
+ *  - Calls that share one workspace must not overlap in time (same stream or
+ *    explicitly ordered).  A workspace must be zero-filled once after
+ *    allocation (tf_workspace_clear); each completed call leaves its counters
+ *    at zero again.
+ *  - Caches must hold finite values.
+ */
+#ifndef TF_ATTN_H
+#define TF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* tf_stream_t; /* a hipStream_t */
+
+typedef enum {
+  TF_OK = 0,
+  TF_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment, bad combination */
+  TF_ERR_UNSUPPORTED = 2, /* valid but not implemented (d != 128, too many query rows, ...) */
+  TF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size() */
+  TF_ERR_HIP = 4          /* a HIP launch failed; see tf_last_error_detail() */
+} tf_status;
+
+typedef enum { TF_DTYPE_FP16 = 1, TF_DTYPE_BF16 = 2, TF_DTYPE_FP32 = 3 } tf_dtype;
+
+/*
+ * Head-major ragged cache descriptor.  Row t of head g of sequence b starts
+ * at element  seq_base[b] + (g * seq_cap[b] + t) * d  of the buffer it
+ * describes.  seq_base / seq_cap / seq_len are DEVICE arrays of length B;
+ * the other fields are host values.  Kernels clamp each seq_len[b] into
+ * [0, min(seq_cap[b], max_len)], so a wrong length can drop rows but never
+ * reads outside the rows the descriptor declares.
+ */
+typedef struct {
+  int32_t B;                /* sequences */
+  int32_t H;                /* KV heads */
+  int32_t d;                /* head dimension (128) */
+  int32_t dtype;            /* tf_dtype of the described buffer */
+  const int64_t* seq_base;  /* device [B]: element offset of (b, head 0, row 0) */
+  const int32_t* seq_cap;   /* device [B]: rows allocated per head */
+  const int32_t* seq_len;   /* device [B]: valid rows */
+  int32_t max_len;          /* host: upper bound of every seq_len[b]; sizes the grid */
+} tf_kv_desc;
+
+const char* tf_status_string(int status);
+const char* tf_last_error_detail(void);
+
+/* Zero-fill a workspace (enqueued on `stream`, no memset node). */
+int tf_workspace_clear(void* ws, size_t ws_bytes, tf_stream_t stream);
+
+/*
+ * a1  Chunk-mean keys.  [blog] Force 2 retrieves KV blocks by key-query
+ * similarity; a block is summarised by the mean of its keys.
+ *   ck[b][g][c] = mean of K[b][g][t] over t in [c*cs, min((c+1)*cs, n_b)),
+ * summed in fp32 and rounded once (nearest even) to ckd->dtype, which is the
+ * K dtype or TF_DTYPE_FP32.  Only chunks c in
+ * [chunk_begin[b], min(chunk_begin[b] + max_chunks, ceil(n_b / cs))) are
+ * written, so a decode loop refreshes just the chunks new rows fell into.
+ *   K          : device, described by kv.
+ *   chunk_begin: device int32 [B], or NULL for 0.
+ *   max_chunks : host, > 0; chunks per sequence this call may write.
+ *   ck         : device, described by ckd (rows are chunks; ckd->seq_len is
+ *                not read; ckd->seq_cap[b] must be >= ceil(n_b / cs)).
+ */
+int tf_build_chunk_keys(const void* K, const tf_kv_desc* kv, int32_t chunk_size,
+                        const int32_t* chunk_begin, int32_t max_chunks,
+                        void* ck, const tf_kv_desc* ckd, tf_stream_t stream);
+
+/*
+ * a2  Query-to-chunk scores.  [blog] Force 2, "Key-Query similarity".
+ *   scores[b][g][c] = sum over the G = Hq / H query heads h = g*G .. g*G+G-1
+ *                     of q[b][h] . ck[b][g][c]      (unscaled, fp32)
+ * for c < C_b = ckd->seq_len[b] (chunk count), and -inf for C_b <= c < c_max.
+ *   q      : device [B][Hq][d], ckd->dtype must equal the q dtype `q_dtype`
+ *            unless ckd->dtype is TF_DTYPE_FP32.
+ *   ck     : device, described by ckd (seq_len = chunk counts, max_len <= c_max).
+ *   scores : device fp32 [B][H][c_max].
+ */
+int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq,
+                    const void* ck, const tf_kv_desc* ckd,
+                    float* scores, int32_t c_max, tf_stream_t stream);
+
+/*
+ * a3  Top-k chunk selection under a token budget.  [blog] Force 2 keeps a
+ * small subset of the most critical blocks ("top k = 2,048 tokens").
+ * For each row (b, g): the k = budget / cs chunk indices with the largest
+ * scores among c < n_chunks[b]; ties go to the lower index; NaN ranks as
+ * -inf and -0.0 as +0.0; written ascending; padded with -1 when
+ * n_chunks[b] < k.  Bit-exact for a given score array.
+ *   scores  : device fp32 [B][rows_per_seq][c_max].
+ *   n_chunks: device int32 [B] (clamped into [0, c_max]).
+ *   idx     : device int32 [B][rows_per_seq][k].
+ *   Needs no workspace (ws may be NULL).  c_max <= 1 << 20.
+ */
+int tf_select_topk(const float* scores, int32_t B, int32_t rows_per_seq, int32_t c_max,
+                   const int32_t* n_chunks, int32_t k, int32_t* idx,
+                   void* ws, size_t ws_bytes, tf_stream_t stream);
+size_t tf_select_topk_workspace_size(int32_t B, int32_t rows_per_seq, int32_t c_max, int32_t k);
+
+/*
+ * a4  Attention over the gathered chunks.  [blog] Force 2 runs on the
+ * retrieval-sparse cache; [abs] sparse KV cache via retrieval as draft.
+ *   out[b][h] = sum_t softmax_t(q[b][h] . K_t / sqrt(d)) V_t over the rows t of
+ *   the chunks idx[b][g][0..k) (g = h / G; entries < 0 skipped; rows >= n_b
+ *   skipped), lse[b][h] = log sum_t exp(q . K_t / sqrt(d)); a head with no
+ *   row gets out = 0, lse = -inf.
+ *   q  : device [B][Hq][d] in kv->dtype.   out: device fp32 [B][Hq][d].
+ *   lse: device fp32 [B][Hq] or NULL.      idx: device int32 [B][H][k].
+ *   ws : tf_sparse_attn_workspace_size(kv->B, Hq, kv->H, k, chunk_size) bytes.
+ */
+int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const void* V,
+                   const tf_kv_desc* kv, const int32_t* idx, int32_t k, int32_t chunk_size,
+                   float* out, float* lse, void* ws, size_t ws_bytes, tf_stream_t stream);
+size_t tf_sparse_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t k, int32_t chunk_size);
+
+/*
+ * a5  Sink + window streaming attention.  [blog] Force 1 drafts on a cache of
+ * the initial sink tokens plus the most recent W tokens (StreamingLLM).
+ * With n = sd->seq_len[b] the logical length, the visible positions are
+ *   [0, min(n_sink, n))  U  [max(n_sink, n - window), n).
+ * Ring layout: position p < n_sink is in slot p; p >= n_sink is in slot
+ *   n_sink + (p - n_sink) mod (seq_cap[b] - n_sink),
+ * and seq_cap[b] >= n_sink + window is the caller's contract.  seq_len here
+ * is the LOGICAL length (it may exceed seq_cap; it is not clamped to it).
+ *   q: device [B][Hq][d]; out: device fp32 [B][Hq][d]; lse: [B][Hq] or NULL.
+ *   No workspace.
+ */
+int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const void* Vs,
+                   const tf_kv_desc* sd, int32_t n_sink, int32_t window,
+                   float* out, float* lse, tf_stream_t stream);
+
+/*
+ * a6  Full-cache multi-query verification.  [blog] Force 3 verifies all
+ * candidates against the complete cache in one parallel pass; [abs] the
+ * whole KV cache is loaded for every generated token.  Chain form: the last
+ * Q rows of the cache are the draft positions, so query row i (0 <= i < Q)
+ * of head h sees rows j <= n_b - Q + i:
+ *   out[b][h][i] = sum_{j <= n_b - Q + i} softmax_j(q[b][h][i] . K_j / sqrt(d)) V_j
+ * (a row that sees nothing gets out = 0, lse = -inf).
+ *   q  : device [B][Hq][Q][d] in kv->dtype.  out: device fp32 [B][Hq][Q][d].
+ *   lse: device fp32 [B][Hq][Q] or NULL.     G * Q <= 64.
+ *   ws : tf_verify_attn_workspace_size(kv->B, Hq, kv->H, Q, kv->max_len) bytes.
+ */
+int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                   const tf_kv_desc* kv, float* out, float* lse,
+                   void* ws, size_t ws_bytes, tf_stream_t stream);
+size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len);
+
+/*
+ * a7  Lossless accept / reject.  [blog] "2. Dual Rejection Sampling".
+ * Per sequence b, with p_i = softmax(target[b][i] / T), q_i =
+ * softmax(draft[b][i] / T) in fp64 (T = 0: one-hot at the lowest-index
+ * argmax; flag TF_ACCEPT_PROBS: the rows already are probabilities, used as
+ * given):
+ *   for i = 0 .. gamma-1, x = draft_tokens[b][i]: keep x when p_i(x) > 0 and
+ *   min(1, p_i(x) / q_i(x)) >= uniforms[b][i] (q_i(x) = 0 counts as 1);
+ *   stop at the first rejection j.
+ *   next_token[b] is drawn with u = uniforms[b][gamma] by inverse CDF (the
+ *   smallest t whose running sum exceeds u * total, strictly) from
+ *   max(0, p_j - q_j) (p_j if that sums to 0) after a rejection, or from
+ *   p_gamma when every draft was kept.  n_accepted[b] = j (gamma if none was
+ *   rejected).  Emitted tokens: draft_tokens[b][0 .. n_accepted) then next.
+ *   target: device fp32 [B][gamma+1][V]; draft: device fp32 [B][gamma][V];
+ *   draft_tokens: device int32 [B][gamma] (each in [0, V)); uniforms: device
+ *   fp64 [B][gamma+1] in (0, 1).  Outputs: device int32 [B].
+ *   ws: tf_accept_workspace_size(B, gamma, V) bytes.
+ */
+#define TF_ACCEPT_PROBS 1
+int tf_accept(const float* target, const float* draft, const int32_t* draft_tokens,
+              const double* uniforms, int32_t B, int32_t gamma, int32_t V, float temperature,
+              int32_t flags, int32_t* n_accepted, int32_t* next_token,
+              void* ws, size_t ws_bytes, tf_stream_t stream);
+size_t tf_accept_workspace_size(int32_t B, int32_t gamma, int32_t V);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TF_ATTN_H */

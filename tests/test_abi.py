@@ -1,0 +1,119 @@
+"""The C-ABI library loads without a GPU, exports every function the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(so these calls never reach the GPU: every pointer below is a dummy)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from hierarchical_speculative_attention_amd import _lib as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tf_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(T.LIB_PATH), reason="libtfattn.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced by a failing call
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tf_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared()
+    assert len(names) >= 14
+    L = T.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(T.EXPORTS) == names
+
+
+def desc(B=1, H=4, d=128, dtype=T.TF_DTYPE_BF16, max_len=100, arrays=True):
+    p = FAKE.value if arrays else None
+    return T.TfKvDesc(B, H, d, dtype, p, p, p, max_len)
+
+
+def call_verify(kv, Hq=4, Q=5, q=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return T.lib().tf_verify_attn(q, Hq, Q, FAKE, FAKE, ctypes.byref(kv), FAKE, None, ws, ws_bytes, None)
+
+
+def test_status_strings():
+    L = T.lib()
+    assert L.tf_status_string(0) == b"TF_OK"
+    assert L.tf_status_string(3) == b"TF_ERR_WORKSPACE"
+    assert L.tf_status_string(99) == b"TF_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), T.TF_ERR_UNSUPPORTED),
+    (dict(dtype=T.TF_DTYPE_FP32), T.TF_ERR_UNSUPPORTED),
+    (dict(dtype=7), T.TF_ERR_UNSUPPORTED),
+    (dict(H=0), T.TF_ERR_INVALID_ARG),
+    (dict(B=-1), T.TF_ERR_INVALID_ARG),
+    (dict(max_len=-5), T.TF_ERR_INVALID_ARG),
+    (dict(arrays=False), T.TF_ERR_INVALID_ARG),
+])
+def test_verify_descriptor_errors(kw, status):
+    assert call_verify(desc(**kw)) == status
+    assert T.lib().tf_last_error_detail()
+
+
+def test_verify_argument_errors():
+    L = T.lib()
+    assert call_verify(desc(), Hq=6) == T.TF_ERR_INVALID_ARG           # Hq not a multiple of H
+    assert call_verify(desc(), Q=0) == T.TF_ERR_INVALID_ARG
+    assert call_verify(desc(H=1), Hq=8, Q=9) == T.TF_ERR_UNSUPPORTED   # 72 rows per KV head
+    assert call_verify(desc(), q=None) == T.TF_ERR_INVALID_ARG
+    assert call_verify(desc(), q=ctypes.c_void_p(0x10008)) == T.TF_ERR_INVALID_ARG  # misaligned
+    need = L.tf_verify_attn_workspace_size(1, 4, 4, 5, 100000)
+    assert need > 0
+    assert call_verify(desc(max_len=100000), ws=None, ws_bytes=0) == T.TF_ERR_WORKSPACE
+    assert call_verify(desc(max_len=100000), ws_bytes=need - 1) == T.TF_ERR_WORKSPACE
+    assert call_verify(desc(max_len=100000), ws=ctypes.c_void_p(0x10010)) == T.TF_ERR_INVALID_ARG
+    assert b"workspace" in L.tf_last_error_detail()
+
+
+def test_empty_batch_is_a_no_op():
+    assert call_verify(desc(B=0, arrays=False)) == T.TF_OK
+
+
+def test_other_entry_points_validate():
+    L = T.lib()
+    kv = desc()
+    ckd = desc(dtype=T.TF_DTYPE_FP32)
+    assert L.tf_build_chunk_keys(FAKE, ctypes.byref(kv), 0, None, 10, FAKE, ctypes.byref(ckd), None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_build_chunk_keys(FAKE, ctypes.byref(kv), 8, None, 0, FAKE, ctypes.byref(ckd), None) == T.TF_ERR_INVALID_ARG
+    bad = desc(dtype=T.TF_DTYPE_FP16)
+    assert L.tf_build_chunk_keys(FAKE, ctypes.byref(kv), 8, None, 4, FAKE, ctypes.byref(bad), None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_score_chunks(FAKE, T.TF_DTYPE_BF16, 6, FAKE, ctypes.byref(kv), FAKE, 200, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_score_chunks(FAKE, T.TF_DTYPE_BF16, 4, FAKE, ctypes.byref(kv), FAKE, 50, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_score_chunks(FAKE, T.TF_DTYPE_FP16, 4, FAKE, ctypes.byref(kv), FAKE, 200, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_select_topk(FAKE, 1, 4, 100, FAKE, 0, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_select_topk(FAKE, 1, 4, (1 << 20) + 1, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_UNSUPPORTED
+    assert L.tf_select_topk(None, 1, 4, 100, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_sparse_attn(FAKE, 4, FAKE, FAKE, ctypes.byref(kv), FAKE, 0, 8, FAKE, None, None, 0, None) == T.TF_ERR_INVALID_ARG
+    need = L.tf_sparse_attn_workspace_size(1, 4, 4, 512, 8)
+    assert need > 0
+    assert L.tf_sparse_attn(FAKE, 4, FAKE, FAKE, ctypes.byref(kv), FAKE, 512, 8, FAKE, None, None, 0, None) == T.TF_ERR_WORKSPACE
+    assert L.tf_stream_attn(FAKE, 4, FAKE, FAKE, ctypes.byref(kv), -1, 252, FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_stream_attn(FAKE, 3, FAKE, FAKE, ctypes.byref(kv), 4, 252, FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    f = ctypes.c_float
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 0, f(1.0), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(-1.0), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(float("nan")), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(1.0), 4, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_accept(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10004), 1, 4, 100, f(1.0), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_are_deterministic_and_grow_with_length():
+    L = T.lib()
+    a = L.tf_verify_attn_workspace_size(1, 32, 32, 7, 131072)
+    assert a == L.tf_verify_attn_workspace_size(1, 32, 32, 7, 131072)
+    assert L.tf_verify_attn_workspace_size(1, 32, 32, 7, 1 << 20) >= a
+    assert L.tf_verify_attn_workspace_size(0, 32, 32, 7, 131072) == 0
+    assert L.tf_accept_workspace_size(4, 6, 32000) == 0

@@ -1,0 +1,118 @@
+"""GPU parity of the accept / reject step: bit-exact accept counts and
+sampled tokens given the same uniforms, hand-worked examples, and the
+losslessness statistics run on the GPU kernel itself."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import oracle
+from hierarchical_speculative_attention_amd import synth
+import hierarchical_speculative_attention_amd as tf
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "accept_hand_examples.json")
+
+
+def run(target, draft, tokens, u, T, probs=False):
+    t = torch.from_numpy(np.ascontiguousarray(target, np.float32)).cuda()
+    d = torch.from_numpy(np.ascontiguousarray(draft, np.float32)).cuda()
+    x = torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda()
+    uu = torch.from_numpy(np.ascontiguousarray(u, np.float64)).cuda()
+    n, nxt = tf.accept(t, d, x, uu, T, probs=probs)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), nxt.cpu().numpy()
+
+
+def test_hand_examples():
+    g = json.load(open(GOLDEN))
+    for case in g["cases"]:
+        n, nxt = run(np.array([case["target"]]), np.array([case["draft"]]), np.array([case["tokens"]]),
+                     np.array([case["uniforms"]]), 1.0, probs=True)
+        assert (n[0], nxt[0]) == (case["n_accepted"], case["next_token"]), case["name"]
+    gr = g["greedy"]
+    n, nxt = run(np.array([gr["target"]]), np.array([gr["draft"]]), np.array([gr["tokens"]]),
+                 np.array([gr["uniforms"]]), 0.0)
+    assert (n[0], nxt[0]) == (gr["n_accepted"], gr["next_token"])
+
+
+@pytest.mark.parametrize("T", [1.0, float(np.float32(0.7)), 0.0, float(np.float32(2.5))])
+@pytest.mark.parametrize("correlated", [False, True])
+def test_random_logits_bit_exact(T, correlated):
+    B, gamma, V = 64, 6, 32000
+    a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=correlated, seed=20)
+    tokens = a.tokens.copy()
+    if correlated:
+        # draft tokens drawn from the draft distribution so that long runs get kept
+        rng = np.random.default_rng(21)
+        for b in range(B):
+            for i in range(gamma):
+                q = oracle.distribution(a.draft[b, i], T if T > 0 else 1.0)
+                tokens[b, i] = rng.choice(V, p=q / q.sum())
+    n, nxt = run(a.target, a.draft, tokens, a.uniforms, T)
+    guarded = 0
+    for b in range(B):
+        rn, rnext, margin = oracle.accept(a.target[b], a.draft[b], tokens[b], a.uniforms[b], T)
+        if margin < 1e-12:
+            guarded += 1
+            continue
+        assert (n[b], nxt[b]) == (rn, rnext), b
+    assert guarded <= 1
+    if correlated and T > 0:
+        assert n.max() >= 2
+
+
+def test_gamma_zero_and_out_of_vocab_tokens():
+    a = synth.make_accept_inputs(B=8, gamma=3, vocab=1000, seed=22)
+    toks = a.tokens.copy()
+    toks[:, 0] = -1
+    toks[1, 0] = 5000
+    n, nxt = run(a.target, a.draft, toks, a.uniforms, 1.0)
+    assert np.all(n == 0)                      # a token outside [0, V) is never kept
+    assert np.all((nxt >= 0) & (nxt < 1000))
+    # gamma = 0: a plain sample from the target row
+    t = torch.from_numpy(a.target[:, :1].copy()).cuda()
+    u = torch.from_numpy(a.uniforms[:, :1].copy()).cuda()
+    n0, x0 = tf.accept(t, None, None, u, 1.0)
+    x0 = x0.cpu().numpy()
+    for b in range(8):
+        ref = oracle.inverse_cdf(oracle.distribution(a.target[b, 0], 1.0), a.uniforms[b, 0])
+        assert x0[b] == ref
+    assert np.all(n0.cpu().numpy() == 0)
+
+
+def test_losslessness_on_gpu():
+    """200k independent one-trial sequences in one call: the first emitted
+    token follows p_0 and, when the first draft was kept, the second follows
+    p_1 (chi-square at alpha = 1e-3)."""
+    rng = np.random.default_rng(23)
+    V, gamma, B = 8, 3, 200000
+    p = rng.dirichlet(np.ones(V) * 0.7, gamma + 1)
+    q = rng.dirichlet(np.ones(V) * 0.7, gamma)
+    p[0, 5] = 0.0
+    p[0] /= p[0].sum()
+    p32, q32 = p.astype(np.float32), q.astype(np.float32)
+    target = np.broadcast_to(p32, (B, gamma + 1, V))
+    draft = np.broadcast_to(q32, (B, gamma, V))
+    q64 = q32.astype(np.float64)
+    tokens = np.stack([rng.choice(V, size=B, p=q64[i] / q64[i].sum()) for i in range(gamma)], 1)
+    u = synth.open_uniforms(rng, (B, gamma + 1))
+    n, nxt = run(target, draft, tokens, u, 1.0, probs=True)
+    first = np.where(n > 0, tokens[:, 0], nxt)
+    second = np.where(n > 1, tokens[:, 1], nxt)
+    for counts_src, mask, pr in [(first, np.ones(B, bool), p32[0]), (second, n >= 1, p32[1])]:
+        counts = np.bincount(counts_src[mask], minlength=V)
+        exp = pr.astype(np.float64) / pr.sum() * mask.sum()
+        keep = exp > 0
+        assert np.all(counts[~keep] == 0)
+        stat = ((counts[keep] - exp[keep]) ** 2 / exp[keep]).sum()
+        assert stat < scipy.stats.chi2.ppf(1 - 1e-3, keep.sum() - 1), stat
+    # and the kernel agrees with the oracle trial by trial on a sample
+    for b in range(0, B, 997):
+        rn, rnext, margin = oracle.accept(p32, q32, tokens[b], u[b], 1.0, probs=True)
+        if margin > 1e-12:
+            assert (n[b], nxt[b]) == (rn, rnext)

@@ -1,0 +1,170 @@
+"""GPU parity of the three attention entry points (verify, sparse, stream)
+against the fp64 oracle, through the C ABI, on seeded synthetic inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_speculative_attention_amd import synth
+import hierarchical_speculative_attention_amd as tf
+from tests.gpu_util import ATOL, compare_attn, desc, dev, oracle_sparse, oracle_verify
+
+pytestmark = pytest.mark.gpu
+
+
+def run_verify(inp, Q, max_len=None):
+    kv = desc(inp.layout, inp.dtype, max_len=max_len)
+    q = dev(inp.q_verify, inp.dtype)
+    out, lse = tf.verify_attn(q, dev(inp.K, inp.dtype), dev(inp.V, inp.dtype), kv)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# verify (Force 3)
+# ---------------------------------------------------------------------------
+
+def test_verify_tiny_fp16_all_heads():
+    # 8 heads, n = 4096, fp16, gamma = 4 -> 5 verify queries, 4 planted chunks
+    inp = synth.make_attn_inputs(lens=[4096], Hq=8, Hkv=8, dtype="fp16", Q=5, seed=0,
+                                 chunk_size=8, plant="count", plant_count=4)
+    out, lse = run_verify(inp, 5)
+    o_ref, l_ref = oracle_verify(inp, 5)
+    err = compare_attn(out, lse, o_ref, l_ref)
+    print(f"verify tiny fp16 max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_verify_ragged_gqa_short_sequences(dtype):
+    # lengths below Q (leading rows see nothing), ragged tails, poison past n
+    lens = [1, 4, 5, 37, 100, 1000, 3001, 4100]
+    inp = synth.make_attn_inputs(lens=lens, Hq=8, Hkv=2, dtype=dtype, Q=5, seed=1, cap_extra=13)
+    out, lse = run_verify(inp, 5)
+    compare_attn(out, lse, *oracle_verify(inp, 5))
+
+
+@pytest.mark.parametrize("Hq,Hkv,Q,n", [(32, 8, 9, 2000), (16, 2, 8, 777), (4, 4, 1, 5000), (6, 3, 7, 129)])
+def test_verify_query_tiles(Hq, Hkv, Q, n):
+    # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14
+    inp = synth.make_attn_inputs(lens=[n], Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=2, cap_extra=3)
+    out, lse = run_verify(inp, Q)
+    compare_attn(out, lse, *oracle_verify(inp, Q))
+
+
+def test_verify_empty_and_max_len_clamp():
+    inp = synth.make_attn_inputs(lens=[0, 3, 200], Hq=2, Hkv=2, dtype="bf16", Q=2, seed=3, cap_extra=8)
+    out, lse = run_verify(inp, 2)
+    compare_attn(out, lse, *oracle_verify(inp, 2))
+    # max_len below a sequence's length: that sequence is clamped to max_len rows
+    out, lse = run_verify(inp, 2, max_len=100)
+    lay = inp.layout
+    clamped = synth.AttnInputs(dtype=inp.dtype, layout=synth.KVLayout(lay.B, lay.H, lay.d, np.minimum(lay.seq_len, 100),
+                                                                       lay.seq_cap, lay.seq_base),
+                               Hq=inp.Hq, K=inp.K, V=inp.V, q_verify=inp.q_verify, q_draft=inp.q_draft,
+                               planted=inp.planted, chunk_size=8)
+    compare_attn(out, lse, *oracle_verify(clamped, 2))
+
+
+def test_verify_is_deterministic():
+    inp = synth.make_attn_inputs(lens=[20000], Hq=4, Hkv=4, dtype="bf16", Q=7, seed=4)
+    a, la = run_verify(inp, 7)
+    b, lb = run_verify(inp, 7)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
+# sparse (Force 2)
+# ---------------------------------------------------------------------------
+
+def oracle_idx(inp, k, cs):
+    lay, dt = inp.layout, inp.dtype
+    G = inp.Hq // lay.H
+    idx = np.full((lay.B, lay.H, k), -1, np.int64)
+    for b in range(lay.B):
+        n = int(lay.seq_len[b])
+        for g in range(lay.H):
+            ck = oracle.chunk_keys(oracle.widen(lay.head(inp.K, b, g), dt), n, cs)
+            qg = oracle.widen(inp.q_draft[b, g * G:(g + 1) * G, 0], dt)
+            idx[b, g] = oracle.select_topk(oracle.chunk_scores(qg, ck), k)
+    return idx
+
+
+def run_sparse(inp, idx, cs):
+    kv = desc(inp.layout, inp.dtype)
+    out, lse = tf.sparse_attn(dev(inp.q_draft, inp.dtype).view(inp.layout.B, inp.Hq, 128),
+                              dev(inp.K, inp.dtype), dev(inp.V, inp.dtype), kv,
+                              torch.from_numpy(idx.astype(np.int32)).cuda(), cs)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_sparse_tiny_fp16_oracle_selection():
+    inp = synth.make_attn_inputs(lens=[4096], Hq=8, Hkv=8, dtype="fp16", Q=1, seed=0,
+                                 chunk_size=8, plant="count", plant_count=4)
+    idx = oracle_idx(inp, 64, 8)
+    out, lse = run_sparse(inp, idx, 8)
+    compare_attn(out, lse, *oracle_sparse(inp, idx, 8))
+
+
+def test_sparse_ragged_gqa_padded_and_partial_chunks():
+    lens = [3, 50, 1001, 4099]
+    inp = synth.make_attn_inputs(lens=lens, Hq=8, Hkv=2, dtype="bf16", Q=1, seed=5, cap_extra=7)
+    rng = np.random.default_rng(9)
+    k, cs = 40, 8
+    idx = np.full((4, 2, k), -1, np.int64)
+    for b, n in enumerate(lens):
+        C = -(-n // cs)
+        for g in range(2):
+            m = min(k - 3, C)
+            sel = np.sort(rng.choice(C, size=m, replace=False))
+            idx[b, g, :m] = sel
+            idx[b, g, m] = C - 1            # the partial last chunk (possibly again)
+            idx[b, g, m + 1] = C + 5        # past the end: contributes nothing
+    out, lse = run_sparse(inp, idx, cs)
+    compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
+
+
+def test_sparse_full_budget_equals_verify_q1():
+    inp = synth.make_attn_inputs(lens=[1000], Hq=4, Hkv=4, dtype="bf16", Q=1, seed=6)
+    C = 125
+    idx = np.tile(np.arange(C), (1, 4, 1))
+    out, lse = run_sparse(inp, idx, 8)
+    vo, vl = run_verify(inp, 1)
+    assert (out - vo[:, :, 0]).abs().max().item() <= ATOL
+    compare_attn(out, lse, *oracle_sparse(inp, idx, 8))
+
+
+@pytest.mark.parametrize("cs,k", [(1, 1), (16, 512), (3, 100)])
+def test_sparse_chunk_sizes(cs, k):
+    inp = synth.make_attn_inputs(lens=[3000], Hq=4, Hkv=2, dtype="bf16", Q=1, seed=7)
+    C = -(-3000 // cs)
+    rng = np.random.default_rng(cs)
+    idx = np.full((1, 2, k), -1, np.int64)
+    for g in range(2):
+        m = min(k, C)
+        idx[0, g, :m] = np.sort(rng.choice(C, size=m, replace=False))
+    out, lse = run_sparse(inp, idx, cs)
+    compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
+
+
+# ---------------------------------------------------------------------------
+# stream (Force 1)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,S,W", [("bf16", 4, 252), ("fp16", 4, 252), ("bf16", 0, 1), ("bf16", 2, 7)])
+def test_stream_parity(dtype, S, W):
+    lens = [4096, 1000, 100, 3, 256, 257, 1]
+    s = synth.make_stream_inputs(lens=lens, Hq=8, Hkv=4, dtype=dtype, n_sink=S, window=W, seed=8)
+    sd = desc(s.layout, dtype)
+    out, lse = tf.stream_attn(dev(s.q, dtype).view(len(lens), 8, 128), dev(s.Ks, dtype), dev(s.Vs, dtype), sd, S, W)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((len(lens), 8, 128))
+    l_ref = np.zeros((len(lens), 8))
+    for b, n in enumerate(lens):
+        for h in range(8):
+            g = h // 2
+            q = oracle.widen(s.q[b, h, 0], dtype)
+            o_ref[b, h], l_ref[b, h] = oracle.stream_attn_masked(
+                q, oracle.widen(s.K_logical[b][g], dtype), oracle.widen(s.V_logical[b][g], dtype), n, S, W)
+    compare_attn(out, lse, o_ref, l_ref)

@@ -1,0 +1,162 @@
+"""GPU parity of the retrieval steps: chunk-mean keys, chunk scores and
+top-k selection, each fed the same upstream arrays as the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_speculative_attention_amd import synth, KVDesc
+import hierarchical_speculative_attention_amd as tf
+from tests.gpu_util import TDT, desc, dev, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def ck_layout(layout, cs):
+    C = [max(1, -(-int(n) // cs)) for n in layout.seq_len]
+    return synth.KVLayout.build([-(-int(n) // cs) for n in layout.seq_len], layout.H, layout.d, caps=C)
+
+
+def run_chunk_keys(inp, cs, out_dtype, chunk_begin=None, max_chunks=None):
+    lay = inp.layout
+    cl = ck_layout(lay, cs)
+    odt = torch.float32 if out_dtype == "fp32" else TDT[out_dtype]
+    ck = torch.full((cl.total_elems,), float("nan"), dtype=odt, device="cuda")
+    kv = desc(lay, inp.dtype)
+    ckd = KVDesc.from_layout(cl, odt, "cuda")
+    cb = None if chunk_begin is None else torch.tensor(chunk_begin, dtype=torch.int32, device="cuda")
+    tf.build_chunk_keys(dev(inp.K, inp.dtype), kv, cs, ck, ckd, chunk_begin=cb, max_chunks=max_chunks)
+    torch.cuda.synchronize()
+    return ck, cl, ckd
+
+
+def check_chunk_keys(inp, ck, cl, cs, out_dtype, only=None):
+    lay = inp.layout
+    if out_dtype == "fp32":
+        got_all = ck.cpu().double().numpy()
+    else:
+        got_all = oracle.widen(host_bits(ck), out_dtype)
+    for b in range(lay.B):
+        n = int(lay.seq_len[b])
+        for g in range(lay.H):
+            ref = oracle.chunk_keys(oracle.widen(lay.head(inp.K, b, g), inp.dtype), n, cs)
+            got = cl.head(got_all, b, g)
+            rows = range(ref.shape[0]) if only is None else only[b]
+            for c in rows:
+                r, gv = ref[c], got[c]
+                if out_dtype == "fp32":
+                    np.testing.assert_allclose(gv, r, rtol=1e-6, atol=1e-6)
+                else:
+                    # one rounding of the fp64 mean: equal to the correctly rounded value,
+                    # except where the mean lies within fp32 rounding of a rounding midpoint
+                    exact = oracle.widen(oracle.round_f64_to_bits(r, out_dtype), out_dtype)
+                    ulp = np.abs(np.spacing(exact.astype(np.float32 if out_dtype == "bf16" else np.float16)))
+                    if out_dtype == "bf16":
+                        ulp = np.abs(exact) * 2.0 ** -7 + 1e-40
+                    mism = gv != exact
+                    if mism.any():
+                        assert np.all(np.abs(gv - r)[mism] <= 0.5 * ulp[mism] * (1 + 1e-5) + 1e-7), (b, g, c)
+                        assert mism.mean() < 0.01
+
+
+@pytest.mark.parametrize("dtype,out_dtype", [("bf16", "bf16"), ("bf16", "fp32"), ("fp16", "fp16"), ("fp16", "fp32")])
+def test_chunk_keys_parity(dtype, out_dtype):
+    inp = synth.make_attn_inputs(lens=[4096, 1003, 1, 17], Hq=4, Hkv=4, dtype=dtype, seed=10, cap_extra=5)
+    ck, cl, _ = run_chunk_keys(inp, 8, out_dtype)
+    check_chunk_keys(inp, ck, cl, 8, out_dtype)
+
+
+def test_chunk_keys_partial_refresh():
+    inp = synth.make_attn_inputs(lens=[1000, 64], Hq=2, Hkv=2, dtype="bf16", seed=11)
+    ck, cl, _ = run_chunk_keys(inp, 16, "bf16", chunk_begin=[60, 2], max_chunks=3)
+    got = oracle.widen(host_bits(ck), "bf16")
+    # chunks [60, 63) of sequence 0 (62 is the partial last chunk) and [2, 4) of sequence 1
+    check_chunk_keys(inp, ck, cl, 16, "bf16", only={0: [60, 61, 62], 1: [2, 3]})
+    for g in range(2):
+        assert np.all(np.isnan(cl.head(got, 0, g)[:60]))
+        assert np.all(np.isnan(cl.head(got, 1, g)[:2]))
+
+
+def run_scores(inp, ck, ckd, c_max):
+    q = dev(inp.q_draft, inp.dtype).view(inp.layout.B, inp.Hq, 128)
+    s = tf.score_chunks(q, inp.Hq, ck, ckd, c_max)
+    torch.cuda.synchronize()
+    return s
+
+
+@pytest.mark.parametrize("Hq,Hkv,ck_dtype", [(8, 8, "bf16"), (8, 2, "bf16"), (8, 2, "fp32"), (4, 4, "fp16")])
+def test_scores_parity(Hq, Hkv, ck_dtype):
+    dtype = "fp16" if ck_dtype == "fp16" else "bf16"
+    inp = synth.make_attn_inputs(lens=[4096, 777, 9], Hq=Hq, Hkv=Hkv, dtype=dtype, seed=12,
+                                 plant="count", plant_count=4)
+    ck, cl, ckd = run_chunk_keys(inp, 8, ck_dtype)
+    c_max = 600
+    s = run_scores(inp, ck, ckd, c_max).cpu().double().numpy()
+    got_ck = ck.cpu().double().numpy() if ck_dtype == "fp32" else oracle.widen(host_bits(ck), ck_dtype)
+    G = Hq // Hkv
+    for b in range(3):
+        C = int(cl.seq_len[b])
+        for g in range(Hkv):
+            kbar = cl.head(got_ck, b, g)
+            qg = oracle.widen(inp.q_draft[b, g * G:(g + 1) * G, 0], dtype)
+            ref = oracle.chunk_scores(qg, kbar)
+            scale = np.linalg.norm(qg.sum(0)) * np.linalg.norm(kbar, axis=1) + np.abs(qg).sum() * 1e-3
+            assert np.all(np.abs(s[b, g, :C] - ref) <= 1e-5 * scale)
+            assert np.all(np.isneginf(s[b, g, C:]))
+
+
+def run_topk(scores_np, n_chunks, k):
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, np.float32)).cuda()
+    idx = tf.select_topk(s, torch.tensor(n_chunks, dtype=torch.int32, device="cuda"), k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def test_topk_bit_exact_on_gpu_scores():
+    inp = synth.make_attn_inputs(lens=[4096, 2500], Hq=8, Hkv=8, dtype="bf16", seed=13, plant="count", plant_count=4)
+    ck, cl, ckd = run_chunk_keys(inp, 8, "bf16")
+    s = run_scores(inp, ck, ckd, 512)
+    s_np = s.cpu().numpy()
+    for k in [64, 1, 511, 512, 600]:
+        idx = run_topk(s_np, [512, 313], k)
+        for b, C in enumerate([512, 313]):
+            for g in range(8):
+                ref = oracle.select_topk(s_np[b, g, :C].astype(np.float64), k)
+                assert np.array_equal(idx[b, g], ref), (k, b, g)
+    # every planted chunk of the full-length sequence is selected at k = 64
+    idx = run_topk(s_np, [512, 313], 64)
+    for g in range(8):
+        assert set(inp.planted[0].tolist()) <= set(idx[0, g].tolist())
+
+
+def test_topk_adversarial_rows():
+    rng = np.random.default_rng(14)
+    rows = []
+    C = 1000
+    rows.append(np.zeros(C))                                   # all equal
+    r = np.zeros(C); r[::2] = -0.0; rows.append(r)             # +-0
+    r = rng.standard_normal(C); r[rng.choice(C, 50, replace=False)] = np.inf
+    r[rng.choice(C, 50, replace=False)] = -np.inf; rows.append(r)
+    r = rng.standard_normal(C); r[rng.choice(C, 300, replace=False)] = np.nan; rows.append(r)
+    rows.append(np.round(rng.standard_normal(C) * 2) / 4)     # heavy ties
+    rows.append(np.full(C, np.nan))
+    rows.append(rng.standard_normal(C) * 1e-38)                # subnormal-range fp32
+    scores = np.stack(rows)[None].astype(np.float32)
+    for k in [1, 7, 64, 499, 999, 1000, 1500]:
+        for n in [C, 937, 65, 64, 1]:
+            idx = run_topk(scores, [n], k)
+            for g in range(scores.shape[1]):
+                ref = oracle.select_topk(scores[0, g, :n].astype(np.float64), k)
+                assert np.array_equal(idx[0, g], ref), (k, n, g)
+
+
+@pytest.mark.parametrize("C,k", [(16384, 512), (32768, 512), (70000, 3000)])
+def test_topk_large_rows(C, k):
+    rng = np.random.default_rng(C)
+    s = (rng.standard_normal((2, 3, C)) * 5).astype(np.float32)
+    s[:, :, rng.choice(C, 100)] = 7.5   # ties near the top
+    idx = run_topk(s, [C, C - 11], k)
+    for b, n in enumerate([C, C - 11]):
+        for g in range(3):
+            assert np.array_equal(idx[b, g], oracle.select_topk(s[b, g, :n].astype(np.float64), k))
