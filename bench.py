@@ -1,0 +1,344 @@
+"""Decode-step benchmark of the TriForce decode-attention path on one MI355X.
+
+One step = for every layer: refresh of the chunk-mean keys the newest rows
+fell into, query-to-chunk scores, top-k selection, attention over the
+gathered chunks (the sparse draft), sink + window streaming attention (the
+small drafter) and full-cache verification of the gamma + 1 draft positions;
+then one accept / reject over the vocabulary and the 8-byte-per-sequence
+read-back of its result.  Inputs are synthetic, seeded, resident in HBM
+before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn GB/s & % HBM peak, sparse-draft+verify steps/s at 128K ctx"
+HBM_PEAK_GBPS = 8000.0
+VERIFY_SRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2-7b-128k-32layers")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ck-dtype", default="kv", choices=["kv", "fp32"])
+    return ap.parse_args()
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per verify launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attn_hip_sha256") != file_sha(VERIFY_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Layer:
+    pass
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the path is not sharded "
+                                   "across GPUs (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from hierarchical_speculative_attention_amd import synth
+    import hierarchical_speculative_attention_amd as tf
+
+    W = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    B, Hq, Hkv, d = W["B"], W["Hq"], W["Hkv"], W["d"]
+    lens = W["lens"]
+    layers = args.layers or W["layers"]
+    cs, budget, gamma, vocab = W["chunk_size"], W["budget"], W["gamma"], W["vocab"]
+    S, Wn = W["n_sink"], W["window"]
+    Q = gamma + 1
+    k = budget // cs
+    tdt = torch.bfloat16 if W["dtype"] == "bf16" else torch.float16
+    ck_dt = torch.float32 if args.ck_dtype == "fp32" else tdt
+    n_max = max(lens)
+    C = [-(-n // cs) for n in lens]
+    c_max = max(C)
+    t_setup = time.perf_counter()
+
+    # ---- inputs, resident in HBM ------------------------------------------
+    L = []
+    with torch.cuda.stream(stream):
+        for l in range(layers):
+            K, V, qv, qd, lay, planted = synth.make_layer_torch(
+                lens=lens, Hq=Hq, Hkv=Hkv, d=d, dtype=W["dtype"], Q=Q, chunk_size=cs, plant=W["plant"],
+                seed=0, layer=l, device=dev, plant_fraction=W.get("plant_fraction", 0.01),
+                plant_count=W.get("plant_count", 0), zipf_s=W.get("zipf_s", 1.1))
+            x = Layer()
+            x.K, x.V, x.qv, x.qd = K, V, qv, qd.view(B, Hq, d)
+            x.kv = tf.KVDesc.from_layout(lay, tdt, dev)
+            ck_lay = synth.KVLayout.build(C, Hkv, d, caps=C)
+            x.ckd = tf.KVDesc.from_layout(ck_lay, ck_dt, dev)
+            x.ck = torch.empty(ck_lay.total_elems, dtype=ck_dt, device=dev)
+            g = torch.Generator(device=dev).manual_seed(synth.torch_seed(0, l, "ring"))
+            scap = S + Wn + synth.STREAM_SLACK
+            s_lay = synth.KVLayout.build(lens, Hkv, d, caps=[scap] * B)
+            x.Ks = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
+            x.Vs = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
+            x.sd = tf.KVDesc.from_layout(s_lay, tdt, dev)
+            x.planted = planted
+            L.append(x)
+        n_chunks = torch.tensor(C, dtype=torch.int32, device=dev)
+        tail_chunk = torch.tensor([max(0, (n - Q) // cs) for n in lens], dtype=torch.int32, device=dev)
+        tail_count = (Q + cs - 1) // cs + 1
+        scores = torch.empty((B, Hkv, c_max), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        o_sp = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        l_sp = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        o_st = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        l_st = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        o_v = torch.empty((B, Hq, Q, d), dtype=torch.float32, device=dev)
+        l_v = torch.empty((B, Hq, Q), dtype=torch.float32, device=dev)
+        ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Q, n_max), dev)
+        ws_s = tf.workspace(tf.sparse_attn_workspace_size(B, Hq, Hkv, k, cs), dev)
+        acc_in = synth.make_accept_inputs(B=B, gamma=gamma, vocab=vocab, seed=0)
+        tgt = torch.from_numpy(acc_in.target).to(dev)
+        drf = torch.from_numpy(acc_in.draft).to(dev)
+        tok = torch.from_numpy(acc_in.tokens).to(dev)
+        uni = torch.from_numpy(acc_in.uniforms).to(dev)
+        n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        host_out = torch.empty(2 * B, dtype=torch.int32).pin_memory()
+    stream.synchronize()
+
+    # ---- prefill: chunk-mean keys of every layer (timed on its own) --------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for x in L:
+        tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, stream=stream)
+    e1.record(stream)
+    stream.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    tokens_total = sum(lens)
+    prefill_bytes = layers * Hkv * (tokens_total * d * 2 + sum(C) * d * L[0].ck.element_size())
+
+    # ---- one decode step ----------------------------------------------------
+    def step(ev=None):
+        for x in L:
+            tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk, max_chunks=tail_count,
+                                stream=stream)
+            tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream)
+            tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream)
+            tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s, stream=stream)
+            tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+            tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].append((ev[0], ev[1]))
+                ev[0] = torch.cuda.Event(enable_timing=True)
+                ev[1] = torch.cuda.Event(enable_timing=True)
+        tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, stream=stream)
+        host_out[:B].copy_(n_acc, non_blocking=True)
+        host_out[B:].copy_(nxt, non_blocking=True)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+            stream.synchronize()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), []]
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(ev)
+            stream.synchronize()  # the step ends with the host having n_accepted / next_token
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    verify_ms = [a.elapsed_time(b) for a, b in ev[2]]
+    verify_avg_s = float(np.mean(verify_ms)) / 1e3
+
+    # ---- per-kernel breakdown (separate pass, events around each call) -----
+    names = ["chunk_refresh", "score", "topk", "sparse", "stream", "verify", "accept"]
+    per = {n: [] for n in names}
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            for x in L:
+                calls = [
+                    lambda: tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk,
+                                                max_chunks=tail_count, stream=stream),
+                    lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream),
+                    lambda: tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream),
+                    lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s, stream=stream),
+                    lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream),
+                    lambda: tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream),
+                ]
+                for n, fn in zip(names, calls):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    per[n].append((a, b))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, stream=stream)
+            b.record(stream)
+            per["accept"].append((a, b))
+        stream.synchronize()
+    us = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for n, v in per.items()}
+
+    # ---- algorithmic bytes --------------------------------------------------
+    kvb = 2  # bytes per stored K/V element
+    ckb = L[0].ck.element_size()
+    row = d * kvb
+    sel_tokens = sum(min(k * cs, n) for n in lens)
+    vis_stream = sum(min(S, n) + max(0, n - max(S, n - Wn)) for n in lens)
+    by = {
+        "chunk_refresh": Hkv * B * tail_count * (cs * row + d * ckb),
+        "score": Hkv * sum(C) * d * ckb + B * Hq * row + B * Hkv * c_max * 4,
+        "topk": B * Hkv * (sum(C) // B if B else 0) * 4 + B * Hkv * k * 4,
+        "sparse": Hkv * sel_tokens * 2 * row + B * Hkv * k * 4 + B * Hq * (row + d * 4 + 4),
+        "stream": Hkv * vis_stream * 2 * row + B * Hq * (row + d * 4 + 4),
+        "verify": Hkv * tokens_total * 2 * row + B * Hq * Q * (row + d * 4 + 4),
+        "accept": B * (2 * gamma + 1) * vocab * 4,
+    }
+    kernels = {n: {"us": round(us[n], 2), "GB_s": round(by[n] / (us[n] * 1e-6) / 1e9, 1),
+                   "bytes": int(by[n])} for n in names}
+    step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
+    verify_bytes = by["verify"]
+    achieved = verify_bytes / verify_avg_s / 1e9
+    traffic = read_traffic()
+    ms_per_step = elapsed / args.steps * 1e3
+
+    result = {
+        "metric": METRIC,
+        "value": round(args.steps / elapsed, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "context": lens if B > 1 else lens[0], "layers": layers, "chunk_size": cs, "budget": budget,
+                   "gamma": gamma, "verify_queries": Q, "n_sink": S, "window": Wn, "vocab": vocab,
+                   "chunk_key_dtype": str(ck_dt).replace("torch.", ""), "parallelism": "single GPU"},
+        "decode_attn_GB_s": round(step_bytes * args.steps / elapsed / 1e9, 1),
+        "decode_attn_hbm_frac": round(step_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "roofline": {"kernel": "verify_attn (attn_kernel, verify mode)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(verify_bytes),
+                     "avg_launch_us": round(verify_avg_s * 1e6, 2)},
+        "kernels": kernels,
+        "sparse_draft_pass_us": round(us["score"] + us["topk"] + us["sparse"], 2),
+        "prefill_chunk_keys": {"ms_all_layers": round(prefill_ms, 3),
+                               "GB_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},
+        "setup_s": round(time.perf_counter() - t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(L[0], lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_in, tdt)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(x, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_in, tdt):
+    """The fp64 oracle timed on this host: one layer of the workload (every
+    head of every sequence) plus one accept, scaled to the step (x layers)."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    to_bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    dt = "bf16" if tdt == torch.bfloat16 else "fp16"
+    Kb, Vb = to_bits(x.K), to_bits(x.V)
+    qv, qd = to_bits(x.qv), to_bits(x.qd)
+    Ksb, Vsb = to_bits(x.Ks), to_bits(x.Vs)
+    G = Hq // Hkv
+    base = x.kv.seq_base.cpu().numpy()
+    cap = x.kv.seq_cap.cpu().numpy()
+    scap = int(x.sd.seq_cap[0].item())
+    sbase = x.sd.seq_base.cpu().numpy()
+    t_layer = 0.0
+    for b, n in enumerate(lens):
+        for g in range(Hkv):
+            off = int(base[b]) + g * int(cap[b]) * d
+            K = oracle.widen(Kb[off:off + n * d].reshape(n, d), dt)
+            V = oracle.widen(Vb[off:off + n * d].reshape(n, d), dt)
+            ck = oracle.chunk_keys(K, n, cs)            # prefill: not timed
+            soff = int(sbase[b]) + g * scap * d
+            Ks = oracle.widen(Ksb[soff:soff + scap * d].reshape(scap, d), dt)
+            Vs = oracle.widen(Vsb[soff:soff + scap * d].reshape(scap, d), dt)
+            t0 = time.perf_counter()
+            c0 = max(0, (n - Q) // cs)
+            ck[c0:] = oracle.chunk_keys(K[c0 * cs:n], n - c0 * cs, cs)   # tail refresh
+            qg = np.stack([oracle.widen(qd[b, g * G + j], dt) for j in range(G)])
+            sel = oracle.select_topk(oracle.chunk_scores(qg, ck), k)
+            for j in range(G):
+                h = g * G + j
+                oracle.sparse_attn(qg[j], K, V, n, sel, cs)
+                # streaming positions in ring order; every slot of the ring is resident here
+                pos = oracle.stream_positions(n, S, Wn)
+                slots = [p if p < S else S + (p - S) % (scap - S) for p in pos]
+                oracle.attention(qg[j], Ks[slots], Vs[slots])
+                oracle.verify_attn(oracle.widen(qv[b, h], dt), K, V, n)
+            t_layer += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for b in range(acc_in.target.shape[0]):
+        oracle.accept(acc_in.target[b], acc_in.draft[b], acc_in.tokens[b], acc_in.uniforms[b], 1.0)
+    t_acc = time.perf_counter() - t0
+    t_step = t_layer * layers + t_acc
+    return {"value": round(1.0 / t_step, 6), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"fp64 numpy oracle, 1 of {layers} layers (all {Hkv} KV heads x {Hq} query heads, "
+                      f"{len(lens)} sequence(s)) + 1 accept, timed {t_layer + t_acc:.1f} s, scaled to "
+                      f"{layers} layers (per layer {t_layer:.2f} s)"}
+
+
+if __name__ == "__main__":
+    main()
