@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ck-dtype", default="kv", choices=["kv", "fp32"])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (a kernel of known traffic for HBM counters)")
     return ap.parse_args()
 
 
@@ -139,6 +141,7 @@ def main():
         l_v = torch.empty((B, Hq, Q), dtype=torch.float32, device=dev)
         ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Q, n_max), dev)
         ws_s = tf.workspace(tf.sparse_attn_workspace_size(B, Hq, Hkv, k, cs), dev)
+        ws_a = tf.workspace(tf.accept_workspace_size(B, gamma, vocab), dev)
         acc_in = synth.make_accept_inputs(B=B, gamma=gamma, vocab=vocab, seed=0)
         tgt = torch.from_numpy(acc_in.target).to(dev)
         drf = torch.from_numpy(acc_in.draft).to(dev)
@@ -161,69 +164,97 @@ def main():
     prefill_bytes = layers * Hkv * (tokens_total * d * 2 + sum(C) * d * L[0].ck.element_size())
 
     # ---- one decode step ----------------------------------------------------
-    def step(ev=None):
+    def layer_calls(x):
+        return [
+            ("chunk_refresh", lambda: tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk,
+                                                          max_chunks=tail_count, stream=stream)),
+            ("score", lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream)),
+            ("topk", lambda: tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream)),
+            ("sparse", lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s,
+                                              stream=stream)),
+            ("stream", lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream)),
+            ("verify", lambda: tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream)),
+        ]
+
+    def accept_call():
+        tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, ws=ws_a, stream=stream)
+
+    def step_gpu(verify_events=None):
         for x in L:
-            tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk, max_chunks=tail_count,
-                                stream=stream)
-            tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream)
-            tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream)
-            tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s, stream=stream)
-            tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream)
-            if ev is not None:
-                ev[0].record(stream)
-            tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-                ev[2].append((ev[0], ev[1]))
-                ev[0] = torch.cuda.Event(enable_timing=True)
-                ev[1] = torch.cuda.Event(enable_timing=True)
-        tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, stream=stream)
+            for name, fn in layer_calls(x):
+                if name == "verify" and verify_events is not None:
+                    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a_.record(stream)
+                    fn()
+                    b_.record(stream)
+                    verify_events.append((a_, b_))
+                else:
+                    fn()
+        accept_call()
+
+    def readback():
         host_out[:B].copy_(n_acc, non_blocking=True)
         host_out[B:].copy_(nxt, non_blocking=True)
+        stream.synchronize()  # the step ends with n_accepted / next_token on the host
 
     with torch.cuda.stream(stream):
+        # eager warm-up, then the step captured once as a HIP graph
         for _ in range(args.warmup):
-            step()
-            stream.synchronize()
+            step_gpu()
+            readback()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step_gpu()
+        for _ in range(args.warmup):
+            graph.replay()
+            readback()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), []]
+        # timed region 1: graph replays (the reported value)
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step(ev)
-            stream.synchronize()  # the step ends with the host having n_accepted / next_token
+            graph.replay()
+            readback()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    verify_ms = [a.elapsed_time(b) for a, b in ev[2]]
-    verify_avg_s = float(np.mean(verify_ms)) / 1e3
+        # timed region 2: the same steps launched eagerly, HIP events around
+        # every verify launch on the launch stream (roofline of that kernel)
+        vev = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step_gpu(vev)
+            readback()
+        torch.cuda.synchronize()
+        elapsed_eager = time.perf_counter() - t0
+    verify_eager_avg_s = float(np.mean([a_.elapsed_time(b_) for a_, b_ in vev])) / 1e3
 
-    # ---- per-kernel breakdown (separate pass, events around each call) -----
+    # ---- per-kernel breakdown: one graph per kernel kind, one launch per layer
     names = ["chunk_refresh", "score", "topk", "sparse", "stream", "verify", "accept"]
-    per = {n: [] for n in names}
+    us = {}
     with torch.cuda.stream(stream):
-        for _ in range(3):
-            for x in L:
-                calls = [
-                    lambda: tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk,
-                                                max_chunks=tail_count, stream=stream),
-                    lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream),
-                    lambda: tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream),
-                    lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s, stream=stream),
-                    lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream),
-                    lambda: tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream),
-                ]
-                for n, fn in zip(names, calls):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    fn()
-                    b.record(stream)
-                    per[n].append((a, b))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, stream=stream)
-            b.record(stream)
-            per["accept"].append((a, b))
-        stream.synchronize()
-    us = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for n, v in per.items()}
+        for n in names:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                if n == "accept":
+                    accept_call()
+                else:
+                    for x in L:
+                        dict(layer_calls(x))[n]()
+            g.replay()
+            stream.synchronize()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            a_.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b_.record(stream)
+            stream.synchronize()
+            us[n] = a_.elapsed_time(b_) * 1e3 / (reps * (1 if n == "accept" else layers))
+        if args.copy_calibration:
+            src = torch.empty(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB read + 1 GiB written
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            stream.synchronize()
+    verify_avg_s = us["verify"] * 1e-6
 
     # ---- algorithmic bytes --------------------------------------------------
     kvb = 2  # bytes per stored K/V element
@@ -256,6 +287,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "launch": "HIP graph of the whole step, replayed; n_accepted/next_token read back each step",
+        "eager_steps_per_s": round(args.steps / elapsed_eager, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -268,12 +301,16 @@ def main():
         "decode_attn_GB_s": round(step_bytes * args.steps / elapsed / 1e9, 1),
         "decode_attn_hbm_frac": round(step_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": int(step_bytes),
-        "roofline": {"kernel": "verify_attn (attn_kernel, verify mode)", "bound": "hbm",
+        "roofline": {"kernel": "verify_attn (attn_kernel + combine_kernel, verify mode)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(verify_bytes),
-                     "avg_launch_us": round(verify_avg_s * 1e6, 2)},
+                     "avg_launch_us": round(verify_avg_s * 1e6, 2),
+                     "timing": "HIP events on the launch stream around 5 replays of a graph of the step's "
+                               "verify launches (one per layer, back to back)",
+                     "eager_avg_launch_us": round(verify_eager_avg_s * 1e6, 2)},
         "kernels": kernels,
+        "kernels_timing": "per kind: a HIP graph of its launches for every layer, replayed 5x between events",
         "sparse_draft_pass_us": round(us["score"] + us["topk"] + us["sparse"], 2),
         "prefill_chunk_keys": {"ms_all_layers": round(prefill_ms, 3),
                                "GB_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},

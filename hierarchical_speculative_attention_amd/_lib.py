@@ -21,7 +21,7 @@ TF_DTYPE_FP16, TF_DTYPE_BF16, TF_DTYPE_FP32 = 1, 2, 3
 TF_ACCEPT_PROBS = 1
 
 EXPORTS = [
-    "tf_status_string", "tf_last_error_detail", "tf_workspace_clear",
+    "tf_status_string", "tf_last_error_detail",
     "tf_build_chunk_keys", "tf_score_chunks", "tf_select_topk", "tf_select_topk_workspace_size",
     "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
@@ -62,7 +62,6 @@ def lib() -> ctypes.CDLL:
     sig = {
         "tf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tf_last_error_detail": (ctypes.c_char_p, []),
-        "tf_workspace_clear": (ctypes.c_int, [vp, sz, vp]),
         "tf_build_chunk_keys": (ctypes.c_int, [vp, dp, i32, vp, i32, vp, dp, vp]),
         "tf_score_chunks": (ctypes.c_int, [vp, i32, i32, vp, dp, vp, i32, vp]),
         "tf_select_topk": (ctypes.c_int, [vp, i32, i32, i32, vp, i32, vp, vp, sz, vp]),
@@ -139,15 +138,11 @@ class KVDesc:
 # ---------------------------------------------------------------------------
 
 def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """A zero-filled workspace (counters start at zero; each call leaves
-    them at zero)."""
+    """A workspace of the size a *_workspace_size() function returned (or
+    None when that size is 0).  It needs no initialisation."""
     if nbytes == 0:
         return None
-    return torch.zeros(int(nbytes), dtype=torch.uint8, device=device)
-
-
-def workspace_clear(ws: torch.Tensor, stream=None):
-    _check(lib().tf_workspace_clear(_ptr(ws), ws.numel(), _stream(stream, ws.device)), "tf_workspace_clear")
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
 
 
 def verify_attn_workspace_size(B, Hq, H, Q, max_len) -> int:

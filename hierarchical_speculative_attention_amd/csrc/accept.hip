@@ -4,93 +4,118 @@
 // rejection draw the next token from max(0, p - q) normalised; if every draft
 // is kept, draw a bonus token from the target's next row.
 //
-// One 1024-thread workgroup per sequence, everything in fp64 so that every
-// decision is taken in the same precision as the fp64 reference.  Rows are
-// reduced only as far as the chain gets: position i needs the normaliser of
-// target row i and draft row i; the final draw needs one more pass over one
-// row.  The draw is an inverse CDF: thread t owns a contiguous slice of the
-// vocabulary, a block prefix sum of the slice totals gives each slice's
-// starting running sum, and the slice holding the crossing scans itself in
-// order.
+// Everything runs in fp64 so that every decision is taken in the same
+// precision as the fp64 reference.  Two kernels:
+//  1. row statistics, spread over (vocabulary slice, row, sequence): the
+//     largest logit of the slice (with its lowest index) and the slice's sum
+//     of exp(x / T - slice max / T);
+//  2. per sequence: merge the slices of the rows it needs, walk the chain,
+//     then draw the next token by inverse CDF.  Each thread sums the weights
+//     of its contiguous vocabulary slice; a block prefix sum in thread order
+//     locates the slice whose running sum first passes u * total, and one
+//     wave re-evaluates that slice (one entry per lane, prefix sum across
+//     lanes) to find the entry.
 #include "tf_internal.h"
 
 namespace tfk {
 
-constexpr int kAccThreads = 1024;
+constexpr int kStatThreads = 256;
+constexpr int kStatSlice = 4096;       // vocabulary entries per statistics workgroup
+constexpr int kDrawThreads = 1024;
+constexpr int kDrawIpt = 64;           // vocabulary entries per draw thread (at most one wave)
 
-struct RowDist {
-  // p_v = exp(x_v / T - zmax) / Z   (T > 0); one-hot at amax (T == 0);
-  // x_v as given (probabilities mode).
-  int mode;  // 0 softmax, 1 greedy, 2 probabilities
-  double zmax;
-  double Z;
-  int amax;
+struct SliceStat {
+  float mx;   // largest logit in the slice
+  int amax;   // its lowest index
+  double z;   // sum over the slice of exp(x / T - mx / T)
 };
 
-__device__ __forceinline__ double block_sum_d(double x, double* s_red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  if (lane == 0) s_red[w] = x;
-  __syncthreads();
-  double t = 0.0;
-  if (threadIdx.x < 64) {
-    t = threadIdx.x < kAccThreads / 64 ? s_red[threadIdx.x] : 0.0;
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) t += __shfl_xor(t, off);
-    if (threadIdx.x == 0) s_red[32] = t;
-  }
-  __syncthreads();
-  const double r = s_red[32];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
 }
 
-// Max value and its lowest index over the row.
-__device__ __forceinline__ void block_argmax(const float* row, int V, double* s_red, int* s_ri, float* mx, int* am) {
-  float best = -__builtin_huge_valf();
+// ---------------------------------------------------------------------------
+// Kernel 1: one workgroup per (slice, row, sequence), flattened into
+// grid.x = slice + nslices * (row + nrows * b).  Rows 0..gamma are target
+// rows, rows gamma+1 .. 2*gamma are draft rows 0..gamma-1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(const float* __restrict__ target,
+                                                                    const float* __restrict__ draft, int32_t gamma,
+                                                                    int32_t V, float temperature, int32_t nslices,
+                                                                    SliceStat* __restrict__ stats) {
+  __shared__ float s_v[kStatThreads / 64];
+  __shared__ int s_i[kStatThreads / 64];
+  __shared__ double s_z[kStatThreads / 64];
+  const int nrows = 2 * gamma + 1;
+  const int slice = (int)(blockIdx.x % (unsigned)nslices);
+  const int r = (int)((blockIdx.x / (unsigned)nslices) % (unsigned)nrows);
+  const int b = (int)(blockIdx.x / ((unsigned)nslices * (unsigned)nrows));
+  const float* row = (r <= gamma) ? target + ((size_t)b * (gamma + 1) + r) * V
+                                  : draft + ((size_t)b * gamma + (r - gamma - 1)) * V;
+  const int v0 = slice * kStatSlice, v1 = min(V, v0 + kStatSlice);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float bv = -__builtin_huge_valf();
   int bi = 0x7fffffff;
-  for (int v = threadIdx.x; v < V; v += kAccThreads) {
+  for (int v = v0 + threadIdx.x; v < v1; v += kStatThreads) {
     const float x = row[v];
-    if (x > best || (x == best && v < bi)) {
-      best = x;
+    if (better(x, v, bv, bi)) {
+      bv = x;
       bi = v;
     }
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float ob = __shfl_xor(best, off);
+    const float ov = __shfl_xor(bv, off);
     const int oi = __shfl_xor(bi, off);
-    if (ob > best || (ob == best && oi < bi)) {
-      best = ob;
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
       bi = oi;
     }
   }
   if (lane == 0) {
-    s_red[w] = (double)best;
-    s_ri[w] = bi;
+    s_v[w] = bv;
+    s_i[w] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double b0 = s_red[0];
-    int i0 = s_ri[0];
-    for (int j = 1; j < kAccThreads / 64; ++j) {
-      if (s_red[j] > b0 || (s_red[j] == b0 && s_ri[j] < i0)) {
-        b0 = s_red[j];
-        i0 = s_ri[j];
-      }
+  bv = s_v[0];
+  bi = s_i[0];
+#pragma unroll
+  for (int x = 1; x < kStatThreads / 64; ++x)
+    if (better(s_v[x], s_i[x], bv, bi)) {
+      bv = s_v[x];
+      bi = s_i[x];
     }
-    s_red[33] = b0;
-    s_ri[33] = i0;
+  double z = 0.0;
+  if (temperature > 0.f) {
+    const double t = (double)temperature;
+    const double zm = (double)bv / t;
+    for (int v = v0 + threadIdx.x; v < v1; v += kStatThreads) z += exp((double)row[v] / t - zm);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if (lane == 0) s_z[w] = z;
+    __syncthreads();
+    z = 0.0;
+#pragma unroll
+    for (int x = 0; x < kStatThreads / 64; ++x) z += s_z[x];
   }
-  __syncthreads();
-  *mx = (float)s_red[33];
-  *am = s_ri[33];
-  __syncthreads();
+  if (threadIdx.x == 0) {
+    SliceStat st;
+    st.mx = bv;
+    st.amax = bi;
+    st.z = z;
+    stats[((size_t)b * nrows + r) * nslices + slice] = st;
+  }
 }
 
-__device__ RowDist make_dist(const float* row, int V, float temperature, int probs, double* s_red, int* s_ri) {
+// Distribution of one row after merging its slices.
+struct RowDist {
+  int mode;     // 0 softmax(x / T), 1 greedy one-hot, 2 probabilities as given
+  double zmax;  // max x / T
+  double Z;     // sum of exp(x / T - zmax)
+  int amax;
+};
+
+__device__ RowDist merge_row(const SliceStat* st, int nslices, float temperature, int probs) {
   RowDist d;
   d.zmax = 0.0;
   d.Z = 1.0;
@@ -99,21 +124,26 @@ __device__ RowDist make_dist(const float* row, int V, float temperature, int pro
     d.mode = 2;
     return d;
   }
-  float mx;
-  int am;
-  block_argmax(row, V, s_red, s_ri, &mx, &am);
-  d.amax = am;
+  float bv = st[0].mx;
+  int bi = st[0].amax;
+  for (int s = 1; s < nslices; ++s)
+    if (better(st[s].mx, st[s].amax, bv, bi)) {
+      bv = st[s].mx;
+      bi = st[s].amax;
+    }
+  d.amax = bi;
   if (temperature == 0.f) {
     d.mode = 1;
     return d;
   }
   d.mode = 0;
-  // z_v = x_v / T; the largest z comes from the largest x (division by T > 0
-  // is monotone), so zmax is that value divided by T.
-  d.zmax = (double)mx / (double)temperature;
-  double s = 0.0;
-  for (int v = threadIdx.x; v < V; v += kAccThreads) s += exp((double)row[v] / (double)temperature - d.zmax);
-  d.Z = block_sum_d(s, s_red);
+  const double t = (double)temperature;
+  // z_v = x_v / T; division by T > 0 is monotone, so max z = (max x) / T.
+  d.zmax = (double)bv / t;
+  double Z = 0.0;
+  for (int s = 0; s < nslices; ++s)
+    if (st[s].z > 0.0) Z += st[s].z * exp((double)st[s].mx / t - d.zmax);
+  d.Z = Z;
   return d;
 }
 
@@ -123,122 +153,177 @@ __device__ __forceinline__ double dist_p(const RowDist& d, const float* row, int
   return exp((double)row[v] / (double)temperature - d.zmax) / d.Z;
 }
 
-__global__ __launch_bounds__(kAccThreads) void accept_kernel(const float* __restrict__ target,
-                                                             const float* __restrict__ draft,
-                                                             const int32_t* __restrict__ tokens,
-                                                             const double* __restrict__ uniforms, int32_t gamma,
-                                                             int32_t V, float temperature, int32_t probs,
-                                                             int32_t* __restrict__ n_acc, int32_t* __restrict__ next) {
-  __shared__ double s_red[40];
-  __shared__ int s_ri[40];
-  __shared__ double s_scan[kAccThreads / 64 + 1];
-  __shared__ int s_found;
-  const int b = blockIdx.x;
-  const float* trow0 = target + (size_t)b * (gamma + 1) * V;
-  const float* drow0 = draft + (size_t)b * gamma * V;
-  const double* u = uniforms + (size_t)b * (gamma + 1);
-
-  int j = gamma;
-  RowDist dp, dq;
-  for (int i = 0; i < gamma; ++i) {
-    const float* tr = trow0 + (size_t)i * V;
-    const float* dr = drow0 + (size_t)i * V;
-    dp = make_dist(tr, V, temperature, probs, s_red, s_ri);
-    dq = make_dist(dr, V, temperature, probs, s_red, s_ri);
-    const int x = tokens[(size_t)b * gamma + i];
-    const bool in_vocab = x >= 0 && x < V;  // an out-of-range token is rejected
-    const double px = in_vocab ? dist_p(dp, tr, x, temperature) : 0.0;
-    const double qx = in_vocab ? dist_p(dq, dr, x, temperature) : 0.0;
-    bool keep = false;
-    if (px > 0.0) {
-      const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
-      keep = alpha >= u[i];
-    }
-    if (!keep) {
-      j = i;
-      break;
-    }
-  }
-
-  // Weights of the final draw, evaluated element by element:
-  //   rejected at j : r_v = max(0, p_j(v) - q_j(v))   (p_j if that sums to 0)
-  //   all kept      : r_v = p_gamma(v)
-  const float* tr = trow0 + (size_t)j * V;
-  const float* dr = drow0 + (size_t)(j < gamma ? j : 0) * V;
-  bool residual = j < gamma;
-  if (!residual) dp = make_dist(tr, V, temperature, probs, s_red, s_ri);
-
-  const int ipt = (V + kAccThreads - 1) / kAccThreads;
-  const int v0 = threadIdx.x * ipt, v1 = min(V, v0 + ipt);
-  double local = 0.0;
-  for (int v = v0; v < v1; ++v) {
-    const double p = dist_p(dp, tr, v, temperature);
-    local += residual ? fmax(0.0, p - dist_p(dq, dr, v, temperature)) : p;
-  }
-  double total = block_sum_d(local, s_red);
-  if (residual && total == 0.0) {
-    residual = false;  // fall back to p_j
-    local = 0.0;
-    for (int v = v0; v < v1; ++v) local += dist_p(dp, tr, v, temperature);
-    total = block_sum_d(local, s_red);
-  }
-
-  // Exclusive prefix of the slice totals in thread order (fp64).
+// Prefix sums over the 1024 threads in thread order (fp64): returns the
+// inclusive sum, stores the exclusive one in *excl and the block total in
+// *s_total.
+__device__ __forceinline__ double block_scan(double x, double* s_scan, double* s_total, double* excl) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double incl = local;
+  double incl = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
+  double ex = __shfl_up(incl, 1);
+  if (lane == 0) ex = 0.0;
   if (lane == 63) s_scan[w] = incl;
-  if (threadIdx.x == 0) s_found = 0x7fffffff;
   __syncthreads();
-  double excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.0;
-  double wave_off = 0.0;
-  for (int x = 0; x < w; ++x) wave_off += s_scan[x];
-  const double run0 = wave_off + excl;
-  const double tgt = u[gamma] * total;
+  double off_w = 0.0;
+  for (int x2 = 0; x2 < w; ++x2) off_w += s_scan[x2];
+  if (threadIdx.x == kDrawThreads - 1) *s_total = off_w + incl;
+  __syncthreads();
+  *excl = off_w + ex;
+  return off_w + incl;
+}
 
-  // The crossing: smallest v with running sum > tgt.
-  int hit = 0x7fffffff;
+// ---------------------------------------------------------------------------
+// Kernel 2: grid (B), 1024 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
+    const double* __restrict__ uniforms, int32_t gamma, int32_t V, float temperature, int32_t probs,
+    const SliceStat* __restrict__ stats, int32_t nslices, int32_t* __restrict__ n_acc, int32_t* __restrict__ next) {
+  __shared__ double s_scan[kDrawThreads / 64];
+  __shared__ double s_tot;
+  __shared__ int s_j;
+  __shared__ int s_found;
+  __shared__ int s_last;
+  const int b = blockIdx.x;
+  const int nrows = 2 * gamma + 1;
+  const SliceStat* st = stats + (size_t)b * nrows * nslices;
+  const float* trow0 = target + (size_t)b * (gamma + 1) * V;
+  const float* drow0 = draft + (size_t)b * gamma * V;
+  const double* u = uniforms + (size_t)b * (gamma + 1);
+
+  // ---- the chain: one thread, a handful of exp() calls ----------------------
+  if (threadIdx.x == 0) {
+    int j = gamma;
+    for (int i = 0; i < gamma; ++i) {
+      const int x = tokens[(size_t)b * gamma + i];
+      bool keep = false;
+      if (x >= 0 && x < V) {  // a token outside [0, V) is never kept
+        const RowDist dp = merge_row(st + (size_t)i * nslices, nslices, temperature, probs);
+        const RowDist dq = merge_row(st + (size_t)(gamma + 1 + i) * nslices, nslices, temperature, probs);
+        const double px = dist_p(dp, trow0 + (size_t)i * V, x, temperature);
+        const double qx = dist_p(dq, drow0 + (size_t)i * V, x, temperature);
+        if (px > 0.0) {
+          const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
+          keep = alpha >= u[i];
+        }
+      }
+      if (!keep) {
+        j = i;
+        break;
+      }
+    }
+    s_j = j;
+  }
+  __syncthreads();
+  const int j = s_j;
+  bool residual = j < gamma;
+  const float* tr = trow0 + (size_t)j * V;
+  const float* dr = drow0 + (size_t)(residual ? j : 0) * V;
+  const RowDist dp = merge_row(st + (size_t)j * nslices, nslices, temperature, probs);
+  const RowDist dq = residual ? merge_row(st + (size_t)(gamma + 1 + j) * nslices, nslices, temperature, probs) : dp;
+
+  // ---- pass 1: each thread sums the weights of its contiguous slice --------
+  const int ipt = (V + kDrawThreads - 1) / kDrawThreads;  // <= 64 (host-checked)
+  const int v0 = threadIdx.x * ipt, v1 = min(V, v0 + ipt);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double local = 0.0;
   int last_pos = -1;
-  double run = run0;
   for (int v = v0; v < v1; ++v) {
     const double p = dist_p(dp, tr, v, temperature);
     const double r = residual ? fmax(0.0, p - dist_p(dq, dr, v, temperature)) : p;
     if (r > 0.0) last_pos = v;
-    run += r;
-    if (run > tgt && hit == 0x7fffffff) hit = v;
+    local += r;
   }
-  atomicMin(&s_found, hit);
-  // Fallback (running sum never passes u * total through rounding): the last
-  // index with positive weight.
-  __syncthreads();
-  int found = s_found;
-  if (found == 0x7fffffff) {
-    __syncthreads();
-    if (threadIdx.x == 0) s_found = -1;
-    __syncthreads();
-    atomicMax(&s_found, last_pos);
-    __syncthreads();
-    found = s_found;
+  double before;
+  double total = block_scan(local, s_scan, &s_tot, &before);
+  if (residual && s_tot == 0.0) {
+    // max(0, p - q) vanished (only through rounding): draw from p_j instead.
+    residual = false;
+    local = 0.0;
+    last_pos = -1;
+    for (int v = v0; v < v1; ++v) {
+      const double p = dist_p(dp, tr, v, temperature);
+      if (p > 0.0) last_pos = v;
+      local += p;
+    }
+    total = block_scan(local, s_scan, &s_tot, &before);
   }
+  // `total` is this thread's inclusive running sum; s_tot the row's sum.
+  const double tgt = u[gamma] * s_tot;
   if (threadIdx.x == 0) {
-    n_acc[b] = j;
-    next[b] = found;
+    s_found = 0x7fffffff;
+    s_last = -1;
+  }
+  __syncthreads();
+  if (total > tgt) atomicMin(&s_found, (int)threadIdx.x);  // first slice whose end passes the target
+  atomicMax(&s_last, last_pos);
+  __syncthreads();
+  const int tstar = s_found;
+  if (tstar == 0x7fffffff) {
+    // the running sum never passes u * total (rounding): the last index with
+    // positive weight
+    if (threadIdx.x == 0) {
+      n_acc[b] = j;
+      next[b] = s_last;
+    }
+    return;
+  }
+  if (threadIdx.x == tstar) s_tot = before;  // running sum before slice tstar
+  __syncthreads();
+  // ---- pass 2: one wave re-evaluates slice tstar, one element per lane ------
+  if (w == 0) {
+    const int v = tstar * ipt + lane;
+    double r = 0.0;
+    if (lane < ipt && v < V) {
+      const double p = dist_p(dp, tr, v, temperature);
+      r = residual ? fmax(0.0, p - dist_p(dq, dr, v, temperature)) : p;
+    }
+    double run = r;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(run, off);
+      if (lane >= off) run += y;
+    }
+    run += s_tot;
+    const unsigned long long hit = __ballot(r > 0.0 && run > tgt);
+    const unsigned long long pos = __ballot(r > 0.0);
+    if (lane == 0) {
+      n_acc[b] = j;
+      // without a crossing inside the slice (rounding), its last positive entry
+      next[b] = hit ? tstar * ipt + (int)__builtin_ctzll(hit)
+                    : (pos ? tstar * ipt + 63 - (int)__builtin_clzll(pos) : s_last);
+    }
   }
 }
 
-size_t accept_ws_bytes(int32_t, int32_t, int32_t) { return 0; }
+size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
+  if (B < 1 || gamma < 0 || V < 1) return 0;
+  const size_t nslices = (size_t)(V + kStatSlice - 1) / kStatSlice;
+  return ((size_t)B * (2 * gamma + 1) * nslices * sizeof(SliceStat) + 255) & ~(size_t)255;
+}
+
+int32_t accept_max_vocab() { return kDrawThreads * kDrawIpt; }
 
 hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens,
                          const double* uniforms, int32_t B, int32_t gamma, int32_t V,
                          float temperature, int32_t flags, int32_t* n_acc, int32_t* next,
-                         void*, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(kAccThreads), 0, stream, target, draft, tokens, uniforms, gamma, V,
-                     temperature, (int32_t)((flags & TF_ACCEPT_PROBS) != 0), n_acc, next);
+                         void* ws, hipStream_t stream) {
+  const int probs = (flags & TF_ACCEPT_PROBS) != 0;
+  const int nslices = (V + kStatSlice - 1) / kStatSlice;
+  SliceStat* stats = (SliceStat*)ws;
+  if (!probs) {
+    const unsigned blocks = (unsigned)nslices * (unsigned)(2 * gamma + 1) * (unsigned)B;
+    hipLaunchKernelGGL(accept_stats_kernel, dim3(blocks), dim3(kStatThreads), 0, stream, target, draft, gamma, V,
+                       temperature, nslices, stats);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(accept_draw_kernel, dim3(B), dim3(kDrawThreads), 0, stream, target, draft, tokens, uniforms,
+                     gamma, V, temperature, probs, stats, nslices, n_acc, next);
   return hipGetLastError();
 }
 

@@ -69,9 +69,10 @@ int check_ws(void* ws, size_t have, size_t need) {
     if (_s != TF_OK) return _s; \
   } while (0)
 
-// Target number of workgroups per launch: a few per compute unit.
-constexpr int kVerifyTargetWgs = 1024;
-constexpr int kSparseTargetWgs = 1024;
+// Target number of workgroups per launch: two per compute unit (256 CUs),
+// one resident round at two waves per SIMD.
+constexpr int kVerifyTargetWgs = 512;
+constexpr int kSparseTargetWgs = 512;
 
 void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, const tf_kv_desc* kv, int Hq, int Qn,
                  float* out, float* lse) {
@@ -97,7 +98,6 @@ void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, 
   a.lse = lse;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  a.counters = nullptr;
   a.scale_ln = 1.0f / std::sqrt((float)tfk::kHeadDim);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)tfk::kHeadDim));
 }
@@ -108,9 +108,8 @@ void fill_plan(tfk::AttnArgs& a, const tfk::SplitPlan& p, void* ws) {
   a.rows_pad = p.rows_pad;
   if (p.total_bytes) {
     char* w = (char*)ws;
-    a.counters = (int32_t*)w;
-    a.part_ml = (float*)(w + p.counter_bytes);
-    a.part_o = (float*)(w + p.counter_bytes + p.part_ml_bytes);
+    a.part_ml = (float*)w;
+    a.part_o = (float*)(w + p.part_ml_bytes);
   }
 }
 
@@ -128,12 +127,6 @@ TF_EXPORT const char* tf_status_string(int status) {
 }
 
 TF_EXPORT const char* tf_last_error_detail(void) { return g_detail; }
-
-TF_EXPORT int tf_workspace_clear(void* ws, size_t ws_bytes, tf_stream_t stream) {
-  if (ws_bytes == 0) return ok();
-  TRY(check_ptr(ws, "ws", 16));
-  return check_hip(tfk::launch_clear(ws, ws_bytes, (hipStream_t)stream), "tf_workspace_clear");
-}
 
 // ---------------------------------------------------------------------------
 // a1
@@ -262,7 +255,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
   if (plan.tpw < 128) plan.tpw = 128;
   plan.nsplit = 1;
   plan.rows_pad = ((a.rows + 15) / 16) * 16;
-  plan.part_o_bytes = plan.part_ml_bytes = plan.counter_bytes = plan.total_bytes = 0;
+  plan.part_o_bytes = plan.part_ml_bytes = plan.total_bytes = 0;
   fill_plan(a, plan, nullptr);
   return check_hip(tfk::launch_attn(sd->dtype, tfk::kStream, a, (hipStream_t)stream), "tf_stream_attn");
 }
@@ -313,7 +306,10 @@ TF_EXPORT int tf_accept(const float* target, const float* draft, const int32_t* 
   if (!(temperature >= 0.f) || std::isinf(temperature))
     return fail(TF_ERR_INVALID_ARG, "temperature must be finite and >= 0");
   if (flags & ~TF_ACCEPT_PROBS) return fail(TF_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if (B > 0x7fffffff / 2) return fail(TF_ERR_UNSUPPORTED, "B too large");
+  if (V > tfk::accept_max_vocab()) return fail(TF_ERR_UNSUPPORTED, "V=%d above %d", V, tfk::accept_max_vocab());
+  if (gamma > 1024) return fail(TF_ERR_UNSUPPORTED, "gamma above 1024");
+  if ((long)B * (2 * gamma + 1) * ((V + 4095) / 4096) > 0x7fffffffL)
+    return fail(TF_ERR_UNSUPPORTED, "B * (2 * gamma + 1) * ceil(V / 4096) above 2^31 - 1");
   if (B == 0) return ok();
   TRY(check_ptr(target, "target", 4));
   if (gamma > 0) {
@@ -328,27 +324,3 @@ TF_EXPORT int tf_accept(const float* target, const float* draft, const int32_t* 
                                       n_accepted, next_token, ws, (hipStream_t)stream),
                    "tf_accept");
 }
-
-// ---------------------------------------------------------------------------
-// workspace clear: a fill kernel (no memset node, safe under graph capture)
-// ---------------------------------------------------------------------------
-namespace tfk {
-
-__global__ void clear_kernel(uint32_t* p, size_t n_words, unsigned char* tail, size_t n_tail) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t j = i; j < n_words; j += stride) p[j] = 0u;
-  if (i < n_tail) tail[i] = 0;
-}
-
-hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream) {
-  const size_t words = bytes / 4, tail = bytes % 4;
-  size_t blocks = (words + 255) / 256;
-  if (blocks < 1) blocks = 1;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t*)ws, words,
-                     (unsigned char*)ws + words * 4, tail);
-  return hipGetLastError();
-}
-
-}  // namespace tfk

@@ -8,11 +8,12 @@
 // head); a virtual token is a cache row (verify), a row of a selected chunk
 // (sparse) or a visible streaming position (stream).  Wave w walks 32-token
 // tiles w, w+4, w+8, ... of its workgroup's range, keeping an online softmax
-// per query row in registers.  The four waves merge through LDS; when a
+// per query row in registers, with the next tile's loads in flight while it
+// consumes the current one.  The four waves merge through LDS; when a
 // (sequence, head) has several splits, each writes an unnormalised partial
-// (max, sum, 128 accumulators per row) and the last workgroup to finish
-// (device-scope counter) merges them in split order, so results do not
-// depend on scheduling.
+// (max, sum, 128 accumulators per row) and a small second kernel merges them
+// in split order, so results do not depend on scheduling and no device-wide
+// fence (an L2 write-back on this chip) is needed.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_{bf16,f16}; A row / B column = lane % 16,
 // k-slots 8 * (lane / 16) + e; C column = lane % 16, C rows 4 * (lane / 16) + r):
@@ -127,17 +128,133 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
   return slot < g.cap ? slot : -1;
 }
 
+// One 32-token tile of a wave: two 16-token subtiles of K and V in MFMA
+// A-operand layout (lane (t, g): dims 32s + 8g .. +8 of token t, s = 0..3).
+template <int DT>
+struct Tile {
+  typename MT<DT>::V8 k0[4], k1[4], v0[4], v1[4];
+  unsigned mk0, mk1;  // bit t: token t of subtile 0 / 1 is a valid row
+  int t0;             // first virtual token of the tile
+};
+
+template <int DT, int MODE>
+__device__ __forceinline__ void load_tile(Tile<DT>& T, const AttnArgs& a, const Geo& geo, int t0, int v1,
+                                          const int* s_idx, int chunk_lo, const uint16_t* Kb,
+                                          const uint16_t* Vb, int lq, int lg) {
+  using V8 = typename MT<DT>::V8;
+  const int r0 = map_row<MODE>(a, geo, t0 + lq, v1, s_idx, chunk_lo);
+  const int r1 = map_row<MODE>(a, geo, t0 + 16 + lq, v1, s_idx, chunk_lo);
+  T.mk0 = (unsigned)(__ballot(r0 >= 0) & 0xFFFFull);
+  T.mk1 = (unsigned)(__ballot(r1 >= 0) & 0xFFFFull);
+  T.t0 = t0;
+  // Rows that hold nothing read row 0 (in bounds, cached) and are masked.
+  const size_t o0 = (size_t)(r0 < 0 ? 0 : r0) * kHeadDim + 8 * lg;
+  const size_t o1 = (size_t)(r1 < 0 ? 0 : r1) * kHeadDim + 8 * lg;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    T.k0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o0 + 32 * s));
+    T.k1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o1 + 32 * s));
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    T.v0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o0 + 32 * s));
+    T.v1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o1 + 32 * s));
+  }
+}
+
+// Online-softmax update of one wave with one tile.
 template <int DT, int MODE, int NQT>
-__global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
+__device__ __forceinline__ void process_tile(const Tile<DT>& T, const typename MT<DT>::V8 (&qreg)[NQT][4],
+                                             const typename MT<DT>::V8 (&sel)[2], const int (&lim)[NQT],
+                                             int lim_min, f32x4 (&acc)[NQT][8], float (&m_run)[NQT],
+                                             float (&l_run)[NQT], float c2, int lg) {
+  using M = MT<DT>;
+  using V8 = typename M::V8;
+  using S = typename M::S;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // Whole tile visible to every row: no per-element masking needed.
+  const bool full = (T.mk0 & T.mk1) == 0xFFFFu && (MODE != kVerify || T.t0 + 31 <= lim_min);
+  V8 ph[NQT], pl[NQT];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    f32x4 s0 = zero4, s1 = zero4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      s0 = M::mma(T.k0[s], qreg[qt][s], s0);
+      s1 = M::mma(T.k1[s], qreg[qt][s], s1);
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * lg + r;
+        const bool vis0 = ((T.mk0 >> j) & 1u) && (MODE != kVerify || T.t0 + j <= lim[qt]);
+        const bool vis1 = ((T.mk1 >> j) & 1u) && (MODE != kVerify || T.t0 + 16 + j <= lim[qt]);
+        s0[r] = vis0 ? s0[r] : kNegInf;
+        s1[r] = vis1 ? s1[r] : kNegInf;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run[qt], mx);
+    // Rescale only when some row's running max moved (rare once it settles).
+    if (__ballot(m_new != m_run[qt]) != 0ull) {
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run[qt] - m_new) * c2);
+      l_run[qt] *= alpha;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) acc[qt][bb] *= alpha;
+      m_run[qt] = m_new;
+    }
+    const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
+    float psum = 0.f;
+    V8 hi, lo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p0 = fast_exp2(fmaf(s0[r], c2, -mc));
+      const float p1 = fast_exp2(fmaf(s1[r], c2, -mc));
+      psum += p0 + p1;
+      const S h0 = (S)p0, h1 = (S)p1;
+      hi[r] = h0;
+      hi[4 + r] = h1;
+      lo[r] = (S)(p0 - (float)h0);
+      lo[4 + r] = (S)(p1 - (float)h1);
+    }
+    ph[qt] = hi;
+    pl[qt] = lo;
+    l_run[qt] += psum;
+  }
+  // Values: move tokens onto the k axis, then O^T += V^T . P^T.
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const f32x4 t0v = M::mma(T.v0[bb >> 1], sel[bb & 1], zero4);
+    const f32x4 t1v = M::mma(T.v1[bb >> 1], sel[bb & 1], zero4);
+    V8 av;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      av[r] = (S)t0v[r];
+      av[4 + r] = (S)t1v[r];
+    }
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
+      acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
+    }
+  }
+}
+
+// One query tile fits two waves per SIMD (<= 256 registers, no spills) with
+// the double-buffered tile; more query tiles run one wave per SIMD.
+template <int DT, int MODE, int NQT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
+void attn_kernel(const AttnArgs a) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr int kMaxIdx = 4096 / 1 + 2;  // chunk slots per workgroup (tpw <= 4096, cs >= 1)
   __shared__ int s_idx[MODE == kSparse ? kMaxIdx : 1];
-  __shared__ float s_o[4][16][132];
+  __shared__ __attribute__((aligned(16))) float s_o[4][16][132];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -178,6 +295,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     }
     lim[qt] = (MODE == kVerify) ? geo.n - a.Qn + (row % a.Qn) : 0x7fffffff;
   }
+  const int lim_min = (MODE == kVerify) ? geo.n - a.Qn : 0x7fffffff;
 
   // Selection matrices: column j of half h picks dim 16h + j of a 32-dim k-window.
   V8 sel[2];
@@ -196,95 +314,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     for (int bb = 0; bb < 8; ++bb) acc[qt][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = v0 + kTile * w; t0 < v1; t0 += 4 * kTile) {
-    // ---- rows of the two 16-token subtiles, loads of K and V --------------
-    const int r0 = map_row<MODE>(a, geo, t0 + lq, v1, s_idx, chunk_lo);
-    const int r1 = map_row<MODE>(a, geo, t0 + 16 + lq, v1, s_idx, chunk_lo);
-    const unsigned mk0 = (unsigned)(__ballot(r0 >= 0) & 0xFFFFull);
-    const unsigned mk1 = (unsigned)(__ballot(r1 >= 0) & 0xFFFFull);
-    const uint16_t* k0p = Kb + (size_t)(r0 < 0 ? 0 : r0) * kHeadDim + 8 * lg;
-    const uint16_t* k1p = Kb + (size_t)(r1 < 0 ? 0 : r1) * kHeadDim + 8 * lg;
-    const uint16_t* v0p = Vb + (size_t)(r0 < 0 ? 0 : r0) * kHeadDim + 8 * lg;
-    const uint16_t* v1p = Vb + (size_t)(r1 < 0 ? 0 : r1) * kHeadDim + 8 * lg;
-    V8 kr0[4], kr1[4], vr0[4], vr1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kr0[s] = __builtin_bit_cast(V8, *(const u32x4*)(k0p + 32 * s));
-      kr1[s] = __builtin_bit_cast(V8, *(const u32x4*)(k1p + 32 * s));
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      vr0[s] = __builtin_bit_cast(V8, *(const u32x4*)(v0p + 32 * s));
-      vr1[s] = __builtin_bit_cast(V8, *(const u32x4*)(v1p + 32 * s));
-    }
-
-    // ---- scores, online softmax, probabilities as MFMA operands ----------
-    V8 ph[NQT], pl[NQT];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      f32x4 s0 = zero4, s1 = zero4;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        s0 = M::mma(kr0[s], qreg[qt][s], s0);
-        s1 = M::mma(kr1[s], qreg[qt][s], s1);
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * lg + r;
-        const bool vis0 = ((mk0 >> j) & 1u) && (MODE != kVerify || t0 + j <= lim[qt]);
-        const bool vis1 = ((mk1 >> j) & 1u) && (MODE != kVerify || t0 + 16 + j <= lim[qt]);
-        s0[r] = vis0 ? s0[r] : kNegInf;
-        s1[r] = vis1 ? s1[r] : kNegInf;
-        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx);
-      float alpha = 1.f, mc = 0.f;
-      if (m_new != kNegInf) {
-        alpha = fast_exp2((m_run[qt] - m_new) * c2);
-        mc = m_new * c2;
-      }
-      float psum = 0.f;
-      V8 hi, lo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p0 = fast_exp2(fmaf(s0[r], c2, -mc));
-        const float p1 = fast_exp2(fmaf(s1[r], c2, -mc));
-        psum += p0 + p1;
-        const S h0 = (S)p0, h1 = (S)p1;
-        hi[r] = h0;
-        hi[4 + r] = h1;
-        lo[r] = (S)(p0 - (float)h0);
-        lo[4 + r] = (S)(p1 - (float)h1);
-      }
-      ph[qt] = hi;
-      pl[qt] = lo;
-      l_run[qt] = l_run[qt] * alpha + psum;
-      m_run[qt] = m_new;
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) acc[qt][bb] *= alpha;
-    }
-
-    // ---- values: move tokens onto the k axis, then O^T += V^T . P^T ------
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const f32x4 t0v = M::mma(vr0[bb >> 1], sel[bb & 1], zero4);
-      const f32x4 t1v = M::mma(vr1[bb >> 1], sel[bb & 1], zero4);
-      V8 av;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        av[r] = (S)t0v[r];
-        av[4 + r] = (S)t1v[r];
-      }
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
-        acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
-      }
+  // Software pipeline: the next tile's 16 loads are in flight while the
+  // current one is consumed.  The prefetch is unconditional (past the end it
+  // reads row 0, masked), so every iteration has the same loads outstanding.
+  int t = v0 + kTile * w;
+  if (t < v1) {
+    Tile<DT> A, B;
+    load_tile<DT, MODE>(A, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+    while (true) {
+      load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(A, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
+      load_tile<DT, MODE>(A, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(B, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
     }
   }
 
@@ -323,10 +371,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
       float o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float t = 0.f;
+        float acc_o = 0.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) t += ew[x] * s_o[x][q][dc + j];
-        o[j] = t;
+        for (int x = 0; x < 4; ++x) acc_o += ew[x] * s_o[x][q][dc + j];
+        o[j] = acc_o;
       }
       if (row < a.rows) {
         if (nsp == 1) {
@@ -349,40 +397,68 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     }
     __syncthreads();
   }
-  if (nsp == 1) return;
+}
 
-  // ---- last workgroup of this (sequence, head) merges the splits -----------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == nsp - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t pbase = bh * a.nsplit * a.rows_pad;
-  for (int item = tid; item < a.rows * 32; item += kThreads) {
-    const int row = item >> 5;
-    const int dq = (item & 31) * 4;
-    float Mx = kNegInf;
-    for (int s = 0; s < nsp; ++s) Mx = fmaxf(Mx, a.part_ml[(pbase + (size_t)s * a.rows_pad + row) * 2]);
-    float Ls = 0.f;
-    f32x4 o = zero4;
-    if (Mx != kNegInf) {
-      for (int s = 0; s < nsp; ++s) {
-        const size_t pr = pbase + (size_t)s * a.rows_pad + row;
-        const float ms = a.part_ml[pr * 2];
-        const float e = (ms == kNegInf) ? 0.f : fast_exp2((ms - Mx) * c2);
-        Ls += e * a.part_ml[pr * 2 + 1];
-        o += e * *(const f32x4*)(a.part_o + pr * kHeadDim + dq);
+// Merge of the split partials of every (sequence, KV head, query row) whose
+// sequence needed more than one split: one wave per row, two dims per lane,
+// splits in order.  Runs as its own launch so that no device-wide fence is
+// needed inside the attention kernel.  Lanes fetch 64 splits' (max, sum) at
+// once; the accumulator rows of a group of 64 splits are then read 8 at a
+// time, independent loads in flight together.
+template <int MODE>
+__global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
+  const int row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const Geo geo = make_geo<MODE>(a, b);
+  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+  if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
+  const int lane = threadIdx.x;
+  const float c2 = a.scale_log2;
+  const size_t bh = (size_t)b * a.Hkv + hk;
+  const size_t pbase = bh * a.nsplit * a.rows_pad + row;
+  const float2* ml = (const float2*)a.part_ml;
+  float Mx = kNegInf;
+  for (int s = lane; s < nsp; s += 64) Mx = fmaxf(Mx, ml[pbase + (size_t)s * a.rows_pad].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
+  float Ls = 0.f, o0 = 0.f, o1 = 0.f;
+  if (Mx != kNegInf) {
+    for (int s0 = 0; s0 < nsp; s0 += 64) {
+      const int s = s0 + lane;
+      float e = 0.f, le = 0.f;
+      if (s < nsp) {
+        const float2 v = ml[pbase + (size_t)s * a.rows_pad];
+        e = (v.x == kNegInf) ? 0.f : fast_exp2((v.x - Mx) * c2);
+        le = e * v.y;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) le += __shfl_xor(le, off);
+      Ls += le;
+      const int cnt = min(64, nsp - s0);
+      int i = 0;
+      for (; i + 8 <= cnt; i += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + i + u) * a.rows_pad) * kHeadDim + 2 * lane);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float eu = __shfl(e, i + u);
+          o0 += eu * v[u].x;
+          o1 += eu * v[u].y;
+        }
+      }
+      for (; i < cnt; ++i) {
+        const float2 v = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + i) * a.rows_pad) * kHeadDim + 2 * lane);
+        const float eu = __shfl(e, i);
+        o0 += eu * v.x;
+        o1 += eu * v.y;
       }
     }
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    *(f32x4*)(a.out + (qrow0 + row) * kHeadDim + dq) = o * inv;
-    if (a.lse && dq == 0) a.lse[qrow0 + row] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
   }
-  if (tid == 0) a.counters[bh] = 0;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
+  *(float2*)(a.out + (qrow0 + row) * kHeadDim + 2 * lane) = make_float2(o0 * inv, o1 * inv);
+  if (a.lse && lane == 0) a.lse[qrow0 + row] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
 }
 
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs) {
@@ -396,13 +472,12 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
   p.rows_pad = ((rows + 15) / 16) * 16;
   const size_t parts = (size_t)heads * p.nsplit * p.rows_pad;
   if (p.nsplit > 1) {
+    p.part_ml_bytes = (parts * 2 * sizeof(float) + 255) & ~(size_t)255;
     p.part_o_bytes = parts * kHeadDim * sizeof(float);
-    p.part_ml_bytes = parts * 2 * sizeof(float);
-    p.counter_bytes = ((size_t)heads * sizeof(int32_t) + 255) & ~(size_t)255;
   } else {
-    p.part_o_bytes = p.part_ml_bytes = p.counter_bytes = 0;
+    p.part_o_bytes = p.part_ml_bytes = 0;
   }
-  p.total_bytes = p.counter_bytes + p.part_ml_bytes + p.part_o_bytes;
+  p.total_bytes = p.part_ml_bytes + p.part_o_bytes;
   return p;
 }
 
@@ -417,6 +492,9 @@ static hipError_t launch_nqt(const AttnArgs& a, hipStream_t stream) {
     case 4: hipLaunchKernelGGL((attn_kernel<DT, MODE, 4>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((combine_kernel<MODE>), dim3(a.rows, a.Hkv, a.B), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

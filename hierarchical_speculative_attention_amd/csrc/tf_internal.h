@@ -39,7 +39,6 @@ struct AttnArgs {
   float* lse;               // [B][Hq][Qn] or null
   float* part_o;            // [B][Hkv][nsplit][rows_pad][d]
   float* part_ml;           // [B][Hkv][nsplit][rows_pad][2]
-  int32_t* counters;        // [B][Hkv]
   float scale_log2;         // log2(e) / sqrt(d)
   float scale_ln;           // 1 / sqrt(d)
 };
@@ -49,7 +48,7 @@ struct SplitPlan {
   int32_t tpw;
   int32_t nsplit;
   int32_t rows_pad;
-  size_t part_o_bytes, part_ml_bytes, counter_bytes, total_bytes;
+  size_t part_o_bytes, part_ml_bytes, total_bytes;
 };
 
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs);
@@ -67,11 +66,10 @@ hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_m
                        const int32_t* n_chunks, int32_t k, int32_t* idx, hipStream_t stream);
 // accept
 size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V);
+int32_t accept_max_vocab();
 hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens,
                          const double* uniforms, int32_t B, int32_t gamma, int32_t V,
                          float temperature, int32_t flags, int32_t* n_acc, int32_t* next,
                          void* ws, hipStream_t stream);
-// workspace
-hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);
 
 }  // namespace tfk

@@ -33,9 +33,8 @@
  *  - Pointers must be 16-byte aligned, and every row offset a descriptor
  *    implies (seq_base[b] and seq_cap[b] * d) a multiple of 8 elements.
  *  - Calls that share one workspace must not overlap in time (same stream or
- *    explicitly ordered).  A workspace must be zero-filled once after
- *    allocation (tf_workspace_clear); each completed call leaves its counters
- *    at zero again.
+ *    explicitly ordered).  A workspace needs no initialisation: it only holds
+ *    per-split partial results that each call writes before reading.
  *  - Caches must hold finite values.
  */
 #ifndef TF_ATTN_H
@@ -81,9 +80,6 @@ typedef struct {
 
 const char* tf_status_string(int status);
 const char* tf_last_error_detail(void);
-
-/* Zero-fill a workspace (enqueued on `stream`, no memset node). */
-int tf_workspace_clear(void* ws, size_t ws_bytes, tf_stream_t stream);
 
 /*
  * a1  Chunk-mean keys.  [blog] Force 2 retrieves KV blocks by key-query
@@ -200,7 +196,8 @@ size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q
  *   target: device fp32 [B][gamma+1][V]; draft: device fp32 [B][gamma][V];
  *   draft_tokens: device int32 [B][gamma] (each in [0, V)); uniforms: device
  *   fp64 [B][gamma+1] in (0, 1).  Outputs: device int32 [B].
- *   ws: tf_accept_workspace_size(B, gamma, V) bytes.
+ *   ws: tf_accept_workspace_size(B, gamma, V) bytes (per-row statistics).
+ *   Limits: V <= 65536, gamma <= 1024, B * (2 gamma + 1) * ceil(V / 4096) < 2^31.
  */
 #define TF_ACCEPT_PROBS 1
 int tf_accept(const float* target, const float* draft, const int32_t* draft_tokens,

@@ -26,7 +26,7 @@ def declared():
 
 def test_every_declared_function_is_exported():
     names = declared()
-    assert len(names) >= 14
+    assert len(names) >= 13
     L = T.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -108,6 +108,8 @@ def test_other_entry_points_validate():
     assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(float("nan")), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(1.0), 4, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_accept(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10004), 1, 4, 100, f(1.0), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 70000, f(1.0), 0, FAKE, FAKE, FAKE, 1 << 20, None) == T.TF_ERR_UNSUPPORTED
+    assert L.tf_accept(FAKE, FAKE, FAKE, FAKE, 1, 4, 100, f(1.0), 0, FAKE, FAKE, None, 0, None) == T.TF_ERR_WORKSPACE
 
 
 def test_workspace_sizes_are_deterministic_and_grow_with_length():
@@ -116,4 +118,5 @@ def test_workspace_sizes_are_deterministic_and_grow_with_length():
     assert a == L.tf_verify_attn_workspace_size(1, 32, 32, 7, 131072)
     assert L.tf_verify_attn_workspace_size(1, 32, 32, 7, 1 << 20) >= a
     assert L.tf_verify_attn_workspace_size(0, 32, 32, 7, 131072) == 0
-    assert L.tf_accept_workspace_size(4, 6, 32000) == 0
+    assert L.tf_accept_workspace_size(4, 6, 32000) >= 4 * 13 * 8 * 16
+    assert L.tf_accept_workspace_size(0, 6, 32000) == 0
