@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn GB/s & % HBM peak, sparse-draft+verify steps/s at 128K ctx"
 HBM_PEAK_GBPS = 8000.0
-VERIFY_SRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc", "attn.hip")
+CSRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc")
+VERIFY_SRCS = [os.path.join(CSRC, f) for f in ("attn.hip", "api.hip", "tf_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_traffic.txt")
 
 
@@ -48,9 +49,12 @@ def parse():
     return ap.parse_args()
 
 
-def file_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic():
@@ -63,7 +67,7 @@ def read_traffic():
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("attn_hip_sha256") != file_sha(VERIFY_SRC):
+    if kv.get("attn_hip_sha256") != sources_sha(VERIFY_SRCS):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
