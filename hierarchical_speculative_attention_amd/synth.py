@@ -351,7 +351,8 @@ def make_layer_torch(*, lens: Sequence[int], Hq: int, Hkv: int, d: int, dtype: s
     """Generate one layer directly in device memory.
 
     Returns (K, V, q_verify, q_draft, layout, planted) with K and V flat torch
-    tensors of the storage dtype laid out as KVLayout describes.  K_out/V_out
+    tensors of the storage dtype laid out as KVLayout describes; planted[b]
+    lists the planted chunk indices (Zipf: the rank-1..3 chunks per KV head).  K_out/V_out
     may be preallocated flat views to fill (so many layers can share one big
     allocation).  The recipe is the one of make_attn_inputs; the random
     streams differ (torch Philox instead of numpy PCG64)."""
@@ -397,10 +398,12 @@ def make_layer_torch(*, lens: Sequence[int], Hq: int, Hkv: int, d: int, dtype: s
                 noise = torch.randn((rows.numel(), d), generator=gn, device=device) * 0.5
                 head[rows] = (0.5 * qbar[None, :] + noise).to(tdt)
         elif plant == "zipf" and C > 0:
-            planted.append(np.zeros(0, np.int64))
+            top = np.zeros((Hkv, 3), np.int64)  # per KV head: chunks of rank 1, 2, 3
             full_chunks = n // chunk_size
             for g in range(Hkv):
-                perm = torch.as_tensor(r["zipf_perm"].permutation(C), device=device)
+                perm_np = r["zipf_perm"].permutation(C)
+                top[g] = np.argsort(perm_np)[:3]
+                perm = torch.as_tensor(perm_np, device=device)
                 w = 0.5 * (perm.double() + 1.0) ** (-zipf_s)
                 qbar = q_round[b, g * G:(g + 1) * G, 0, :].mean(dim=0)
                 head = K[base + g * cap * d: base + (g + 1) * cap * d].view(cap, d)
@@ -410,6 +413,7 @@ def make_layer_torch(*, lens: Sequence[int], Hq: int, Hkv: int, d: int, dtype: s
                 if full_chunks * chunk_size < n:
                     t0 = full_chunks * chunk_size
                     head[t0:n] = (head[t0:n].float() + float(w[-1]) * qbar[None, :]).to(tdt)
+            planted.append(top)
         else:
             planted.append(np.zeros(0, np.int64))
     return K, V, qv.contiguous(), qv[:, :, :1, :].contiguous(), lay, planted
