@@ -200,7 +200,7 @@ TF_EXPORT size_t tf_sparse_attn_workspace_size(int32_t B, int32_t Hq, int32_t H,
   if (B < 1 || H < 1 || Hq < 1 || k < 1 || chunk_size < 1) return 0;
   const long virt = (long)k * chunk_size;
   if (virt > 0x7fffffffL) return 0;
-  return tfk::plan_splits(B, H, Hq / H, (int32_t)virt, kSparseTargetWgs).total_bytes;
+  return tfk::plan_splits(B, H, Hq / H, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw).total_bytes;
 }
 
 TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const void* V, const tf_kv_desc* kv,
@@ -218,7 +218,8 @@ TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const voi
   TRY(check_ptr(idx, "idx", 4));
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
-  const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, Hq / kv->H, k * chunk_size, kSparseTargetWgs);
+  const tfk::SplitPlan plan =
+      tfk::plan_splits(kv->B, kv->H, Hq / kv->H, k * chunk_size, kSparseTargetWgs, tfk::kSparseMaxTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, 1, out, lse);
@@ -265,7 +266,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
 // ---------------------------------------------------------------------------
 TF_EXPORT size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len) {
   if (B < 1 || H < 1 || Hq < 1 || Q < 1 || max_len < 0) return 0;
-  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs).total_bytes;
+  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw).total_bytes;
 }
 
 TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
@@ -283,7 +284,8 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   TRY(check_ptr(V, "V", 16));
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
-  const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs);
+  const tfk::SplitPlan plan =
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);

@@ -59,6 +59,8 @@ template <> struct MT<TF_DTYPE_FP16> {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kMaxSparseTpw = kSparseMaxTpw;      // virtual tokens per sparse workgroup (host-capped)
+constexpr int kMaxSparseIdx = kMaxSparseTpw + 2;  // chunk slots one sparse workgroup can touch
 
 // Sequence geometry of one (b) for a mode: virtual length and what a
 // virtual token maps to.
@@ -128,67 +130,88 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
   return slot < g.cap ? slot : -1;
 }
 
-// One 32-token tile of a wave: two 16-token subtiles of K and V in MFMA
-// A-operand layout (lane (t, g): dims 32s + 8g .. +8 of token t, s = 0..3).
-template <int DT>
-struct Tile {
-  typename MT<DT>::V8 k0[4], k1[4], v0[4], v1[4];
-  unsigned mk0, mk1;  // bit t: token t of subtile 0 / 1 is a valid row
-  int t0;             // first virtual token of the tile
+// Tiles travel HBM -> registers -> LDS -> MFMA operands.  A 32-token tile of
+// K and V (16 KB) is fetched with 16 nontemporal 16-byte loads per lane in
+// which each wave instruction covers 1 KB of contiguous memory (4 rows of 256
+// bytes): on this chip that pattern streams at about 7.0 TB/s, while loading
+// straight into the MFMA operand layout (16 rows x 64 bytes per instruction)
+// tops out near 6.3 TB/s.  The tile is staged in a wave-private LDS slab with
+// a 272-byte row pitch, so both the contiguous writes and the 16-row operand
+// reads are free of bank conflicts.
+constexpr int kPitch = 272;                  // LDS bytes per staged 256-byte row
+constexpr int kStageRows = 2 * kTile;        // 32 key rows, then 32 value rows
+constexpr int kStageBytes = kStageRows * kPitch;
+constexpr int kMergeBytes = 4 * 16 * 132 * 4;  // per-query-tile merge buffer (reuses the slabs)
+static_assert(kMergeBytes <= 4 * kStageBytes, "merge buffer must fit in the staging slabs");
+
+struct Stage {
+  u32x4 v[16];     // v[i]: staged row 4 i + lane / 16, bytes 16 (lane % 16) .. +16
+  unsigned mask;   // bit j: token j of the tile is a valid row
 };
 
-template <int DT, int MODE>
-__device__ __forceinline__ void load_tile(Tile<DT>& T, const AttnArgs& a, const Geo& geo, int t0, int v1,
-                                          const int* s_idx, int chunk_lo, const uint16_t* Kb,
-                                          const uint16_t* Vb, int lq, int lg) {
-  using V8 = typename MT<DT>::V8;
-  const int r0 = map_row<MODE>(a, geo, t0 + lq, v1, s_idx, chunk_lo);
-  const int r1 = map_row<MODE>(a, geo, t0 + 16 + lq, v1, s_idx, chunk_lo);
-  T.mk0 = (unsigned)(__ballot(r0 >= 0) & 0xFFFFull);
-  T.mk1 = (unsigned)(__ballot(r1 >= 0) & 0xFFFFull);
-  T.t0 = t0;
-  // Rows that hold nothing read row 0 (in bounds, cached) and are masked.
-  const size_t o0 = (size_t)(r0 < 0 ? 0 : r0) * kHeadDim + 8 * lg;
-  const size_t o1 = (size_t)(r1 < 0 ? 0 : r1) * kHeadDim + 8 * lg;
+template <int MODE>
+__device__ __forceinline__ void load_stage(Stage& st, const AttnArgs& a, const Geo& geo, int t0, int v1,
+                                           const int* s_idx, int chunk_lo, const uint16_t* Kb,
+                                           const uint16_t* Vb, int lane) {
+  const int rv = map_row<MODE>(a, geo, t0 + (lane & 31), v1, s_idx, chunk_lo);
+  st.mask = (unsigned)(__ballot(rv >= 0) & 0xFFFFFFFFull);
+  size_t off[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    T.k0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o0 + 32 * s));
-    T.k1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o1 + 32 * s));
+  for (int i = 0; i < 8; ++i) {
+    // Rows that hold nothing read row 0 (in bounds) and are masked later.
+    const int r = map_row<MODE>(a, geo, t0 + 4 * i + (lane >> 4), v1, s_idx, chunk_lo);
+    off[i] = (size_t)(r < 0 ? 0 : r) * kHeadDim + 8 * (lane & 15);
   }
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    T.v0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o0 + 32 * s));
-    T.v1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o1 + 32 * s));
-  }
+  for (int i = 0; i < 8; ++i) st.v[i] = __builtin_nontemporal_load((const u32x4*)(Kb + off[i]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.v[8 + i] = __builtin_nontemporal_load((const u32x4*)(Vb + off[i]));
 }
 
-// Online-softmax update of one wave with one tile.
+__device__ __forceinline__ void write_stage(const Stage& st, unsigned char* slab, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *(u32x4*)(slab + (4 * i + (lane >> 4)) * kPitch + 16 * (lane & 15)) = st.v[i];
+}
+
+// Online-softmax update of one wave with the tile staged in its slab.
 template <int DT, int MODE, int NQT>
-__device__ __forceinline__ void process_tile(const Tile<DT>& T, const typename MT<DT>::V8 (&qreg)[NQT][4],
+__device__ __forceinline__ void process_tile(const unsigned char* slab, unsigned mask, int t0,
+                                             const typename MT<DT>::V8 (&qreg)[NQT][4],
                                              const typename MT<DT>::V8 (&sel)[2], const int (&lim)[NQT],
                                              int lim_min, f32x4 (&acc)[NQT][8], float (&m_run)[NQT],
-                                             float (&l_run)[NQT], float c2, int lg) {
+                                             float (&l_run)[NQT], float c2, int lq, int lg) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const unsigned mk0 = mask & 0xFFFFu, mk1 = mask >> 16;
+  // MFMA operand of subtile u, k-step s: row 16 u + lq, bytes 64 s + 16 lg.
+  const unsigned char* kp = slab + lq * kPitch + 16 * lg;
+  const unsigned char* vp = kp + kTile * kPitch;
   // Whole tile visible to every row: no per-element masking needed.
-  const bool full = (T.mk0 & T.mk1) == 0xFFFFu && (MODE != kVerify || T.t0 + 31 <= lim_min);
+  const bool full = mask == 0xFFFFFFFFu && (MODE != kVerify || t0 + 31 <= lim_min);
   V8 ph[NQT], pl[NQT];
+  V8 k0[4], k1[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    k0[s] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 64 * s));
+    k1[s] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 16 * kPitch + 64 * s));
+  }
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     f32x4 s0 = zero4, s1 = zero4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      s0 = M::mma(T.k0[s], qreg[qt][s], s0);
-      s1 = M::mma(T.k1[s], qreg[qt][s], s1);
+      s0 = M::mma(k0[s], qreg[qt][s], s0);
+      s1 = M::mma(k1[s], qreg[qt][s], s1);
     }
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * lg + r;
-        const bool vis0 = ((T.mk0 >> j) & 1u) && (MODE != kVerify || T.t0 + j <= lim[qt]);
-        const bool vis1 = ((T.mk1 >> j) & 1u) && (MODE != kVerify || T.t0 + 16 + j <= lim[qt]);
+        const bool vis0 = ((mk0 >> j) & 1u) && (MODE != kVerify || t0 + j <= lim[qt]);
+        const bool vis1 = ((mk1 >> j) & 1u) && (MODE != kVerify || t0 + 16 + j <= lim[qt]);
         s0[r] = vis0 ? s0[r] : kNegInf;
         s1[r] = vis1 ? s1[r] : kNegInf;
       }
@@ -225,36 +248,42 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& T, const typename M
   }
   // Values: move tokens onto the k axis, then O^T += V^T . P^T.
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    const f32x4 t0v = M::mma(T.v0[bb >> 1], sel[bb & 1], zero4);
-    const f32x4 t1v = M::mma(T.v1[bb >> 1], sel[bb & 1], zero4);
-    V8 av;
+  for (int s = 0; s < 4; ++s) {
+    const V8 v0 = __builtin_bit_cast(V8, *(const u32x4*)(vp + 64 * s));
+    const V8 v1 = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * kPitch + 64 * s));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      av[r] = (S)t0v[r];
-      av[4 + r] = (S)t1v[r];
-    }
+    for (int h = 0; h < 2; ++h) {
+      const int bb = 2 * s + h;
+      const f32x4 t0v = M::mma(v0, sel[h], zero4);
+      const f32x4 t1v = M::mma(v1, sel[h], zero4);
+      V8 av;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
-      acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
+      for (int r = 0; r < 4; ++r) {
+        av[r] = (S)t0v[r];
+        av[4 + r] = (S)t1v[r];
+      }
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
+        acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
+      }
     }
   }
 }
 
-// One query tile fits two waves per SIMD (<= 256 registers, no spills) with
-// the double-buffered tile; more query tiles run one wave per SIMD.
+// One query tile fits two waves per SIMD (<= 256 registers, no spills);
+// more query tiles run one wave per SIMD.
 template <int DT, int MODE, int NQT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
 void attn_kernel(const AttnArgs a) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
-  constexpr int kMaxIdx = 4096 / 1 + 2;  // chunk slots per workgroup (tpw <= 4096, cs >= 1)
-  __shared__ int s_idx[MODE == kSparse ? kMaxIdx : 1];
-  __shared__ __attribute__((aligned(16))) float s_o[4][16][132];
+  __shared__ int s_idx[MODE == kSparse ? kMaxSparseIdx : 1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[4 * kStageBytes];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
+  float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -315,26 +344,30 @@ void attn_kernel(const AttnArgs a) {
   }
   const float c2 = a.scale_log2;
 
-  // Software pipeline: the next tile's 16 loads are in flight while the
-  // current one is consumed.  The prefetch is unconditional (past the end it
-  // reads row 0, masked), so every iteration has the same loads outstanding.
+  // Software pipeline: while a wave consumes the tile staged in its slab, the
+  // next tile's 16 loads are in flight.  The prefetch is unconditional (past
+  // the end it reads row 0, masked), so every iteration has the same loads
+  // outstanding.  LDS operations of one wave complete in order, so a slab is
+  // rewritten only after the previous tile's operand reads.
+  unsigned char* slab = s_stage + w * kStageBytes;
   int t = v0 + kTile * w;
   if (t < v1) {
-    Tile<DT> A, B;
-    load_tile<DT, MODE>(A, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+    Stage st;
+    load_stage<MODE>(st, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
+    unsigned mask = st.mask;
+    write_stage(st, slab, lane);
+    load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     while (true) {
-      load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(A, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lg);
+      process_tile<DT, MODE, NQT>(slab, mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lq, lg);
       t += 4 * kTile;
       if (t >= v1) break;
-      load_tile<DT, MODE>(A, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
-      __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(B, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lg);
-      t += 4 * kTile;
-      if (t >= v1) break;
+      mask = st.mask;
+      write_stage(st, slab, lane);
+      load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     }
   }
+  __syncthreads();  // every slab consumed: the merge reuses them
 
   // ---- merge the four waves (per query tile) -------------------------------
   const size_t bh = (size_t)b * a.Hkv + hk;
@@ -461,9 +494,10 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   if (a.lse && lane == 0) a.lse[qrow0 + row] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
 }
 
-SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs) {
+SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
+                      int32_t max_tpw) {
   SplitPlan p;
-  int32_t tpw = 4096;
+  int32_t tpw = max_tpw;
   const long heads = (long)B * Hkv;
   while (tpw > 128 && heads * (((long)max_virtual + tpw - 1) / tpw) < target_wgs) tpw >>= 1;
   p.tpw = tpw;

@@ -3,8 +3,8 @@
 // the most critical KV blocks by key-query similarity).  A block is
 // summarised by the mean of its keys; the score of a block is the dot product
 // of that mean with the draft query (summed over the query heads sharing the
-// KV head).  Both kernels stream HBM once with 16-byte loads: 16 lanes cover
-// one 256-byte row of 128 16-bit values.
+// KV head).  Both kernels stream HBM once with 16-byte nontemporal loads: 16
+// lanes cover one 256-byte row of 128 16-bit values.
 #include "tf_internal.h"
 
 namespace tfk {
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void chunk_keys_kernel(
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < hi - lo; ++t) {
     float f[8];
-    widen8(IN_DT, *(const u32x4*)(src + (size_t)t * kHeadDim), f);
+    widen8(IN_DT, __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * kHeadDim)), f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[j] += f[j];
   }
@@ -130,12 +130,12 @@ __global__ __launch_bounds__(256) void score_kernel(
       const size_t row = (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
       float f[8];
       if (CK_DT == TF_DTYPE_FP32) {
-        const f32x4 x0 = *(const f32x4*)((const float*)ck + row);
-        const f32x4 x1 = *(const f32x4*)((const float*)ck + row + 4);
+        const f32x4 x0 = __builtin_nontemporal_load((const f32x4*)((const float*)ck + row));
+        const f32x4 x1 = __builtin_nontemporal_load((const f32x4*)((const float*)ck + row + 4));
         f[0] = x0[0]; f[1] = x0[1]; f[2] = x0[2]; f[3] = x0[3];
         f[4] = x1[0]; f[5] = x1[1]; f[6] = x1[2]; f[7] = x1[3];
       } else {
-        widen8(CK_DT, *(const u32x4*)((const uint16_t*)ck + row), f);
+        widen8(CK_DT, __builtin_nontemporal_load((const u32x4*)((const uint16_t*)ck + row)), f);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc = fmaf(qs[j], f[j], acc);

@@ -51,7 +51,12 @@ struct SplitPlan {
   size_t part_o_bytes, part_ml_bytes, total_bytes;
 };
 
-SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs);
+// Virtual tokens per workgroup: a power of two in [128, max_tpw], the largest
+// that still gives at least target_wgs workgroups.
+constexpr int32_t kVerifyMaxTpw = 4096;
+constexpr int32_t kSparseMaxTpw = 1024;
+SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
+                      int32_t max_tpw);
 
 hipError_t launch_attn(int dtype, int mode, const AttnArgs& a, hipStream_t stream);
 
