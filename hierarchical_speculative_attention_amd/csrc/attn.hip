@@ -130,18 +130,27 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
   return slot < g.cap ? slot : -1;
 }
 
-// Tiles travel HBM -> registers -> LDS -> MFMA operands.  A 32-token tile of
+// Two ways to bring a 32-token tile of K and V (16 KB) to the MFMAs:
+//
+// Staged (verify: long streams, bandwidth-bound).  HBM -> registers -> LDS ->
+// MFMA operands.  A 32-token tile of
 // K and V (16 KB) is fetched with 16 nontemporal 16-byte loads per lane in
 // which each wave instruction covers 1 KB of contiguous memory (4 rows of 256
 // bytes): on this chip that pattern streams at about 7.0 TB/s, while loading
 // straight into the MFMA operand layout (16 rows x 64 bytes per instruction)
 // tops out near 6.3 TB/s.  The tile is staged in a wave-private LDS slab with
 // a 272-byte row pitch, so both the contiguous writes and the 16-row operand
-// reads are free of bank conflicts.
+// reads are free of bank conflicts.  One tile is in flight while the staged
+// one is consumed.
+//
+// Direct (sparse and streaming: a few tiles per wave, latency-bound).  Loads
+// go straight into the MFMA operand layout (lane (t, g): dims 32 s + 8 g ..
+// +8 of token t) and two tiles are in flight at once, so a wave pays one
+// memory round trip for its first two tiles.
 constexpr int kPitch = 272;                  // LDS bytes per staged 256-byte row
 constexpr int kStageRows = 2 * kTile;        // 32 key rows, then 32 value rows
 constexpr int kStageBytes = kStageRows * kPitch;
-constexpr int kMergeBytes = 4 * 16 * 132 * 4;  // per-query-tile merge buffer (reuses the slabs)
+constexpr int kMergeBytes = 4 * 16 * 132 * 4;  // per-query-tile merge buffer (staged: reuses the slabs)
 static_assert(kMergeBytes <= 4 * kStageBytes, "merge buffer must fit in the staging slabs");
 
 struct Stage {
@@ -174,9 +183,59 @@ __device__ __forceinline__ void write_stage(const Stage& st, unsigned char* slab
     *(u32x4*)(slab + (4 * i + (lane >> 4)) * kPitch + 16 * (lane & 15)) = st.v[i];
 }
 
-// Online-softmax update of one wave with the tile staged in its slab.
-template <int DT, int MODE, int NQT>
-__device__ __forceinline__ void process_tile(const unsigned char* slab, unsigned mask, int t0,
+// Direct tile: MFMA operands of both subtiles, in registers.
+template <int DT>
+struct Tile {
+  typename MT<DT>::V8 k0[4], k1[4], v0[4], v1[4];
+  unsigned mask;  // bit j: token j of the tile is a valid row
+};
+
+template <int DT, int MODE>
+__device__ __forceinline__ void load_tile(Tile<DT>& T, const AttnArgs& a, const Geo& geo, int t0, int v1,
+                                          const int* s_idx, int chunk_lo, const uint16_t* Kb,
+                                          const uint16_t* Vb, int lq, int lg) {
+  using V8 = typename MT<DT>::V8;
+  const int r0 = map_row<MODE>(a, geo, t0 + lq, v1, s_idx, chunk_lo);
+  const int r1 = map_row<MODE>(a, geo, t0 + 16 + lq, v1, s_idx, chunk_lo);
+  T.mask = (unsigned)(__ballot(r0 >= 0) & 0xFFFFull) | ((unsigned)(__ballot(r1 >= 0) & 0xFFFFull) << 16);
+  // Rows that hold nothing read row 0 (in bounds) and are masked.
+  const size_t o0 = (size_t)(r0 < 0 ? 0 : r0) * kHeadDim + 8 * lg;
+  const size_t o1 = (size_t)(r1 < 0 ? 0 : r1) * kHeadDim + 8 * lg;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    T.k0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o0 + 32 * s));
+    T.k1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Kb + o1 + 32 * s));
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    T.v0[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o0 + 32 * s));
+    T.v1[s] = __builtin_bit_cast(V8, *(const u32x4*)(Vb + o1 + 32 * s));
+  }
+}
+
+// Operand sources for process_tile: k(u, s) / v(u, s) give the MFMA operand
+// of subtile u, k-step s (row 16 u + lane % 16, dims 32 s + 8 (lane / 16) ..).
+template <int DT>
+struct SlabSource {
+  const unsigned char* kp;  // slab + (lane % 16) * kPitch + 16 (lane / 16)
+  __device__ __forceinline__ typename MT<DT>::V8 k(int u, int s) const {
+    return __builtin_bit_cast(typename MT<DT>::V8, *(const u32x4*)(kp + u * 16 * kPitch + 64 * s));
+  }
+  __device__ __forceinline__ typename MT<DT>::V8 v(int u, int s) const {
+    return __builtin_bit_cast(typename MT<DT>::V8, *(const u32x4*)(kp + (kTile + u * 16) * kPitch + 64 * s));
+  }
+};
+
+template <int DT>
+struct RegSource {
+  const Tile<DT>& T;
+  __device__ __forceinline__ typename MT<DT>::V8 k(int u, int s) const { return u ? T.k1[s] : T.k0[s]; }
+  __device__ __forceinline__ typename MT<DT>::V8 v(int u, int s) const { return u ? T.v1[s] : T.v0[s]; }
+};
+
+// Online-softmax update of one wave with one tile.
+template <int DT, int MODE, int NQT, class Src>
+__device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int t0,
                                              const typename MT<DT>::V8 (&qreg)[NQT][4],
                                              const typename MT<DT>::V8 (&sel)[2], const int (&lim)[NQT],
                                              int lim_min, f32x4 (&acc)[NQT][8], float (&m_run)[NQT],
@@ -186,17 +245,14 @@ __device__ __forceinline__ void process_tile(const unsigned char* slab, unsigned
   using S = typename M::S;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const unsigned mk0 = mask & 0xFFFFu, mk1 = mask >> 16;
-  // MFMA operand of subtile u, k-step s: row 16 u + lq, bytes 64 s + 16 lg.
-  const unsigned char* kp = slab + lq * kPitch + 16 * lg;
-  const unsigned char* vp = kp + kTile * kPitch;
   // Whole tile visible to every row: no per-element masking needed.
   const bool full = mask == 0xFFFFFFFFu && (MODE != kVerify || t0 + 31 <= lim_min);
   V8 ph[NQT], pl[NQT];
   V8 k0[4], k1[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    k0[s] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 64 * s));
-    k1[s] = __builtin_bit_cast(V8, *(const u32x4*)(kp + 16 * kPitch + 64 * s));
+    k0[s] = src.k(0, s);
+    k1[s] = src.k(1, s);
   }
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
@@ -249,8 +305,8 @@ __device__ __forceinline__ void process_tile(const unsigned char* slab, unsigned
   // Values: move tokens onto the k axis, then O^T += V^T . P^T.
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const V8 v0 = __builtin_bit_cast(V8, *(const u32x4*)(vp + 64 * s));
-    const V8 v1 = __builtin_bit_cast(V8, *(const u32x4*)(vp + 16 * kPitch + 64 * s));
+    const V8 v0 = src.v(0, s);
+    const V8 v1 = src.v(1, s);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int bb = 2 * s + h;
@@ -279,8 +335,9 @@ void attn_kernel(const AttnArgs a) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
+  constexpr bool kStaged = MODE == kVerify;
   __shared__ int s_idx[MODE == kSparse ? kMaxSparseIdx : 1];
-  __shared__ __attribute__((aligned(16))) unsigned char s_stage[4 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
   float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
@@ -349,9 +406,10 @@ void attn_kernel(const AttnArgs a) {
   // the end it reads row 0, masked), so every iteration has the same loads
   // outstanding.  LDS operations of one wave complete in order, so a slab is
   // rewritten only after the previous tile's operand reads.
-  unsigned char* slab = s_stage + w * kStageBytes;
   int t = v0 + kTile * w;
-  if (t < v1) {
+  if (kStaged && t < v1) {
+    unsigned char* slab = s_stage + w * kStageBytes;
+    const SlabSource<DT> src{slab + lq * kPitch + 16 * lg};
     Stage st;
     load_stage<MODE>(st, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
     unsigned mask = st.mask;
@@ -359,15 +417,32 @@ void attn_kernel(const AttnArgs a) {
     load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     while (true) {
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(slab, mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lq, lg);
+      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lq, lg);
       t += 4 * kTile;
       if (t >= v1) break;
       mask = st.mask;
       write_stage(st, slab, lane);
       load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     }
+  } else if (!kStaged && t < v1) {
+    Tile<DT> A, B;
+    load_tile<DT, MODE>(A, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+    while (true) {
+      load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(RegSource<DT>{A}, A.mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2,
+                                  lq, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
+      load_tile<DT, MODE>(A, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(RegSource<DT>{B}, B.mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2,
+                                  lq, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
+    }
   }
-  __syncthreads();  // every slab consumed: the merge reuses them
+  if (kStaged) __syncthreads();  // every slab consumed: the merge reuses them
 
   // ---- merge the four waves (per query tile) -------------------------------
   const size_t bh = (size_t)b * a.Hkv + hk;

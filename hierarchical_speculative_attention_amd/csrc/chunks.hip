@@ -96,10 +96,13 @@ hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs
 }
 
 // ---------------------------------------------------------------------------
-// a2: grid (ceil(c_max / (16 * CPL)), H, B).  Each 16-lane group scores CPL
-// chunks (loads issued together), then reduces its 16 partial sums.
+// a2: grid (ceil(c_max / (64 * kCPL)), H, B), 256 threads.  Each wave scores
+// 16 * kCPL consecutive chunks; its load instruction i covers chunks
+// 4 i .. 4 i + 3 of its range, 1 KB of contiguous memory (16 lanes per
+// 256-byte key).  The 16 partial dot products of a key are reduced across
+// its 16 lanes.
 // ---------------------------------------------------------------------------
-constexpr int kCPL = 4;
+constexpr int kCPL = 8;  // chunks per lane group, loads in flight together
 
 template <int CK_DT>
 __global__ __launch_bounds__(256) void score_kernel(
@@ -108,8 +111,9 @@ __global__ __launch_bounds__(256) void score_kernel(
     int32_t c_max_len, float* __restrict__ scores, int32_t c_max) {
   const int b = blockIdx.z, g = blockIdx.y;
   const int G = Hq / H;
-  const int part = threadIdx.x & 15;
-  const int grp = threadIdx.x >> 4;  // 16 groups per block
+  const int part = threadIdx.x & 15;        // 16-byte piece of a 256-byte key
+  const int grp = (threadIdx.x >> 4) & 3;   // key of the wave instruction
+  const int w = threadIdx.x >> 6;
   const int cap = ccap[b];
   const int C = min(max(clen[b], 0), min(cap, c_max_len));
   // Group query: the sum of the G query heads' vectors (8 dims of it per lane).
@@ -120,27 +124,42 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) qs[j] += f[j];
   }
-  const int c0 = (blockIdx.x * 16 + grp) * kCPL;
+  const int c_wave = (blockIdx.x * 4 + w) * (4 * kCPL);  // first chunk of this wave
   float dot[kCPL];
+  if (CK_DT == TF_DTYPE_FP32) {
 #pragma unroll
-  for (int i = 0; i < kCPL; ++i) {
-    const int c = c0 + i;
-    float acc = 0.f;
-    if (c < C) {
-      const size_t row = (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
-      float f[8];
-      if (CK_DT == TF_DTYPE_FP32) {
-        const f32x4 x0 = __builtin_nontemporal_load((const f32x4*)((const float*)ck + row));
-        const f32x4 x1 = __builtin_nontemporal_load((const f32x4*)((const float*)ck + row + 4));
-        f[0] = x0[0]; f[1] = x0[1]; f[2] = x0[2]; f[3] = x0[3];
-        f[4] = x1[0]; f[5] = x1[1]; f[6] = x1[2]; f[7] = x1[3];
-      } else {
-        widen8(CK_DT, __builtin_nontemporal_load((const u32x4*)((const uint16_t*)ck + row)), f);
+    for (int i = 0; i < kCPL; ++i) {
+      const int c = c_wave + 4 * i + grp;
+      float acc = 0.f;
+      if (c < C) {
+        const float* row = (const float*)ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
+        const f32x4 x0 = __builtin_nontemporal_load((const f32x4*)row);
+        const f32x4 x1 = __builtin_nontemporal_load((const f32x4*)(row + 4));
+        acc = qs[0] * x0[0] + qs[1] * x0[1] + qs[2] * x0[2] + qs[3] * x0[3];
+        acc = fmaf(qs[4], x1[0], fmaf(qs[5], x1[1], fmaf(qs[6], x1[2], fmaf(qs[7], x1[3], acc))));
       }
+      dot[i] = acc;
+    }
+  } else {
+    u32x4 x[kCPL];
+#pragma unroll
+    for (int i = 0; i < kCPL; ++i) {
+      x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (C > 0) {  // chunks past C read chunk C - 1 (in bounds) and are masked below
+        const int c = min(c_wave + 4 * i + grp, C - 1);
+        x[i] = __builtin_nontemporal_load(
+            (const u32x4*)((const uint16_t*)ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kCPL; ++i) {
+      float f[8];
+      widen8(CK_DT, x[i], f);
+      float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc = fmaf(qs[j], f[j], acc);
+      dot[i] = (c_wave + 4 * i + grp < C) ? acc : 0.f;
     }
-    dot[i] = acc;
   }
 #pragma unroll
   for (int i = 0; i < kCPL; ++i) {
@@ -151,19 +170,20 @@ __global__ __launch_bounds__(256) void score_kernel(
     v += __shfl_xor(v, 1, 16);
     dot[i] = v;
   }
+  // lane `part` of key group `grp` writes chunk c_wave + 4 part + grp
   if (part < kCPL) {
-    const int c = c0 + part;
     float v = dot[0];
 #pragma unroll
     for (int i = 1; i < kCPL; ++i)
       if (part == i) v = dot[i];
+    const int c = c_wave + 4 * part + grp;
     if (c < c_max) scores[((size_t)b * H + g) * c_max + c] = (c < C) ? v : -__builtin_huge_valf();
   }
 }
 
 hipError_t launch_scores(const uint16_t* q, int32_t q_dtype, int32_t Hq, const void* ck,
                          const tf_kv_desc& ckd, float* scores, int32_t c_max, hipStream_t stream) {
-  const dim3 grid((c_max + 16 * kCPL - 1) / (16 * kCPL), ckd.H, ckd.B), block(256);
+  const dim3 grid((c_max + 16 * kCPL - 1) / (16 * kCPL), ckd.H, ckd.B), block(256);  // 4 waves x 4 keys x kCPL
   switch (ckd.dtype) {
     case TF_DTYPE_BF16:
       hipLaunchKernelGGL(score_kernel<TF_DTYPE_BF16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
