@@ -510,11 +510,13 @@ void attn_kernel(const AttnArgs a) {
 // Merge of the split partials of every (sequence, KV head, query row) whose
 // sequence needed more than one split: one wave per row, two dims per lane,
 // splits in order.  Runs as its own launch so that no device-wide fence is
-// needed inside the attention kernel.  Lanes fetch 64 splits' (max, sum) at
-// once; the accumulator rows of a group of 64 splits are then read 8 at a
-// time, independent loads in flight together.
+// needed inside the attention kernel.  Splits are taken in groups of 32: the
+// group's (max, sum) pairs and its 32 accumulator rows are all requested
+// before any is used, so a group costs one memory round trip; groups are
+// folded with an online rescale.
 template <int MODE>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
+  constexpr int kGroup = 32;
   const int row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const Geo geo = make_geo<MODE>(a, b);
   const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
@@ -524,44 +526,38 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   const size_t bh = (size_t)b * a.Hkv + hk;
   const size_t pbase = bh * a.nsplit * a.rows_pad + row;
   const float2* ml = (const float2*)a.part_ml;
-  float Mx = kNegInf;
-  for (int s = lane; s < nsp; s += 64) Mx = fmaxf(Mx, ml[pbase + (size_t)s * a.rows_pad].x);
+  float Mx = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < nsp; s0 += kGroup) {
+    const int cnt = min(kGroup, nsp - s0);
+    const int sl = s0 + (lane & (kGroup - 1));
+    float2 mlv = make_float2(kNegInf, 0.f);
+    if (sl < nsp) mlv = ml[pbase + (size_t)sl * a.rows_pad];
+    float2 v[kGroup];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
-  float Ls = 0.f, o0 = 0.f, o1 = 0.f;
-  if (Mx != kNegInf) {
-    for (int s0 = 0; s0 < nsp; s0 += 64) {
-      const int s = s0 + lane;
-      float e = 0.f, le = 0.f;
-      if (s < nsp) {
-        const float2 v = ml[pbase + (size_t)s * a.rows_pad];
-        e = (v.x == kNegInf) ? 0.f : fast_exp2((v.x - Mx) * c2);
-        le = e * v.y;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) le += __shfl_xor(le, off);
-      Ls += le;
-      const int cnt = min(64, nsp - s0);
-      int i = 0;
-      for (; i + 8 <= cnt; i += 8) {
-        float2 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + i + u) * a.rows_pad) * kHeadDim + 2 * lane);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float eu = __shfl(e, i + u);
-          o0 += eu * v[u].x;
-          o1 += eu * v[u].y;
-        }
-      }
-      for (; i < cnt; ++i) {
-        const float2 v = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + i) * a.rows_pad) * kHeadDim + 2 * lane);
-        const float eu = __shfl(e, i);
-        o0 += eu * v.x;
-        o1 += eu * v.y;
-      }
+    for (int u = 0; u < kGroup; ++u) {
+      v[u] = make_float2(0.f, 0.f);
+      if (u < cnt) v[u] = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + u) * a.rows_pad) * kHeadDim + 2 * lane);
     }
+    float gm = mlv.x;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+    const float Mn = fmaxf(Mx, gm);
+    if (Mn == kNegInf) continue;  // nothing seen yet
+    const float r = (Mx == kNegInf) ? 0.f : fast_exp2((Mx - Mn) * c2);
+    const float e = (mlv.x == kNegInf) ? 0.f : fast_exp2((mlv.x - Mn) * c2);
+    float le = (lane < kGroup) ? e * mlv.y : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) le += __shfl_xor(le, off);
+    Ls = Ls * r + le;
+    o0 *= r;
+    o1 *= r;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const float eu = __shfl(e, u);
+      o0 += eu * v[u].x;
+      o1 += eu * v[u].y;
+    }
+    Mx = Mn;
   }
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
