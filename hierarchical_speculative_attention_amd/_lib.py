@@ -23,7 +23,8 @@ TF_ACCEPT_PROBS = 1
 EXPORTS = [
     "tf_status_string", "tf_last_error_detail",
     "tf_build_chunk_keys", "tf_score_chunks", "tf_select_topk", "tf_select_topk_workspace_size",
-    "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_stream_attn",
+    "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_sparse_verify_attn",
+    "tf_sparse_verify_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
 ]
 
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         "tf_select_topk_workspace_size": (sz, [i32, i32, i32, i32]),
         "tf_sparse_attn": (ctypes.c_int, [vp, i32, vp, vp, dp, vp, i32, i32, vp, vp, vp, sz, vp]),
         "tf_sparse_attn_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "tf_sparse_verify_attn": (ctypes.c_int, [vp, i32, i32, vp, vp, dp, vp, i32, i32, i32, vp, vp, vp, sz, vp]),
+        "tf_sparse_verify_attn_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "tf_stream_attn": (ctypes.c_int, [vp, i32, vp, vp, dp, i32, i32, vp, vp, vp]),
         "tf_verify_attn": (ctypes.c_int, [vp, i32, i32, vp, vp, dp, vp, vp, vp, sz, vp]),
         "tf_verify_attn_workspace_size": (sz, [i32, i32, i32, i32, i32]),
@@ -220,6 +223,34 @@ def sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc, i
     _check(lib().tf_sparse_attn(_ptr(q), Hq, _ptr(K), _ptr(V), ctypes.byref(kd), _ptr(idx), int(k), int(chunk_size),
                                 _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
                                 _stream(stream, q.device)), "tf_sparse_attn")
+    return out, lse
+
+
+def sparse_verify_attn_workspace_size(B, Hq, H, Q, k, chunk_size, tail) -> int:
+    return int(lib().tf_sparse_verify_attn_workspace_size(B, Hq, H, Q, k, chunk_size, tail))
+
+
+def sparse_verify_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc, idx: torch.Tensor,
+                       chunk_size: int, tail: int, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    _need(q, "q", kv.dtype)
+    _need(K, "K", kv.dtype)
+    _need(V, "V", kv.dtype)
+    _need(idx, "idx", torch.int32)
+    B, Hq, Q = q.shape[0], q.shape[1], q.shape[2]
+    k = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, Q, kv.d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Q), dtype=torch.float32, device=q.device)
+    need = sparse_verify_attn_workspace_size(kv.B, Hq, kv.H, Q, k, chunk_size, tail)
+    if ws is None:
+        ws = workspace(need, q.device)
+    kd = kv.c()
+    _check(lib().tf_sparse_verify_attn(_ptr(q), Hq, Q, _ptr(K), _ptr(V), ctypes.byref(kd), _ptr(idx), int(k),
+                                       int(chunk_size), int(tail), _ptr(out), _ptr(lse), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(stream, q.device)),
+           "tf_sparse_verify_attn")
     return out, lse
 
 

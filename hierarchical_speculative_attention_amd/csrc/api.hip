@@ -92,6 +92,7 @@ void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, 
   a.idx = nullptr;
   a.k = 0;
   a.cs = 1;
+  a.tail = 0;
   a.n_sink = 0;
   a.window = 0;
   a.out = out;
@@ -228,6 +229,50 @@ TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const voi
   a.cs = chunk_size;
   fill_plan(a, plan, ws);
   return check_hip(tfk::launch_attn(kv->dtype, tfk::kSparse, a, (hipStream_t)stream), "tf_sparse_attn");
+}
+
+// ---------------------------------------------------------------------------
+// a4, multi-query form with a causal tail (Force 2 verifying Force 1's drafts)
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_sparse_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t k,
+                                                      int32_t chunk_size, int32_t tail) {
+  if (B < 1 || H < 1 || Hq < 1 || Q < 1 || k < 1 || chunk_size < 1 || tail < 1) return 0;
+  const long virt = (long)k * chunk_size + tail;
+  if (virt > 0x7fffffffL) return 0;
+  return tfk::plan_splits(B, H, (Hq / H) * Q, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw).total_bytes;
+}
+
+TF_EXPORT int tf_sparse_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                                    const tf_kv_desc* kv, const int32_t* idx, int32_t k, int32_t chunk_size,
+                                    int32_t tail, float* out, float* lse, void* ws, size_t ws_bytes,
+                                    tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (Hq < 1 || Hq % kv->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, kv->H);
+  if (Q < 1) return fail(TF_ERR_INVALID_ARG, "Q must be >= 1");
+  if ((long)(Hq / kv->H) * Q > tfk::kMaxRows)
+    return fail(TF_ERR_UNSUPPORTED, "G*Q = %ld query rows per KV head (at most %d)", (long)(Hq / kv->H) * Q,
+                tfk::kMaxRows);
+  if (k < 1 || chunk_size < 1 || chunk_size > 4096) return fail(TF_ERR_INVALID_ARG, "k=%d chunk_size=%d", k, chunk_size);
+  if (tail < Q) return fail(TF_ERR_INVALID_ARG, "tail=%d must cover the Q=%d drafted rows", tail, Q);
+  if ((long)k * chunk_size + tail > 0x7fffffffL) return fail(TF_ERR_UNSUPPORTED, "k * chunk_size + tail too large");
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  TRY(check_ptr(idx, "idx", 4));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, k * chunk_size + tail,
+                                               kSparseTargetWgs, tfk::kSparseMaxTpw);
+  TRY(check_ws(ws, ws_bytes, plan.total_bytes));
+  tfk::AttnArgs a;
+  fill_common(a, q, K, V, kv, Hq, Q, out, lse);
+  a.idx = idx;
+  a.k = k;
+  a.cs = chunk_size;
+  a.tail = tail;
+  fill_plan(a, plan, ws);
+  return check_hip(tfk::launch_attn(kv->dtype, tfk::kSparseTail, a, (hipStream_t)stream), "tf_sparse_verify_attn");
 }
 
 // ---------------------------------------------------------------------------

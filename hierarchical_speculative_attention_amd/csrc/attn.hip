@@ -69,7 +69,7 @@ struct Geo {
   int cap;     // rows allocated per head
   int L;       // virtual tokens
   int s_eff;   // stream: sinks present
-  int lo;      // stream: first window position
+  int lo;      // stream: first window position; sparse with tail: first tail row
   int ring;    // stream: ring slots (cap - n_sink)
   int nchunks; // sparse: chunks covering the n valid rows
 };
@@ -102,6 +102,10 @@ __device__ __forceinline__ Geo make_geo(const AttnArgs& a, int b) {
     g.n = n;
     g.L = (MODE == kVerify) ? n : a.k * a.cs;
     g.nchunks = (n + a.cs - 1) / a.cs;
+    if (MODE == kSparseTail) {
+      g.lo = max(0, n - a.tail);       // first tail row
+      g.L = a.k * a.cs + (n - g.lo);   // chunk rows, then the tail
+    }
   }
   return g;
 }
@@ -112,12 +116,15 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
                                        const int* s_idx, int chunk_lo) {
   if (v >= v_end) return -1;
   if (MODE == kVerify) return v;
-  if (MODE == kSparse) {
+  if (MODE == kSparse || MODE == kSparseTail) {
+    const int kcs = a.k * a.cs;
+    if (MODE == kSparseTail && v >= kcs) return g.lo + (v - kcs);  // tail row (< n since v < L)
     int slot = v / a.cs;
     const int c = s_idx[slot - chunk_lo];
     if (c < 0 || c >= g.nchunks) return -1;  // padding or out of range: nothing read
     const int row = c * a.cs + (v - slot * a.cs);
-    return row < g.n ? row : -1;
+    // with a tail, chunk rows from the tail on are attended as tail rows
+    return row < (MODE == kSparseTail ? g.lo : g.n) ? row : -1;
   }
   // stream
   int slot;
@@ -246,7 +253,8 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const unsigned mk0 = mask & 0xFFFFu, mk1 = mask >> 16;
   // Whole tile visible to every row: no per-element masking needed.
-  const bool full = mask == 0xFFFFFFFFu && (MODE != kVerify || t0 + 31 <= lim_min);
+  constexpr bool kCausal = MODE == kVerify || MODE == kSparseTail;
+  const bool full = mask == 0xFFFFFFFFu && (!kCausal || t0 + 31 <= lim_min);
   V8 ph[NQT], pl[NQT];
   V8 k0[4], k1[4];
 #pragma unroll
@@ -266,8 +274,8 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * lg + r;
-        const bool vis0 = ((mk0 >> j) & 1u) && (MODE != kVerify || t0 + j <= lim[qt]);
-        const bool vis1 = ((mk1 >> j) & 1u) && (MODE != kVerify || t0 + 16 + j <= lim[qt]);
+        const bool vis0 = ((mk0 >> j) & 1u) && (!kCausal || t0 + j <= lim[qt]);
+        const bool vis1 = ((mk1 >> j) & 1u) && (!kCausal || t0 + 16 + j <= lim[qt]);
         s0[r] = vis0 ? s0[r] : kNegInf;
         s1[r] = vis1 ? s1[r] : kNegInf;
       }
@@ -336,7 +344,7 @@ void attn_kernel(const AttnArgs a) {
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr bool kStaged = MODE == kVerify;
-  __shared__ int s_idx[MODE == kSparse ? kMaxSparseIdx : 1];
+  __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
@@ -358,7 +366,7 @@ void attn_kernel(const AttnArgs a) {
   const uint16_t* __restrict__ Vb = a.V + base;
 
   int chunk_lo = 0;
-  if (MODE == kSparse) {
+  if (MODE == kSparse || MODE == kSparseTail) {
     chunk_lo = v0 / a.cs;
     const int chunk_hi = min(a.k, (v1 + a.cs - 1) / a.cs);
     const int32_t* src = a.idx + ((size_t)b * a.Hkv + hk) * a.k;
@@ -379,9 +387,15 @@ void attn_kernel(const AttnArgs a) {
       if (row < a.rows) x = *(const u32x4*)(a.q + (qrow0 + row) * kHeadDim + 32 * s + 8 * lg);
       qreg[qt][s] = __builtin_bit_cast(V8, x);
     }
-    lim[qt] = (MODE == kVerify) ? geo.n - a.Qn + (row % a.Qn) : 0x7fffffff;
+    // Causal limit of this lane's query row i = row % Qn, as a virtual token:
+    // verify sees cache rows <= n - Qn + i; with a tail, virtual token
+    // k*cs + (r - lo) is cache row r.
+    const int causal0 = (MODE == kVerify) ? geo.n - a.Qn : a.k * a.cs + (geo.n - geo.lo) - a.Qn;
+    lim[qt] = (MODE == kVerify || MODE == kSparseTail) ? causal0 + (row % a.Qn) : 0x7fffffff;
   }
-  const int lim_min = (MODE == kVerify) ? geo.n - a.Qn : 0x7fffffff;
+  const int lim_min = (MODE == kVerify)       ? geo.n - a.Qn
+                      : (MODE == kSparseTail) ? a.k * a.cs + (geo.n - geo.lo) - a.Qn
+                                              : 0x7fffffff;
 
   // Selection matrices: column j of half h picks dim 16h + j of a 32-dim k-window.
   V8 sel[2];
@@ -609,6 +623,7 @@ static hipError_t launch_mode(int mode, const AttnArgs& a, hipStream_t stream) {
     case kVerify: return launch_nqt<DT, kVerify>(a, stream);
     case kSparse: return launch_nqt<DT, kSparse>(a, stream);
     case kStream: return launch_nqt<DT, kStream>(a, stream);
+    case kSparseTail: return launch_nqt<DT, kSparseTail>(a, stream);
   }
   return hipErrorInvalidValue;
 }

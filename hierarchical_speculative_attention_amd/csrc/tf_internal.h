@@ -15,7 +15,7 @@ constexpr int kThreads = 256;          // 4 waves of 64 lanes
 constexpr int kTile = 32;              // virtual tokens per wave iteration
 constexpr int kMaxRows = 64;           // query rows per KV head (4 MFMA query tiles)
 
-enum AttnMode { kVerify = 0, kSparse = 1, kStream = 2 };
+enum AttnMode { kVerify = 0, kSparse = 1, kStream = 2, kSparseTail = 3 };
 
 struct AttnArgs {
   const uint16_t* q;        // [B][Hq][Qn][d]
@@ -29,6 +29,7 @@ struct AttnArgs {
   // sparse
   const int32_t* idx;       // [B][Hkv][k]
   int32_t k, cs;
+  int32_t tail;             // sparse with tail: most recent rows attended causally
   // stream
   int32_t n_sink, window;
   // split-K

@@ -147,6 +147,26 @@ int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const void* V,
 size_t tf_sparse_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t k, int32_t chunk_size);
 
 /*
+ * a4, multi-query form: Force 2 verifying the small drafter's tokens on the
+ * sparse cache ([blog] Force 2 evaluates the candidates from Force 1;
+ * "2. Dual Rejection Sampling" then tests them r -> q).  The cache already
+ * holds the Q drafted rows as its last Q rows (as for tf_verify_attn).  With
+ * n = n_b and t0 = max(0, n - tail), query row i (0 <= i < Q) of head h sees
+ *   { rows of the chunks idx[b][g][0..k) below t0 }  U  [t0, n - Q + i]
+ * (g = h / G; entries < 0 skipped).  With every chunk selected, or tail >= n,
+ * this is tf_verify_attn.  Requires tail >= Q.
+ *   q  : device [B][Hq][Q][d] in kv->dtype.  out: device fp32 [B][Hq][Q][d].
+ *   lse: device fp32 [B][Hq][Q] or NULL.     idx: device int32 [B][H][k].
+ *   ws : tf_sparse_verify_attn_workspace_size(kv->B, Hq, kv->H, Q, k, chunk_size, tail).
+ */
+int tf_sparse_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                          const tf_kv_desc* kv, const int32_t* idx, int32_t k, int32_t chunk_size,
+                          int32_t tail, float* out, float* lse, void* ws, size_t ws_bytes,
+                          tf_stream_t stream);
+size_t tf_sparse_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t k,
+                                            int32_t chunk_size, int32_t tail);
+
+/*
  * a5  Sink + window streaming attention.  [blog] Force 1 drafts on a cache of
  * the initial sink tokens plus the most recent W tokens (StreamingLLM).
  * With n = sd->seq_len[b] the logical length, the visible positions are

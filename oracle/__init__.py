@@ -3,7 +3,8 @@ imported by the tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path)."""
 from .triforce_oracle import (  # noqa: F401
     NEG_INF, widen, round_f64_to_bits, chunk_keys, chunk_scores, select_topk,
-    attention, sparse_token_positions, sparse_attn, stream_positions,
+    attention, sparse_token_positions, sparse_attn, sparse_verify_positions, sparse_verify_attn,
+    stream_positions,
     stream_attn_masked, stream_attn_ring, verify_attn, distribution,
     inverse_cdf, accept,
 )

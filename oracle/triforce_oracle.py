@@ -180,6 +180,35 @@ def sparse_attn(q: np.ndarray, K: np.ndarray, V: np.ndarray, n: int,
     return attention(q, K[pos], V[pos])
 
 
+def sparse_verify_positions(n: int, Q: int, i: int, idx: Sequence[int], chunk_size: int,
+                            tail: int) -> np.ndarray:
+    """Rows seen by query row i when the retrieval-sparse cache verifies Q
+    drafted rows: the rows of the selected chunks that lie below the tail,
+    then the tail [t0, n - Q + i] with t0 = max(0, n - tail)."""
+    t0 = max(0, n - tail)
+    chunk_rows = [int(p) for p in sparse_token_positions(idx, chunk_size, n) if p < t0]
+    return np.asarray(chunk_rows + list(range(t0, max(t0, n - Q + i + 1))), np.int64)
+
+
+def sparse_verify_attn(qs: np.ndarray, K: np.ndarray, V: np.ndarray, n: int, idx: Sequence[int],
+                       chunk_size: int, tail: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Force 2 verifying the small drafter's tokens on the sparse cache.
+
+    [blog] "1. The Three Forces of TriForce", Force 2 evaluates the candidates
+    from Force 1 on a retrieval-sparse KV cache; "2. Dual Rejection Sampling"
+    then tests them r -> q.  Readings: the Q drafted rows are the last Q cache
+    rows (as for the full verification); each query row attends the retrieved
+    chunks below a causal tail of the most recent `tail` rows (tail >= Q) and
+    the tail up to its own position.  qs: [Q][d].  Returns o [Q][d], lse [Q]."""
+    Q, d = qs.shape
+    o = np.zeros((Q, d), np.float64)
+    lse = np.zeros(Q, np.float64)
+    for i in range(Q):
+        pos = sparse_verify_positions(n, Q, i, idx, chunk_size, tail)
+        o[i], lse[i] = attention(qs[i], K[pos], V[pos])
+    return o, lse
+
+
 # ---------------------------------------------------------------------------
 # a5  Sink + window streaming attention
 # ---------------------------------------------------------------------------

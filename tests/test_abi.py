@@ -26,7 +26,7 @@ def declared():
 
 def test_every_declared_function_is_exported():
     names = declared()
-    assert len(names) >= 13
+    assert len(names) >= 15
     L = T.lib()
     for n in names:
         assert hasattr(L, n), n

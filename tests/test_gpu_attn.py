@@ -168,3 +168,62 @@ def test_stream_parity(dtype, S, W):
             o_ref[b, h], l_ref[b, h] = oracle.stream_attn_masked(
                 q, oracle.widen(s.K_logical[b][g], dtype), oracle.widen(s.V_logical[b][g], dtype), n, S, W)
     compare_attn(out, lse, o_ref, l_ref)
+
+
+# ---------------------------------------------------------------------------
+# multi-query sparse verification with a causal tail (Force 2 over Force 1)
+# ---------------------------------------------------------------------------
+
+def oracle_sparse_verify(inp, idx, cs, tail, Q):
+    lay, dt = inp.layout, inp.dtype
+    G = inp.Hq // lay.H
+    o = np.zeros((lay.B, inp.Hq, Q, lay.d))
+    lse = np.zeros((lay.B, inp.Hq, Q))
+    for b in range(lay.B):
+        n = int(lay.seq_len[b])
+        for g in range(lay.H):
+            K = oracle.widen(lay.head(inp.K, b, g), dt)
+            V = oracle.widen(lay.head(inp.V, b, g), dt)
+            for j in range(G):
+                h = g * G + j
+                o[b, h], lse[b, h] = oracle.sparse_verify_attn(oracle.widen(inp.q_verify[b, h], dt), K, V, n,
+                                                               idx[b, g], cs, tail)
+    return o, lse
+
+
+def run_sparse_verify(inp, idx, cs, tail):
+    kv = desc(inp.layout, inp.dtype)
+    out, lse = tf.sparse_verify_attn(dev(inp.q_verify, inp.dtype), dev(inp.K, inp.dtype), dev(inp.V, inp.dtype),
+                                     kv, torch.from_numpy(idx.astype(np.int32)).cuda(), cs, tail)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("tail", [5, 16, 100, 5000])
+def test_sparse_verify_ragged_gqa(tail):
+    lens = [3, 50, 1001, 4099]
+    Q, cs, k = 5, 8, 40
+    inp = synth.make_attn_inputs(lens=lens, Hq=8, Hkv=2, dtype="bf16", Q=Q, seed=40, cap_extra=7)
+    rng = np.random.default_rng(tail)
+    idx = np.full((4, 2, k), -1, np.int64)
+    for b, n in enumerate(lens):
+        C = -(-n // cs)
+        for g in range(2):
+            m = min(k - 2, C)
+            idx[b, g, :m] = np.sort(rng.choice(C, size=m, replace=False))
+            idx[b, g, m] = C - 1          # the last chunk: inside the tail
+            idx[b, g, m + 1] = C + 3      # past the end
+    out, lse = run_sparse_verify(inp, idx, cs, tail)
+    compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
+
+
+def test_sparse_verify_full_selection_equals_verify():
+    inp = synth.make_attn_inputs(lens=[3000, 777], Hq=4, Hkv=4, dtype="fp16", Q=7, seed=41)
+    C = -(-3000 // 8)
+    idx = np.full((2, 4, C), -1, np.int64)
+    idx[0, :, :] = np.arange(C)
+    idx[1, :, :98] = np.arange(98)
+    out, lse = run_sparse_verify(inp, idx, 8, 7)
+    vo, vl = run_verify(inp, 7)
+    assert (out - vo).abs().max().item() <= ATOL
+    compare_attn(out, lse, *oracle_sparse_verify(inp, idx, 8, 7, 7))

@@ -155,3 +155,20 @@ def test_stream_full_logical_length():
             V_log[p] = oracle.widen(vslots[synth.ring_slot(int(p), S, cap)], "bf16")
         o, l = oracle.stream_attn_masked(oracle.widen(qb[0, h], "bf16"), K_log, V_log, n, S, Wn)
         assert np.abs(o_h[0, h] - o).max() <= ATOL and abs(l_h[0, h] - l) <= ATOL
+
+
+def test_llama2_7b_128k_sparse_verify_with_tail():
+    # Force 2 verifying gamma1 = 4 drafted rows over the retrieved 4096 tokens + a 64-row tail
+    Q, tail = 5, 64
+    W, K, V, qv, qd, lay, planted = layer("llama2-7b-128k-1layer", Q)
+    kv, ck, ckl, scores, idx = retrieval(W, K, qd, lay, W["budget"])
+    out, lse = tf.sparse_verify_attn(qv, K, V, kv, idx, W["chunk_size"], tail)
+    torch.cuda.synchronize()
+    ix, qv_b = idx.cpu().numpy(), host_bits(qv)
+    o_h, l_h = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    for g in [0, 21]:
+        Kh = oracle.widen(head_bits_gpu(K, lay, 0, g).reshape(-1, 128), "bf16")
+        Vh = oracle.widen(head_bits_gpu(V, lay, 0, g).reshape(-1, 128), "bf16")
+        o, l = oracle.sparse_verify_attn(oracle.widen(qv_b[0, g], "bf16"), Kh, Vh, Kh.shape[0], ix[0, g],
+                                         W["chunk_size"], tail)
+        assert np.abs(o_h[0, g] - o).max() <= ATOL and np.abs(l_h[0, g] - l).max() <= ATOL

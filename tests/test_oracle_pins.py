@@ -384,3 +384,39 @@ def test_inverse_cdf_never_draws_zero_weight():
     for u in np.linspace(1e-9, 1 - 1e-9, 2001):
         assert oracle.inverse_cdf(r, u) in (1, 4)
     assert oracle.inverse_cdf(r, 0.3 / 1.0) == 4   # u*Z on a running sum -> strictly past it
+
+
+# ---------------------------------------------------------------------------
+# multi-query sparse verification with a causal tail
+# ---------------------------------------------------------------------------
+
+def test_sparse_verify_full_selection_and_tail_is_full_verify():
+    rng = np.random.default_rng(59)
+    n, Q, cs = 203, 5, 8
+    qs, K, V = rng.standard_normal((Q, 128)), rng.standard_normal((n, 128)), rng.standard_normal((n, 128))
+    C = -(-n // cs)
+    o, lse = oracle.sparse_verify_attn(qs, K, V, n, list(range(C)), cs, tail=Q)
+    o2, lse2 = oracle.verify_attn(qs, K, V, n)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-12, atol=1e-12)
+    o, lse = oracle.sparse_verify_attn(qs, K, V, n, [-1] * 4, cs, tail=n)  # tail covers everything
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_verify_rows_match_masked_library_attention():
+    rng = np.random.default_rng(61)
+    n, Q, cs, tail = 100, 3, 8, 10
+    qs, K, V = rng.standard_normal((Q, 128)), rng.standard_normal((n, 128)), rng.standard_normal((n, 128))
+    idx = [2, 7, 11, 12, -1]   # chunk 11 straddles the tail start 90, chunk 12 lies inside it
+    o, _ = oracle.sparse_verify_attn(qs, K, V, n, idx, cs, tail)
+    for i in range(Q):
+        mask = np.zeros(n, bool)
+        mask[16:24] = True      # chunk 2
+        mask[56:64] = True      # chunk 7
+        mask[88:90] = True      # chunk 11 below the tail
+        mask[90:n - Q + i + 1] = True
+        np.testing.assert_allclose(o[i], sdpa(qs[i], K, V, mask), rtol=1e-12, atol=1e-13)
+    # no chunk selected: the tail alone, i.e. verification of the last `tail` rows
+    o, _ = oracle.sparse_verify_attn(qs, K, V, n, [-1], cs, tail)
+    o2, _ = oracle.verify_attn(qs, K[n - tail:], V[n - tail:], tail)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
