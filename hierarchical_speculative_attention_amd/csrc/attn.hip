@@ -74,11 +74,30 @@ struct Geo {
   int nchunks; // sparse: chunks covering the n valid rows
 };
 
+// The per-sequence descriptor values, read once at kernel entry.
+struct SeqDesc {
+  int64_t base;
+  int cap, len;
+};
+
+// Loads the descriptor of sequence b.  The empty asm uses the three values in
+// scalar registers at this point, so the loads cannot be sunk past later
+// branches: they are issued together, and their one round trip overlaps the
+// vector loads already in flight.
+__device__ __forceinline__ SeqDesc load_seq(const AttnArgs& a, int b) {
+  SeqDesc d;
+  d.base = a.seq_base[b];
+  d.cap = a.seq_cap[b];
+  d.len = a.seq_len[b];
+  asm volatile("" : : "s"(d.base), "s"(d.cap), "s"(d.len));
+  return d;
+}
+
 template <int MODE>
-__device__ __forceinline__ Geo make_geo(const AttnArgs& a, int b) {
+__device__ __forceinline__ Geo make_geo(const AttnArgs& a, const SeqDesc& d) {
   Geo g;
-  g.cap = a.seq_cap[b];
-  int n = a.seq_len[b];
+  g.cap = d.cap;
+  int n = d.len;
   g.s_eff = 0;
   g.lo = 0;
   g.ring = 0;
@@ -354,30 +373,31 @@ void attn_kernel(const AttnArgs a) {
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-
-  const Geo geo = make_geo<MODE>(a, b);
-  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
-  if (split >= nsp) return;
   const int v0 = split * a.tpw;
-  const int v1 = min(geo.L, v0 + a.tpw);
 
-  const size_t base = (size_t)a.seq_base[b] + (size_t)hk * (size_t)geo.cap * kHeadDim;
-  const uint16_t* __restrict__ Kb = a.K + base;
-  const uint16_t* __restrict__ Vb = a.V + base;
-
-  int chunk_lo = 0;
-  if (MODE == kSparse || MODE == kSparseTail) {
+  // Loads that need only the arguments (chunk slots, query rows) are issued
+  // before the sequence geometry is read, so their round trips overlap it.
+  // The slots fetched cover every chunk virtual tokens [v0, v0 + tpw) can
+  // touch, clamped to the k slots of the row, so they stay in bounds whatever
+  // the sequence length turns out to be.
+  constexpr bool kSparseIdx = MODE == kSparse || MODE == kSparseTail;
+  constexpr int kIdxPerThread = kSparseIdx ? (kMaxSparseIdx + kThreads - 1) / kThreads : 1;
+  int chunk_lo = 0, n_idx = 0;
+  int idx_reg[kIdxPerThread];
+  if (kSparseIdx) {
     chunk_lo = v0 / a.cs;
-    const int chunk_hi = min(a.k, (v1 + a.cs - 1) / a.cs);
-    const int32_t* src = a.idx + ((size_t)b * a.Hkv + hk) * a.k;
-    for (int j = tid; j < chunk_hi - chunk_lo; j += kThreads) s_idx[j] = src[chunk_lo + j];
-    __syncthreads();
+    n_idx = min(a.k, (v0 + a.tpw + a.cs - 1) / a.cs) - chunk_lo;
+    const int32_t* src = a.idx + ((size_t)b * a.Hkv + hk) * a.k + chunk_lo;
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+      const int j = tid + u * kThreads;
+      idx_reg[u] = j < n_idx ? src[j] : -1;
+    }
   }
 
   // Query rows of this KV head: heads hk*G .. hk*G+G-1, Qn rows each, contiguous.
   const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
   V8 qreg[NQT][4];
-  int lim[NQT];
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int row = qt * 16 + lq;
@@ -387,6 +407,31 @@ void attn_kernel(const AttnArgs a) {
       if (row < a.rows) x = *(const u32x4*)(a.q + (qrow0 + row) * kHeadDim + 32 * s + 8 * lg);
       qreg[qt][s] = __builtin_bit_cast(V8, x);
     }
+  }
+
+  const SeqDesc sd = load_seq(a, b);
+  const Geo geo = make_geo<MODE>(a, sd);
+  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+  if (split >= nsp) return;
+  const int v1 = min(geo.L, v0 + a.tpw);
+
+  const size_t base = (size_t)sd.base + (size_t)hk * (size_t)geo.cap * kHeadDim;
+  const uint16_t* __restrict__ Kb = a.K + base;
+  const uint16_t* __restrict__ Vb = a.V + base;
+
+  if (kSparseIdx) {
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+      const int j = tid + u * kThreads;
+      if (j < n_idx) s_idx[j] = idx_reg[u];
+    }
+    __syncthreads();
+  }
+
+  int lim[NQT];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int row = qt * 16 + lq;
     // Causal limit of this lane's query row i = row % Qn, as a virtual token:
     // verify sees cache rows <= n - Qn + i; with a tail, virtual token
     // k*cs + (r - lo) is cache row r.
@@ -527,31 +572,43 @@ void attn_kernel(const AttnArgs a) {
 // needed inside the attention kernel.  Splits are taken in groups of 32: the
 // group's (max, sum) pairs and its 32 accumulator rows are all requested
 // before any is used, so a group costs one memory round trip; groups are
-// folded with an online rescale.
+// folded with an online rescale.  The first group is requested before the
+// sequence geometry is read: every split index below the planned split count
+// lies inside the workspace, and splits past this sequence's own count are
+// dropped by selection (their contents are never combined arithmetically).
 template <int MODE>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   constexpr int kGroup = 32;
   const int row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const Geo geo = make_geo<MODE>(a, b);
-  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
-  if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
   const int lane = threadIdx.x;
   const float c2 = a.scale_log2;
   const size_t bh = (size_t)b * a.Hkv + hk;
   const size_t pbase = bh * a.nsplit * a.rows_pad + row;
   const float2* ml = (const float2*)a.part_ml;
+
+  float2 mlv;
+  float2 v[kGroup];
+  auto load_group = [&](int s0, int bound) {
+    const int sl = s0 + (lane & (kGroup - 1));
+    mlv = sl < bound ? ml[pbase + (size_t)sl * a.rows_pad] : make_float2(kNegInf, 0.f);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      v[u] = (s0 + u < bound) ? *(const float2*)(a.part_o + (pbase + (size_t)(s0 + u) * a.rows_pad) * kHeadDim + 2 * lane)
+                              : make_float2(0.f, 0.f);
+  };
+  load_group(0, a.nsplit);
+
+  const Geo geo = make_geo<MODE>(a, load_seq(a, b));
+  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+  if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
+
   float Mx = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += kGroup) {
-    const int cnt = min(kGroup, nsp - s0);
-    const int sl = s0 + (lane & (kGroup - 1));
-    float2 mlv = make_float2(kNegInf, 0.f);
-    if (sl < nsp) mlv = ml[pbase + (size_t)sl * a.rows_pad];
-    float2 v[kGroup];
+    if (s0 > 0) load_group(s0, nsp);
+    if (s0 + (lane & (kGroup - 1)) >= nsp) mlv = make_float2(kNegInf, 0.f);
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      v[u] = make_float2(0.f, 0.f);
-      if (u < cnt) v[u] = *(const float2*)(a.part_o + (pbase + (size_t)(s0 + u) * a.rows_pad) * kHeadDim + 2 * lane);
-    }
+    for (int u = 0; u < kGroup; ++u)
+      if (s0 + u >= nsp) v[u] = make_float2(0.f, 0.f);
     float gm = mlv.x;
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
