@@ -362,3 +362,76 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
         lo = cs[nxt - 1] if nxt > 0 else 0.0
         margin = min(margin, abs(cs[nxt] - tgt), abs(tgt - lo))
     return j, nxt, margin
+
+
+# ---------------------------------------------------------------------------
+# Cache maintenance around the path: drafted rows enter the caches before
+# they are verified, rejected ones leave them.
+# ---------------------------------------------------------------------------
+
+APPEND_OK, APPEND_NO_ROOM, APPEND_RING_TOO_SMALL, APPEND_BAD_LENGTH = 0, 1, 2, 3
+
+
+def append_full(rows: np.ndarray, n: int, new: np.ndarray) -> Tuple[np.ndarray, int]:
+    """Full cache of one (sequence, head): rows [cap][d], n valid.  The R new
+    rows go to positions n .. n + R - 1; a sequence without room for all of
+    them is left as it is.  [blog] Force 3 reads the complete cache, which by
+    the verification reading already holds the drafted rows.  Returns the
+    updated copy and a status."""
+    cap, R = rows.shape[0], new.shape[0]
+    out = rows.copy()
+    if n < 0:
+        return out, APPEND_BAD_LENGTH
+    if n + R > cap:
+        return out, APPEND_NO_ROOM
+    out[n:n + R] = new
+    return out, APPEND_OK
+
+
+def ring_slot_of(p: int, n_sink: int, cap: int) -> int:
+    """Slot of logical position p in a streaming cache of cap slots: the
+    first n_sink positions keep their own slot, later ones cycle through the
+    remaining cap - n_sink slots."""
+    if p < n_sink:
+        return p
+    return n_sink + (p - n_sink) % (cap - n_sink)
+
+
+def append_ring(slots: np.ndarray, n: int, n_sink: int, window: int,
+                new: np.ndarray, reserve: Optional[int] = None) -> Tuple[np.ndarray, int]:
+    """Streaming cache of one (sequence, head) after n logical positions:
+    the R new rows become positions n .. n + R - 1.  [blog] Force 1 keeps the
+    sinks and a rolling window of the W most recent tokens.  Reading:
+    `reserve` (default R) bounds the rows appended since the last length that
+    can no longer be rolled back; the ring keeps window + reserve slots after
+    the sinks, so a rollback to any later length never exposes a visible
+    position whose slot a newer row took.  A ring without that room is left
+    as it is."""
+    cap, R = slots.shape[0], new.shape[0]
+    reserve = R if reserve is None else reserve
+    out = slots.copy()
+    if n < 0:
+        return out, APPEND_BAD_LENGTH
+    if cap - n_sink < window + reserve:
+        return out, APPEND_RING_TOO_SMALL
+    for r in range(R):
+        out[ring_slot_of(n + r, n_sink, cap)] = new[r]
+    return out, APPEND_OK
+
+
+def ring_visible(slots: np.ndarray, n: int, n_sink: int, window: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The positions a5 attends after n logical positions, and the rows the
+    ring holds for them (in position order)."""
+    pos = stream_positions(n, n_sink, window)
+    cap = slots.shape[0]
+    return pos, slots[[ring_slot_of(int(p), n_sink, cap) for p in pos]]
+
+
+def commit_length(n: int, add: int, gamma: int = 0, n_accepted: Optional[int] = None) -> int:
+    """Length after a decode step: `add` appended rows become valid, and with
+    an accept result the gamma - n_accepted rejected drafts leave again
+    ([blog] "2. Dual Rejection Sampling": the tokens after the first
+    rejection are discarded).  n_accepted is clamped into [0, gamma]; the
+    length never goes below 0."""
+    drop = 0 if n_accepted is None else gamma - min(max(int(n_accepted), 0), gamma)
+    return max(0, n + add - drop)

@@ -89,6 +89,23 @@ def accept_no_bonus(target, draft, tokens, uniforms, temperature, probs=False):
 ORIG_ACCEPT = T.accept
 
 
+def append_ring_short_reserve(slots, n, n_sink, window, new, reserve=None):
+    reserve = new.shape[0] if reserve is None else reserve
+    return ORIG_APPEND_RING(slots, n, n_sink, window, new, reserve - 1)   # mistake: one slot of slack short
+
+
+ORIG_APPEND_RING = T.append_ring
+
+
+def commit_drops_one_more(n, add, gamma=0, n_accepted=None):
+    drop = 0 if n_accepted is None else gamma - min(max(int(n_accepted), 0), gamma) + 1  # mistake
+    return max(0, n + add - drop)
+
+
+def ring_slot_one_short(p, n_sink, cap):
+    return p if p < n_sink else n_sink + (p - n_sink) % (cap - n_sink - 1)   # mistake: ring one slot short
+
+
 CASES = [
     ("verify_attn", verify_off_by_one, pins.test_verify_rows_are_prefix_attention),
     ("verify_attn", verify_off_by_one, pins.test_verify_alignment_closed_form),
@@ -98,6 +115,10 @@ CASES = [
     ("stream_positions", stream_positions_short, lambda: pins.test_stream_ring_equals_mask_and_library(1000, 4, 252)),
     ("accept", accept_flipped_residual, pins.test_accept_hand_examples),
     ("accept", accept_no_bonus, pins.test_accept_hand_examples),
+    ("append_ring", append_ring_short_reserve, pins.test_ring_without_slack_refuses_and_would_corrupt),
+    ("commit_length", commit_drops_one_more, pins.test_commit_length_closed_forms),
+    ("commit_length", commit_drops_one_more, pins.test_full_cache_decode_loop_matches_list_model),
+    ("ring_slot_of", ring_slot_one_short, pins.test_ring_slot_hand_table),
 ]
 
 

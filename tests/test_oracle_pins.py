@@ -420,3 +420,107 @@ def test_sparse_verify_rows_match_masked_library_attention():
     o, _ = oracle.sparse_verify_attn(qs, K, V, n, [-1], cs, tail)
     o2, _ = oracle.verify_attn(qs, K[n - tail:], V[n - tail:], tail)
     np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# cache maintenance: a decode loop against a plain list model
+# ---------------------------------------------------------------------------
+
+def test_commit_length_closed_forms():
+    assert oracle.commit_length(10, 7) == 17
+    assert oracle.commit_length(17, 0, gamma=6, n_accepted=2) == 13     # 4 rejected drafts leave
+    assert oracle.commit_length(17, 0, gamma=6, n_accepted=6) == 17     # all kept
+    assert oracle.commit_length(17, 0, gamma=6, n_accepted=9) == 17     # clamped to gamma
+    assert oracle.commit_length(17, 0, gamma=6, n_accepted=-3) == 11    # clamped to 0
+    assert oracle.commit_length(2, 0, gamma=6, n_accepted=0) == 0       # never below 0
+
+
+def test_full_cache_decode_loop_matches_list_model():
+    rng = np.random.default_rng(71)
+    cap, d = 120, 4
+    rows = np.full((cap, d), 1000.0)
+    model = [rng.standard_normal(d) for _ in range(20)]
+    rows[:20] = np.array(model)
+    n = 20
+    no_room = 0
+    for step in range(60):
+        gamma = int(rng.integers(1, 7))
+        new = rng.standard_normal((gamma + 1, d))
+        rows2, st = oracle.append_full(rows, n, new)
+        if n + gamma + 1 > cap:
+            assert st == oracle.APPEND_NO_ROOM and np.array_equal(rows2, rows)
+            no_room += 1
+            n = oracle.commit_length(n, 0, gamma, 0) if n > 60 else n   # free some room
+            model = model[:n]
+            continue
+        assert st == oracle.APPEND_OK
+        rows = rows2
+        n = oracle.commit_length(n, gamma + 1)
+        model += list(new)
+        n_acc = int(rng.integers(0, gamma + 1))
+        n = oracle.commit_length(n, 0, gamma, n_acc)
+        model = model[:len(model) - (gamma - n_acc)]
+        assert n == len(model)
+        np.testing.assert_array_equal(rows[:n], np.array(model))
+    assert no_room > 0
+    assert oracle.append_full(rows, -1, new)[1] == oracle.APPEND_BAD_LENGTH
+
+
+@pytest.mark.parametrize("n_sink,window,slack", [(4, 10, 6), (0, 7, 3), (2, 1, 5)])
+def test_ring_decode_loop_matches_list_model(n_sink, window, slack):
+    # Force 1 drafts one row at a time (gamma1 appends of R = 1 with
+    # reserve = gamma1), then Force 2's result rolls the rejected ones back.
+    rng = np.random.default_rng(73 + window)
+    d, cap = 3, n_sink + window + slack
+    slots = np.full((cap, d), 1000.0)
+    model = []
+    n = 0
+    for step in range(150):
+        g1 = int(rng.integers(1, slack + 1))
+        for r in range(g1):
+            row = rng.standard_normal((1, d))
+            slots, st = oracle.append_ring(slots, n, n_sink, window, row, reserve=g1)
+            assert st == oracle.APPEND_OK
+            n = oracle.commit_length(n, 1)
+            model.append(row[0])
+            # every intermediate length is readable
+            pos, held = oracle.ring_visible(slots, n, n_sink, window)
+            np.testing.assert_array_equal(held, np.array(model)[pos])
+        n_acc = int(rng.integers(0, g1 + 1))
+        n = oracle.commit_length(n, 0, g1, n_acc)
+        model = model[:n]
+        pos, held = oracle.ring_visible(slots, n, n_sink, window)
+        np.testing.assert_array_equal(held, np.array(model)[pos] if n else np.zeros((0, d)))
+    # the ring's attention equals streaming attention over the logical sequence
+    q = rng.standard_normal(d)
+    pos, held = oracle.ring_visible(slots, n, n_sink, window)
+    o_ring, l_ring = oracle.attention(q, held, held[:, ::-1])
+    L = np.array(model)
+    o_log, l_log = oracle.stream_attn_masked(q, L, L[:, ::-1], n, n_sink, window)
+    np.testing.assert_allclose(o_ring, o_log, rtol=1e-13, atol=1e-14)
+    assert abs(l_ring - l_log) < 1e-12
+
+
+def test_ring_without_slack_refuses_and_would_corrupt():
+    n_sink, window, d = 2, 5, 2
+    cap = n_sink + window + 2
+    slots = np.arange(cap * d, dtype=np.float64).reshape(cap, d)
+    new = np.ones((3, d))
+    out, st = oracle.append_ring(slots, 30, n_sink, window, new)       # reserve 3 > slack 2
+    assert st == oracle.APPEND_RING_TOO_SMALL and np.array_equal(out, slots)
+    # what the check prevents: writing anyway overwrites a position that is
+    # visible again after rolling the three rows back
+    forced = slots.copy()
+    for r in range(3):
+        forced[oracle.ring_slot_of(30 + r, n_sink, cap)] = new[r]
+    vis_slots = {oracle.ring_slot_of(int(p), n_sink, cap) for p in oracle.stream_positions(30, n_sink, window)}
+    assert any(oracle.ring_slot_of(30 + r, n_sink, cap) in vis_slots for r in range(3))
+    out, st = oracle.append_ring(slots, 30, n_sink, window, new[:2])  # reserve 2 fits
+    assert st == oracle.APPEND_OK
+
+
+def test_ring_slot_hand_table():
+    # 2 sinks, 7 slots: positions 0 and 1 keep slots 0 and 1, later positions
+    # cycle through slots 2..6
+    assert [oracle.ring_slot_of(p, 2, 7) for p in range(13)] == [0, 1, 2, 3, 4, 5, 6, 2, 3, 4, 5, 6, 2]
+    assert [oracle.ring_slot_of(p, 0, 3) for p in range(7)] == [0, 1, 2, 0, 1, 2, 0]
