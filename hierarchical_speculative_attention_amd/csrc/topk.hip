@@ -5,17 +5,33 @@
 // order-preserving unsigned key (NaN -> key of -inf, -0.0 -> +0.0).  Thread t
 // owns the contiguous index range [t * IPT, (t + 1) * IPT) and keeps its keys
 // in registers for the whole kernel.  A most-significant-digit-first radix
-// select (four 8-bit passes; one LDS histogram per wave, summed) finds the
-// exact k-th largest key T and how many keys equal to T must be taken.  Two
-// block-wide prefix sums in thread order then give (1) which T-valued items
-// are taken (the lowest indices) and (2) each kept item's output slot, so the
-// output is ascending and bit-exact for a given score array.
+// select (four 8-bit passes over LDS histograms) finds the exact k-th largest
+// key T and how many keys equal to T must be taken.  One block-wide prefix sum
+// in thread order then gives each kept item's output slot (all keys > T, then
+// the lowest-index keys == T), so the output is ascending and bit-exact for a
+// given score array.
+//
+// Costs that shaped it (measured on the chip, 16384 chunks per row):
+//  * the score loads are issued unconditionally (index clamped into the row)
+//    and all at once, before the chunk count arrives: one memory round trip
+//    instead of one per key;
+//  * real score rows crowd a few top-byte bins and same-address LDS atomics
+//    within one instruction serialise, so each histogram is kept in kSub
+//    copies indexed by lane % kSub, 257 words apart (8 copies beat 4, 16, 32);
+//  * histograms are double-buffered (the next pass's copy is cleared while
+//    this one fills), so a pass needs two barriers;
+//  * both output counts share one prefix sum.
+// A direct rank of the keys left in the k-th key's bin (in place of the last
+// passes) measured slower than the passes it replaced and is not used.
 #include "tf_internal.h"
 
 namespace tfk {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kSub = 8;            // histogram copies, one per lane % kSub
+constexpr int kHistStride = 257;   // words between copies (different LDS banks for one bin)
+constexpr int kHistWords = kSub * kHistStride;
 
 // Keys of real scores are >= 0x007FFFFF (the key of -inf), so 0 marks
 // "no item".
@@ -26,122 +42,157 @@ __device__ __forceinline__ unsigned order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the 1024 threads in thread order.
-__device__ __forceinline__ int block_excl_scan(int x, int* s_warp) {
+// Exclusive prefix sum over the 1024 threads in thread order (modulo 2^32).
+__device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* s_warp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = x;
+  unsigned incl = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
+    const unsigned y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
   if (lane == 63) s_warp[w] = incl;
   __syncthreads();
   if (w == 0) {
-    const int t = lane < kTopkWaves ? s_warp[lane] : 0;
-    int ti = t;
+    const unsigned t = lane < kTopkWaves ? s_warp[lane] : 0u;
+    unsigned ti = t;
 #pragma unroll
     for (int off = 1; off < kTopkWaves; off <<= 1) {
-      const int y = __shfl_up(ti, off);
+      const unsigned y = __shfl_up(ti, off);
       if (lane >= off) ti += y;
     }
     if (lane < kTopkWaves) s_warp[kTopkWaves + lane] = ti - t;  // exclusive wave offsets
   }
   __syncthreads();
-  const int r = s_warp[kTopkWaves + w] + incl - x;
+  const unsigned r = s_warp[kTopkWaves + w] + incl - x;
   __syncthreads();
   return r;
+}
+
+// Chooses, in descending digit order, the bin of histogram h (kSub copies)
+// that holds the krem-th largest key; run by the 64 threads of wave 0.
+__device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int krem, unsigned* s_prefix, int* s_krem) {
+  const int lane = threadIdx.x;
+  // lane l owns bins 255-4l .. 252-4l
+  int c[4];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bin = 255 - 4 * lane - j;
+    int t = 0;
+#pragma unroll
+    for (int x = 0; x < kSub; ++x) t += h[x * kHistStride + bin];
+    c[j] = t;
+    sum += t;
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  int above = incl - sum;  // keys in higher digits than this lane's bins
+  if (above < krem && krem <= incl) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (above < krem && krem <= above + c[j]) {
+        *s_prefix = (prefix << 8) | (unsigned)(255 - 4 * lane - j);
+        *s_krem = krem - above;
+      }
+      above += c[j];
+    }
+  }
 }
 
 template <int IPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int32_t rows,
                                                              int32_t c_max, const int32_t* __restrict__ n_chunks,
                                                              int32_t k, int32_t* __restrict__ idx) {
-  __shared__ int s_hist[kTopkWaves][256];
-  __shared__ int s_warp[2 * kTopkWaves];
+  __shared__ int s_hist[2][kHistWords];
+  __shared__ unsigned s_warp[2 * kTopkWaves];
   __shared__ unsigned s_prefix;
   __shared__ int s_krem;
   const int row = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const float* src = scores + ((size_t)b * rows + row) * c_max;
   int32_t* dst = idx + ((size_t)b * rows + row) * k;
+  const int i0 = tid * IPT;
+
+  // Scores first: every load is in bounds (index clamped into the row) and
+  // none waits for another or for the chunk count.
+  // (32-bit byte offsets from the row base: one address register per load)
+  const char* srcb = (const char*)src;
+  float v[IPT];
+  if (IPT >= 4 && (c_max & 3) == 0) {
+    const int last4 = c_max / 4 - 1;
+#pragma unroll
+    for (int q = 0; q < IPT / 4; ++q) {
+      const float4 x = *(const float4*)(srcb + (unsigned)min(i0 / 4 + q, last4) * 16u);
+      v[4 * q + 0] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else if (IPT <= 32) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, c_max - 1) * 4u);
+  } else {
+    // (64 keys per thread: one address register per load would not fit beside
+    // the values; load in groups of 16)
+#pragma unroll
+    for (int g = 0; g < IPT; g += 16) {
+#pragma unroll
+      for (int j = g; j < g + 16; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, c_max - 1) * 4u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;
   const int C = min(max(n_chunks[b], 0), c_max);
 
   if (C <= k) {
     for (int j = tid; j < k; j += kTopkThreads) dst[j] = j < C ? j : -1;
     return;
   }
-
-  const int i0 = tid * IPT;
   unsigned key[IPT];
 #pragma unroll
-  for (int j = 0; j < IPT; ++j) key[j] = (i0 + j < C) ? order_key(src[i0 + j]) : 0u;
+  for (int j = 0; j < IPT; ++j) key[j] = (i0 + j < C) ? order_key(v[j]) : 0u;
+  __syncthreads();
 
   unsigned prefix = 0;
   int krem = k;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < 4; ++pass) {  // (left to the compiler to unroll: 0.7 us faster than a rolled loop)
     const int shift = 24 - 8 * pass;
-    for (int j = tid; j < kTopkWaves * 256; j += kTopkThreads) (&s_hist[0][0])[j] = 0;
-    __syncthreads();
+    int* h = s_hist[pass & 1];
+    int* hn = s_hist[(pass & 1) ^ 1];
+    for (int j = tid; j < kHistWords; j += kTopkThreads) hn[j] = 0;  // next pass's histogram
+    const int sub = (lane & (kSub - 1)) * kHistStride;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const unsigned kk = key[j];
       const bool match = kk != 0u && (pass == 0 || (kk >> (shift + 8)) == prefix);
-      if (match) atomicAdd(&s_hist[w][(kk >> shift) & 255u], 1);
+      if (match) atomicAdd(&h[sub + ((kk >> shift) & 255u)], 1);
     }
     __syncthreads();
-    if (tid < 256) {  // fold the per-wave histograms
-      int t = 0;
-#pragma unroll
-      for (int x = 0; x < kTopkWaves; ++x) t += s_hist[x][tid];
-      s_hist[0][tid] = t;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending digit order)
-      int c[4];
-      int sum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = s_hist[0][255 - 4 * tid - j];
-        sum += c[j];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (tid >= off) incl += y;
-      }
-      int above = incl - sum;  // keys in higher digits than this lane's bins
-      if (above < krem && krem <= incl) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (above < krem && krem <= above + c[j]) {
-            s_prefix = (prefix << 8) | (unsigned)(255 - 4 * tid - j);
-            s_krem = krem - above;
-          }
-          above += c[j];
-        }
-      }
-    }
+    if (tid < 64) pick_bin(h, prefix, krem, &s_prefix, &s_krem);
     __syncthreads();
     prefix = s_prefix;
     krem = s_krem;
   }
   const unsigned T = prefix;
 
-  int n_gt = 0, n_eq = 0;
+  // Output slots: keys > T and the krem lowest-index keys == T, in index
+  // order.  Both counts share one prefix sum (gt in the low 16 bits: fewer
+  // than k <= 65535 keys exceed T, so it never carries into the high half).
+  unsigned n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     n_gt += key[j] > T;
     n_eq += key[j] == T;
   }
-  const int eq_before = block_excl_scan(n_eq, s_warp);
-  const int take_eq = min(max(krem - eq_before, 0), n_eq);
-  const int mine = n_gt + take_eq;
-  const int pos0 = block_excl_scan(mine, s_warp);
-  int pos = pos0, eq_left = take_eq;
+  const unsigned pre = block_excl_scan((n_eq << 16) | n_gt, s_warp);
+  const int eq_before = (int)(pre >> 16), gt_before = (int)(pre & 0xFFFFu);
+  int eq_left = min(max(krem - eq_before, 0), (int)n_eq);
+  int pos = gt_before + min(eq_before, krem);
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     bool keep = key[j] > T;
@@ -160,7 +211,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel_long(const float* __
                                                                   int32_t c_max, const int32_t* __restrict__ n_chunks,
                                                                   int32_t k, int32_t* __restrict__ idx) {
   __shared__ int s_hist[kTopkWaves][256];
-  __shared__ int s_warp[2 * kTopkWaves];
+  __shared__ unsigned s_warp[2 * kTopkWaves];
   __shared__ unsigned s_prefix;
   __shared__ int s_krem;
   const int row = blockIdx.x, b = blockIdx.y;
@@ -225,10 +276,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel_long(const float* __
     n_gt += kk > T;
     n_eq += kk == T;
   }
-  const int eq_before = block_excl_scan(n_eq, s_warp);
+  const int eq_before = (int)block_excl_scan((unsigned)n_eq, s_warp);
   const int take_eq = min(max(krem - eq_before, 0), n_eq);
   const int mine = n_gt + take_eq;
-  int pos = block_excl_scan(mine, s_warp);
+  int pos = (int)block_excl_scan((unsigned)mine, s_warp);
   int eq_left = take_eq;
   for (int i = i0; i < i1; ++i) {
     const unsigned kk = order_key(src[i]);

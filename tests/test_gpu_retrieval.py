@@ -160,3 +160,26 @@ def test_topk_large_rows(C, k):
     for b, n in enumerate([C, C - 11]):
         for g in range(3):
             assert np.array_equal(idx[b, g], oracle.select_topk(s[b, g, :n].astype(np.float64), k))
+
+
+@pytest.mark.parametrize("C", [5003, 16384, 40000, 50001])
+def test_topk_value_spreads(C):
+    """Rows whose k-th key sits in bins of every size: exponents spread so the
+    first 8-bit digit already isolates a small bin, quantised values whose
+    16-bit bins hold exact duplicates, a narrow band that needs all four
+    digits, and 64 keys per thread (C > 32768) with row lengths that are and
+    are not a multiple of 4."""
+    rng = np.random.default_rng(C + 1)
+    rows = [
+        np.sign(rng.standard_normal(C)) * np.exp2(rng.uniform(-60, 60, C)),     # spread exponents
+        np.round(rng.standard_normal(C) * 4 * 1024) / 1024,                     # duplicates in small bins
+        1.0 + rng.integers(0, 1 << 12, C) * 2.0 ** -23,                          # one narrow band
+        (rng.standard_normal(C) * 4).astype(np.float32),                         # score-like
+    ]
+    s = np.stack(rows)[None].astype(np.float32)
+    for k in [1, 512, 1023, 2049]:
+        for n in [C, C - 3]:
+            idx = run_topk(s, [n], k)
+            for g in range(s.shape[1]):
+                ref = oracle.select_topk(s[0, g, :n].astype(np.float64), k)
+                assert np.array_equal(idx[0, g], ref), (k, n, g)
