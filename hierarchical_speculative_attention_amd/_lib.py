@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfattn.s
 TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_WORKSPACE, TF_ERR_HIP = 0, 1, 2, 3, 4
 TF_DTYPE_FP16, TF_DTYPE_BF16, TF_DTYPE_FP32 = 1, 2, 3
 TF_ACCEPT_PROBS = 1
+TF_APPEND_FULL, TF_APPEND_RING = 0, 1
+TF_APPEND_OK, TF_APPEND_NO_ROOM, TF_APPEND_RING_TOO_SMALL, TF_APPEND_BAD_LENGTH = 0, 1, 2, 3
 
 EXPORTS = [
     "tf_status_string", "tf_last_error_detail",
@@ -26,6 +28,7 @@ EXPORTS = [
     "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_sparse_verify_attn",
     "tf_sparse_verify_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
+    "tf_append_kv", "tf_commit_length",
 ]
 
 
@@ -76,6 +79,8 @@ def lib() -> ctypes.CDLL:
         "tf_verify_attn_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "tf_accept": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]),
         "tf_accept_workspace_size": (sz, [i32, i32, i32]),
+        "tf_append_kv": (ctypes.c_int, [vp, vp, i32, vp, vp, dp, i32, i32, i32, i32, vp, vp]),
+        "tf_commit_length": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -313,3 +318,40 @@ def accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
                            TF_ACCEPT_PROBS if probs else 0, _ptr(n_accepted), _ptr(next_token), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream(stream, target.device)), "tf_accept")
     return n_accepted, next_token
+
+
+def append_kv(K_new: torch.Tensor, V_new: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc,
+              ring: bool = False, n_sink: int = 0, window: int = 0, reserve: Optional[int] = None,
+              status: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """Copy the R new rows per (sequence, head), K_new / V_new [B][H][R][d],
+    into the cache at the current lengths (full cache, or streaming ring).
+    Returns the per-sequence status array (device int32 [B])."""
+    _need(K_new, "K_new", kv.dtype)
+    _need(V_new, "V_new", kv.dtype)
+    _need(K, "K", kv.dtype)
+    _need(V, "V", kv.dtype)
+    R = int(K_new.shape[-2]) if K_new.dim() >= 2 else 0
+    if tuple(K_new.shape) != (kv.B, kv.H, R, kv.d) or tuple(V_new.shape) != tuple(K_new.shape):
+        raise ValueError(f"K_new / V_new must be [{kv.B}][{kv.H}][R][{kv.d}]")
+    if status is None:
+        status = torch.empty(kv.B, dtype=torch.int32, device=K.device)
+    _need(status, "status", torch.int32)
+    kd = kv.c()
+    _check(lib().tf_append_kv(_ptr(K_new), _ptr(V_new), R, _ptr(K), _ptr(V), ctypes.byref(kd),
+                              TF_APPEND_RING if ring else TF_APPEND_FULL, int(n_sink), int(window),
+                              int(R if reserve is None else reserve), _ptr(status), _stream(stream, K.device)),
+           "tf_append_kv")
+    return status
+
+
+def commit_length(seq_len: torch.Tensor, add: int, gamma: int = 0, n_accepted: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """seq_len[b] += add, minus the gamma - n_accepted[b] rejected drafts
+    (device int32 [B], in place)."""
+    _need(seq_len, "seq_len", torch.int32)
+    if n_accepted is not None:
+        _need(n_accepted, "n_accepted", torch.int32)
+    _check(lib().tf_commit_length(_ptr(seq_len), int(seq_len.numel()), int(add), int(gamma), _ptr(n_accepted),
+                                  _stream(stream, seq_len.device)), "tf_commit_length")
+    return seq_len
+

@@ -371,3 +371,35 @@ TF_EXPORT int tf_accept(const float* target, const float* draft, const int32_t* 
                                       n_accepted, next_token, ws, (hipStream_t)stream),
                    "tf_accept");
 }
+
+// ---------------------------------------------------------------------------
+// Cache maintenance
+// ---------------------------------------------------------------------------
+TF_EXPORT int tf_append_kv(const void* K_new, const void* V_new, int32_t R, void* K, void* V, const tf_kv_desc* kv,
+                           int32_t mode, int32_t n_sink, int32_t window, int32_t reserve, int32_t* status,
+                           tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (R < 0 || R > (1 << 20)) return fail(TF_ERR_INVALID_ARG, "R=%d out of range", R);
+  if (mode != TF_APPEND_FULL && mode != TF_APPEND_RING) return fail(TF_ERR_INVALID_ARG, "mode %d unknown", mode);
+  if (mode == TF_APPEND_RING && (n_sink < 0 || window < 0 || reserve < R))
+    return fail(TF_ERR_INVALID_ARG, "ring: n_sink=%d window=%d reserve=%d (need >= 0, >= 0, >= R=%d)", n_sink,
+                window, reserve, R);
+  if (kv->B == 0 || R == 0) return ok();
+  TRY(check_ptr(K_new, "K_new", 16));
+  TRY(check_ptr(V_new, "V_new", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  if (status) TRY(check_ptr(status, "status", 4));
+  return check_hip(tfk::launch_append((const uint16_t*)K_new, (const uint16_t*)V_new, R, (uint16_t*)K, (uint16_t*)V,
+                                      *kv, mode, n_sink, window, reserve, status, (hipStream_t)stream),
+                   "tf_append_kv");
+}
+
+TF_EXPORT int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
+                               tf_stream_t stream) {
+  if (B < 0 || add < 0 || gamma < 0) return fail(TF_ERR_INVALID_ARG, "B=%d add=%d gamma=%d must be >= 0", B, add, gamma);
+  if (B == 0) return ok();
+  TRY(check_ptr(seq_len, "seq_len", 4));
+  if (n_accepted) TRY(check_ptr(n_accepted, "n_accepted", 4));
+  return check_hip(tfk::launch_commit(seq_len, B, add, gamma, n_accepted, (hipStream_t)stream), "tf_commit_length");
+}

@@ -78,4 +78,11 @@ hipError_t launch_accept(const float* target, const float* draft, const int32_t*
                          float temperature, int32_t flags, int32_t* n_acc, int32_t* next,
                          void* ws, hipStream_t stream);
 
+// cache maintenance
+hipError_t launch_append(const uint16_t* Knew, const uint16_t* Vnew, int32_t R, uint16_t* K, uint16_t* V,
+                         const tf_kv_desc& kv, int32_t mode, int32_t n_sink, int32_t window, int32_t reserve,
+                         int32_t* status, hipStream_t stream);
+hipError_t launch_commit(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
+                         hipStream_t stream);
+
 }  // namespace tfk

@@ -226,6 +226,51 @@ int tf_accept(const float* target, const float* draft, const int32_t* draft_toke
               void* ws, size_t ws_bytes, tf_stream_t stream);
 size_t tf_accept_workspace_size(int32_t B, int32_t gamma, int32_t V);
 
+/*
+ * Cache maintenance around the step.  Drafted rows enter the caches before
+ * they are verified and the rejected ones leave again ([blog] Force 3 reads
+ * the complete cache; Force 1 keeps the sinks plus a rolling window of the
+ * most recent tokens; "2. Dual Rejection Sampling" discards every draft after
+ * the first rejection).  Lengths stay on the device, so a decode loop of
+ * append / attention / accept / commit needs no host round trip.
+ *
+ * tf_append_kv: copies R new rows per (sequence, head) into K and V.
+ *   K_new, V_new: device [kv->B][kv->H][R][d] in kv->dtype (fp16 / bf16).
+ *   K, V        : device caches described by kv; kv->seq_len[b] = n_b is the
+ *                 current length (read, not changed: see tf_commit_length).
+ *   mode TF_APPEND_FULL: the rows become positions n_b .. n_b + R - 1 in rows
+ *     n_b .. n_b + R - 1; a sequence with n_b + R > seq_cap[b] gets
+ *     TF_APPEND_NO_ROOM and is left as it is.
+ *   mode TF_APPEND_RING (the streaming cache of tf_stream_attn; n_b is the
+ *     logical length): position p goes to slot p if p < n_sink, else to slot
+ *     n_sink + (p - n_sink) mod (seq_cap[b] - n_sink).  `reserve` (>= R)
+ *     bounds the rows appended since the last length that can no longer be
+ *     rolled back; a ring with seq_cap[b] - n_sink < window + reserve gets
+ *     TF_APPEND_RING_TOO_SMALL and is left as it is (with fewer slots, a
+ *     rollback could expose a visible position whose slot a newer row took).
+ *   n_b < 0 gives TF_APPEND_BAD_LENGTH.  status: device int32 [B] (per
+ *   sequence, one of tf_append_status) or NULL.  R = 0 enqueues nothing.
+ *   kv->max_len is not used.
+ *
+ * tf_commit_length: seq_len[b] = max(0, seq_len[b] + add - drop_b), with
+ *   drop_b = gamma - clamp(n_accepted[b], 0, gamma) when n_accepted (device
+ *   int32 [B], e.g. the output of tf_accept) is given, else 0.  seq_len is a
+ *   device int32 [B] array (a descriptor's seq_len), updated in place.
+ *   add >= 0, gamma >= 0.
+ */
+typedef enum { TF_APPEND_FULL = 0, TF_APPEND_RING = 1 } tf_append_mode;
+typedef enum {
+  TF_APPEND_OK = 0,
+  TF_APPEND_NO_ROOM = 1,
+  TF_APPEND_RING_TOO_SMALL = 2,
+  TF_APPEND_BAD_LENGTH = 3
+} tf_append_status;
+int tf_append_kv(const void* K_new, const void* V_new, int32_t R, void* K, void* V, const tf_kv_desc* kv,
+                 int32_t mode, int32_t n_sink, int32_t window, int32_t reserve, int32_t* status,
+                 tf_stream_t stream);
+int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
+                     tf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

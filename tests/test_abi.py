@@ -120,3 +120,21 @@ def test_workspace_sizes_are_deterministic_and_grow_with_length():
     assert L.tf_verify_attn_workspace_size(0, 32, 32, 7, 131072) == 0
     assert L.tf_accept_workspace_size(4, 6, 32000) >= 4 * 13 * 8 * 16
     assert L.tf_accept_workspace_size(0, 6, 32000) == 0
+
+
+def test_cache_maintenance_validates():
+    L = T.lib()
+    kv = desc()
+    assert L.tf_append_kv(FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(kv), 0, 0, 0, 0, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_append_kv(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(kv), 5, 0, 0, 3, None, None) == T.TF_ERR_INVALID_ARG
+    # ring: reserve below R, negative sinks or window
+    assert L.tf_append_kv(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(kv), T.TF_APPEND_RING, 4, 252, 2, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_append_kv(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(kv), T.TF_APPEND_RING, -1, 252, 3, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_append_kv(None, FAKE, 3, FAKE, FAKE, ctypes.byref(kv), T.TF_APPEND_FULL, 0, 0, 3, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_append_kv(FAKE, FAKE, 3, ctypes.c_void_p(0x10008), FAKE, ctypes.byref(kv), 0, 0, 0, 3, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_append_kv(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(desc(dtype=T.TF_DTYPE_FP32)), 0, 0, 0, 3, None, None) == T.TF_ERR_UNSUPPORTED
+    assert L.tf_append_kv(FAKE, FAKE, 0, FAKE, FAKE, ctypes.byref(kv), 0, 0, 0, 0, None, None) == T.TF_OK  # nothing to do
+    assert L.tf_commit_length(FAKE, 4, -1, 0, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_commit_length(FAKE, 4, 0, -2, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_commit_length(None, 4, 1, 0, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_commit_length(None, 0, 1, 0, None, None) == T.TF_OK
