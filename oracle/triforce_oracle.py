@@ -365,6 +365,55 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
 
 
 # ---------------------------------------------------------------------------
+# Two-level (dual) rejection sampling across the three tiers
+# ---------------------------------------------------------------------------
+
+def two_level_accept(p_rows: np.ndarray, q_rows: np.ndarray, r_rows: np.ndarray, w: Sequence[float],
+                     u1: Sequence[float], v1: Sequence[float], u2: Sequence[float], gamma1: int, gamma2: int,
+                     temperature: float, probs: bool = False) -> Tuple[List[int], int, int, int]:
+    """One step of the hierarchy's sampling, r -> q -> p.
+
+    [blog] "2. Dual Rejection Sampling": a candidate x proposed by the
+    streaming drafter (distribution r) is kept by the sparse-cache target
+    (distribution q) when min(1, q(x)/r(x)) >= u1; the candidates that Force 2
+    passes on are then tested against the full-cache target p with
+    min(1, p(x)/q(x)) >= u2, and a rejection there draws from
+    max(0, p - q) / sum max(0, p - q).  "1. The Three Forces of TriForce":
+    Force 1 drafts, Force 2 evaluates the drafts, Force 3 verifies what Force
+    2 passes on in one pass.
+
+    Readings where the page is silent: rows are indexed by absolute position
+    t (row t is the distribution of token t given the tokens before it);
+    Force 2 runs rounds of `gamma1` drafts until `gamma2` candidates are
+    collected (each round emits its kept drafts plus the token it draws,
+    exactly one level of `accept`), the surplus of the last round is dropped,
+    and the level-2 draft distribution of a collected token is q at its
+    position (the distribution level 1 makes it follow).  The drafter samples
+    position t by inverse CDF of r_t with w[t]; a round starting at t0 tests
+    its drafts with u1[t0 ..] and draws with v1[t0]; level 2 uses u2.  No
+    uniform is ever consulted twice.
+
+    p_rows: [gamma2 + 1][V]; q_rows: [gamma2 + gamma1][V];
+    r_rows: [gamma2 + gamma1 - 1][V]; w, u1: gamma2 + gamma1 - 1 values;
+    v1: gamma2 values; u2: gamma2 + 1 values.
+    Returns (candidates, n_accepted, next_token, rounds): the step emits
+    candidates[:n_accepted] followed by next_token."""
+    cand: List[int] = []
+    rounds = 0
+    while len(cand) < gamma2:
+        t0 = len(cand)
+        drafts = [inverse_cdf(distribution(r_rows[t0 + j], temperature, probs), float(w[t0 + j]))
+                  for j in range(gamma1)]
+        uni = [float(x) for x in u1[t0:t0 + gamma1]] + [float(v1[t0])]
+        n1, y, _ = accept(q_rows[t0:t0 + gamma1 + 1], r_rows[t0:t0 + gamma1], drafts, uni, temperature, probs)
+        cand += drafts[:n1] + [y]
+        rounds += 1
+    cand = cand[:gamma2]
+    n2, nxt, _ = accept(p_rows[:gamma2 + 1], q_rows[:gamma2], cand, u2, temperature, probs)
+    return cand, n2, nxt, rounds
+
+
+# ---------------------------------------------------------------------------
 # Cache maintenance around the path: drafted rows enter the caches before
 # they are verified, rejected ones leave them.
 # ---------------------------------------------------------------------------

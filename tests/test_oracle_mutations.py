@@ -106,6 +106,36 @@ def ring_slot_one_short(p, n_sink, cap):
     return p if p < n_sink else n_sink + (p - n_sink) % (cap - n_sink - 1)   # mistake: ring one slot short
 
 
+def _two_level_variant(level1_swap=False, level2_rows="q", shift=0):
+    def two_level(p_rows, q_rows, r_rows, w, u1, v1, u2, gamma1, gamma2, temperature, probs=False):
+        cand, rounds = [], 0
+        while len(cand) < gamma2:
+            t0 = len(cand)
+            drafts = [T.inverse_cdf(T.distribution(r_rows[t0 + j], temperature, probs), float(w[t0 + j]))
+                      for j in range(gamma1)]
+            uni = [float(x) for x in u1[t0:t0 + gamma1]] + [float(v1[t0])]
+            tgt, drf = (r_rows[t0:t0 + gamma1 + 1], q_rows[t0:t0 + gamma1]) if level1_swap else \
+                (q_rows[t0:t0 + gamma1 + 1], r_rows[t0:t0 + gamma1])
+            if level1_swap and tgt.shape[0] < gamma1 + 1:
+                tgt = np.concatenate([tgt, q_rows[t0 + gamma1:t0 + gamma1 + 1]])
+            n1, y, _ = T.accept(tgt, drf, drafts, uni, temperature, probs)
+            cand += drafts[:n1] + [y]
+            rounds += 1
+        cand = cand[:gamma2]
+        rows = r_rows if level2_rows == "r" else q_rows
+        n2, nxt, _ = T.accept(p_rows[:gamma2 + 1], rows[shift:shift + gamma2], cand, u2, temperature, probs)
+        return cand, n2, nxt, rounds
+    return two_level
+
+
+two_level_level1_swapped = _two_level_variant(level1_swap=True)      # mistake: Force 2 tests r against q
+two_level_level1_swapped.__name__ = "two_level_level1_swapped"
+two_level_draft_rows_r = _two_level_variant(level2_rows="r")          # mistake: level 2 divides by r
+two_level_draft_rows_r.__name__ = "two_level_draft_rows_r"
+two_level_rows_shifted = _two_level_variant(shift=1)                  # mistake: q rows one position late
+two_level_rows_shifted.__name__ = "two_level_rows_shifted"
+
+
 CASES = [
     ("verify_attn", verify_off_by_one, pins.test_verify_rows_are_prefix_attention),
     ("verify_attn", verify_off_by_one, pins.test_verify_alignment_closed_form),
@@ -119,6 +149,11 @@ CASES = [
     ("commit_length", commit_drops_one_more, pins.test_commit_length_closed_forms),
     ("commit_length", commit_drops_one_more, pins.test_full_cache_decode_loop_matches_list_model),
     ("ring_slot_of", ring_slot_one_short, pins.test_ring_slot_hand_table),
+    ("two_level_accept", two_level_level1_swapped, pins.test_two_level_hand_examples),
+    ("two_level_accept", two_level_level1_swapped, pins.test_two_level_is_lossless_statistically),
+    ("two_level_accept", two_level_draft_rows_r, pins.test_two_level_is_lossless_statistically),
+    ("two_level_accept", two_level_rows_shifted, pins.test_two_level_hand_examples),
+    ("two_level_accept", two_level_rows_shifted, pins.test_two_level_is_lossless_statistically),
 ]
 
 

@@ -379,6 +379,75 @@ def test_accept_with_temperature_is_lossless_statistically():
     assert ok, (stat, crit)
 
 
+# ---------------------------------------------------------------------------
+# two-level accept r -> q -> p (dual rejection sampling)
+# ---------------------------------------------------------------------------
+
+def test_two_level_hand_examples():
+    with open(os.path.join(GOLDEN, "two_level_hand_examples.json")) as f:
+        g = json.load(f)
+    P, Qr, R = (np.array(g[k], np.float64) for k in ("p_rows", "q_rows", "r_rows"))
+    for case in g["cases"]:
+        cand, n2, nxt, rounds = oracle.two_level_accept(P, Qr, R, case["w"], case["u1"], case["v1"], case["u2"],
+                                                        g["gamma1"], g["gamma2"], 1.0, probs=True)
+        assert (cand, n2, nxt, rounds) == (case["candidates"], case["n_accepted"], case["next_token"],
+                                           case["rounds"]), case["name"]
+
+
+def _two_level_inputs(rng, V, g1, g2):
+    T = g2 + g1
+    return (rng.random(T - 1), rng.random(T - 1), rng.random(g2), rng.random(g2 + 1))
+
+
+def test_two_level_special_cases():
+    rng = np.random.default_rng(61)
+    V, g1, g2 = 7, 3, 5
+    for _ in range(50):
+        P = rng.dirichlet(np.ones(V), g2 + 1)
+        Qr = rng.dirichlet(np.ones(V), g2 + g1)
+        w, u1, v1, u2 = _two_level_inputs(rng, V, g1, g2)
+        # r = q: every level-1 round keeps all gamma1 drafts, so the chain is
+        # drafts and bonus tokens in rounds of gamma1 + 1
+        cand, n2, nxt, rounds = oracle.two_level_accept(P, Qr, Qr[:-1], w, u1, v1, u2, g1, g2, 1.0, probs=True)
+        assert rounds == -(-g2 // (g1 + 1))
+        for t in range(g2):
+            if t % (g1 + 1) < g1:     # a draft position: the drafter's own sample, kept
+                assert cand[t] == oracle.inverse_cdf(Qr[t], w[t])
+        # q = p on the candidate positions: level 2 keeps every candidate
+        cand, n2, nxt, rounds = oracle.two_level_accept(Qr[:g2 + 1], Qr, rng.dirichlet(np.ones(V), g2 + g1 - 1),
+                                                        w, u1, v1, u2, g1, g2, 1.0, probs=True)
+        assert n2 == g2 and len(cand) == g2
+        assert nxt == oracle.inverse_cdf(Qr[g2], u2[g2])
+
+
+def test_two_level_is_lossless_statistically():
+    """The first candidate Force 2 passes on is distributed as q_0, and the
+    first token the step emits as p_0; given the first candidate is kept by
+    Force 3, the second emitted token is distributed as p_1 (blog, '2. Dual
+    Rejection Sampling': the intermediate approximations cancel)."""
+    rng = np.random.default_rng(67)
+    V, g1, g2, trials = 6, 2, 3, 25000
+    P = rng.dirichlet(np.ones(V) * 0.8, g2 + 1)
+    Qr = rng.dirichlet(np.ones(V) * 0.8, g2 + g1)
+    R = rng.dirichlet(np.ones(V) * 0.8, g2 + g1 - 1)
+    Qr[0, 2] = 0.0
+    Qr[0] /= Qr[0].sum()       # a token Force 2 never passes on at position 0
+    cand0 = np.zeros(V, np.int64)
+    first = np.zeros(V, np.int64)
+    second = np.zeros(V, np.int64)
+    for _ in range(trials):
+        w, u1, v1, u2 = _two_level_inputs(rng, V, g1, g2)
+        cand, n2, nxt, _ = oracle.two_level_accept(P, Qr, R, w, u1, v1, u2, g1, g2, 1.0, probs=True)
+        emitted = cand[:n2] + [nxt]
+        cand0[cand[0]] += 1
+        first[emitted[0]] += 1
+        if n2 >= 1:
+            second[emitted[1]] += 1
+    for counts, ref in ((cand0, Qr[0]), (first, P[0]), (second, P[1])):
+        ok, stat, crit = chi2_ok(counts, ref)
+        assert ok, (stat, crit)
+
+
 def test_inverse_cdf_never_draws_zero_weight():
     r = np.array([0.0, 0.3, 0.0, 0.0, 0.7, 0.0])
     for u in np.linspace(1e-9, 1 - 1e-9, 2001):
