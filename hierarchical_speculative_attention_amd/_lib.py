@@ -28,7 +28,7 @@ EXPORTS = [
     "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_sparse_verify_attn",
     "tf_sparse_verify_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
-    "tf_append_kv", "tf_commit_length",
+    "tf_append_kv", "tf_commit_length", "tf_collect_candidates",
 ]
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "tf_accept_workspace_size": (sz, [i32, i32, i32]),
         "tf_append_kv": (ctypes.c_int, [vp, vp, i32, vp, vp, dp, i32, i32, i32, i32, vp, vp]),
         "tf_commit_length": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
+        "tf_collect_candidates": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -354,4 +355,26 @@ def commit_length(seq_len: torch.Tensor, add: int, gamma: int = 0, n_accepted: O
     _check(lib().tf_commit_length(_ptr(seq_len), int(seq_len.numel()), int(add), int(gamma), _ptr(n_accepted),
                                   _stream(stream, seq_len.device)), "tf_commit_length")
     return seq_len
+
+
+def collect_candidates(draft_tokens: torch.Tensor, n_accepted: torch.Tensor, next_token: torch.Tensor,
+                       q_rows: torch.Tensor, count_in: torch.Tensor, count_out: torch.Tensor,
+                       cand: torch.Tensor, cand_q: torch.Tensor, stream=None) -> None:
+    """Append one Force 2 round's emitted tokens and their q rows to the
+    level-2 candidate chain (cand [B][gamma2], cand_q [B][gamma2][V]);
+    count_out[b] = count_in[b] + the tokens taken."""
+    B, g1p1, V = q_rows.shape
+    gamma2 = cand.shape[1]
+    for t, name, dt in ((n_accepted, "n_accepted", torch.int32), (next_token, "next_token", torch.int32),
+                        (q_rows, "q_rows", torch.float32), (count_in, "count_in", torch.int32),
+                        (count_out, "count_out", torch.int32), (cand, "cand", torch.int32),
+                        (cand_q, "cand_q", torch.float32)):
+        _need(t, name, dt)
+    if g1p1 > 1:
+        _need(draft_tokens, "draft_tokens", torch.int32)
+    if tuple(cand_q.shape) != (B, gamma2, V):
+        raise ValueError("cand_q must be [B][gamma2][V]")
+    _check(lib().tf_collect_candidates(_ptr(draft_tokens) if g1p1 > 1 else None, _ptr(n_accepted), _ptr(next_token),
+                                       _ptr(q_rows), B, g1p1 - 1, V, _ptr(count_in), _ptr(count_out), _ptr(cand),
+                                       _ptr(cand_q), gamma2, _stream(stream, q_rows.device)), "tf_collect_candidates")
 

@@ -403,3 +403,28 @@ TF_EXPORT int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t
   if (n_accepted) TRY(check_ptr(n_accepted, "n_accepted", 4));
   return check_hip(tfk::launch_commit(seq_len, B, add, gamma, n_accepted, (hipStream_t)stream), "tf_commit_length");
 }
+
+// ---------------------------------------------------------------------------
+// Two-level accept: candidate collection between the levels
+// ---------------------------------------------------------------------------
+TF_EXPORT int tf_collect_candidates(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,
+                                    const float* q_rows, int32_t B, int32_t gamma1, int32_t V,
+                                    const int32_t* count_in, int32_t* count_out, int32_t* cand, float* cand_q,
+                                    int32_t gamma2, tf_stream_t stream) {
+  if (B < 0 || gamma1 < 0 || gamma1 > 1024 || V < 1 || gamma2 < 1 || gamma2 > 1024)
+    return fail(TF_ERR_INVALID_ARG, "B=%d gamma1=%d V=%d gamma2=%d out of range", B, gamma1, V, gamma2);
+  if (B == 0) return ok();
+  if (gamma1 > 0) TRY(check_ptr(draft_tokens, "draft_tokens", 4));
+  TRY(check_ptr(n_accepted, "n_accepted", 4));
+  TRY(check_ptr(next_token, "next_token", 4));
+  TRY(check_ptr(q_rows, "q_rows", 16));
+  TRY(check_ptr(count_in, "count_in", 4));
+  TRY(check_ptr(count_out, "count_out", 4));
+  TRY(check_ptr(cand, "cand", 4));
+  TRY(check_ptr(cand_q, "cand_q", 16));
+  if ((const void*)count_in == (const void*)count_out)
+    return fail(TF_ERR_INVALID_ARG, "count_in and count_out must be different arrays");
+  return check_hip(tfk::launch_collect(draft_tokens, n_accepted, next_token, q_rows, B, gamma1, V, count_in,
+                                       count_out, cand, cand_q, gamma2, (hipStream_t)stream),
+                   "tf_collect_candidates");
+}

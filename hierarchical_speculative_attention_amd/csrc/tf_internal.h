@@ -85,4 +85,9 @@ hipError_t launch_append(const uint16_t* Knew, const uint16_t* Vnew, int32_t R, 
 hipError_t launch_commit(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
                          hipStream_t stream);
 
+// two-level accept: candidate collection
+hipError_t launch_collect(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,
+                          const float* q_rows, int32_t B, int32_t gamma1, int32_t V, const int32_t* count_in,
+                          int32_t* count_out, int32_t* cand, float* cand_q, int32_t gamma2, hipStream_t stream);
+
 }  // namespace tfk

@@ -271,6 +271,33 @@ int tf_append_kv(const void* K_new, const void* V_new, int32_t R, void* K, void*
 int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
                      tf_stream_t stream);
 
+/*
+ * Two-level accept, r -> q -> p ([blog] "2. Dual Rejection Sampling": Force 2
+ * keeps a drafter candidate x when min(1, q(x)/r(x)) >= u1; what Force 2
+ * passes on is verified by Force 3 with min(1, p(x)/q(x)) >= u2, a rejection
+ * there drawing from max(0, p - q)).  Both levels are tf_accept calls (the
+ * drafter's own sampling is tf_accept with gamma = 0); between them, after
+ * each Force 2 round of gamma1 drafts (target q_rows, draft r rows),
+ * tf_collect_candidates appends the round's emitted tokens -- draft_tokens[b]
+ * [0 .. n_accepted[b]) then next_token[b] -- to sequence b's chain, as long as
+ * fewer than gamma2 are there, together with the q row of each token's
+ * position (q_rows[b][j] for the round's j-th emitted token).  Force 3 then
+ * calls tf_accept(target = p rows [B][gamma2 + 1][V], draft = cand_q,
+ * draft_tokens = cand).
+ *   draft_tokens: device int32 [B][gamma1]; n_accepted, next_token: device
+ *     int32 [B] (clamped: n_accepted into [0, gamma1]).
+ *   q_rows: device fp32 [B][gamma1 + 1][V] (logits or probabilities: copied).
+ *   count_in: device int32 [B], candidates already collected (clamped into
+ *     [0, gamma2]); count_out: device int32 [B], a DIFFERENT array, receives
+ *     count_in[b] + the tokens taken (alternate the two arrays between rounds).
+ *   cand: device int32 [B][gamma2]; cand_q: device fp32 [B][gamma2][V]; slots
+ *     at and past count_out[b] are not written.
+ *   1 <= gamma2 <= 1024, 0 <= gamma1 <= 1024, V >= 1.  No workspace.
+ */
+int tf_collect_candidates(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,
+                          const float* q_rows, int32_t B, int32_t gamma1, int32_t V, const int32_t* count_in,
+                          int32_t* count_out, int32_t* cand, float* cand_q, int32_t gamma2, tf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

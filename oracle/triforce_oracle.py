@@ -370,7 +370,7 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
 
 def two_level_accept(p_rows: np.ndarray, q_rows: np.ndarray, r_rows: np.ndarray, w: Sequence[float],
                      u1: Sequence[float], v1: Sequence[float], u2: Sequence[float], gamma1: int, gamma2: int,
-                     temperature: float, probs: bool = False) -> Tuple[List[int], int, int, int]:
+                     temperature: float, probs: bool = False, with_margin: bool = False):
     """One step of the hierarchy's sampling, r -> q -> p.
 
     [blog] "2. Dual Rejection Sampling": a candidate x proposed by the
@@ -397,19 +397,32 @@ def two_level_accept(p_rows: np.ndarray, q_rows: np.ndarray, r_rows: np.ndarray,
     r_rows: [gamma2 + gamma1 - 1][V]; w, u1: gamma2 + gamma1 - 1 values;
     v1: gamma2 values; u2: gamma2 + 1 values.
     Returns (candidates, n_accepted, next_token, rounds): the step emits
-    candidates[:n_accepted] followed by next_token."""
+    candidates[:n_accepted] followed by next_token.  With with_margin, a
+    fifth value is the smallest distance of any decision taken to its
+    threshold (tests use it to skip rounding-level ties)."""
     cand: List[int] = []
     rounds = 0
+    margin = math.inf
     while len(cand) < gamma2:
         t0 = len(cand)
-        drafts = [inverse_cdf(distribution(r_rows[t0 + j], temperature, probs), float(w[t0 + j]))
-                  for j in range(gamma1)]
+        drafts = []
+        for j in range(gamma1):
+            rr = distribution(r_rows[t0 + j], temperature, probs)
+            x = inverse_cdf(rr, float(w[t0 + j]))
+            cs = np.cumsum(rr)
+            tgt = float(w[t0 + j]) * float(rr.sum())
+            margin = min(margin, abs(cs[x] - tgt), abs(tgt - (cs[x - 1] if x > 0 else 0.0)))
+            drafts.append(x)
         uni = [float(x) for x in u1[t0:t0 + gamma1]] + [float(v1[t0])]
-        n1, y, _ = accept(q_rows[t0:t0 + gamma1 + 1], r_rows[t0:t0 + gamma1], drafts, uni, temperature, probs)
+        n1, y, m = accept(q_rows[t0:t0 + gamma1 + 1], r_rows[t0:t0 + gamma1], drafts, uni, temperature, probs)
+        margin = min(margin, m)
         cand += drafts[:n1] + [y]
         rounds += 1
     cand = cand[:gamma2]
-    n2, nxt, _ = accept(p_rows[:gamma2 + 1], q_rows[:gamma2], cand, u2, temperature, probs)
+    n2, nxt, m = accept(p_rows[:gamma2 + 1], q_rows[:gamma2], cand, u2, temperature, probs)
+    margin = min(margin, m)
+    if with_margin:
+        return cand, n2, nxt, rounds, margin
     return cand, n2, nxt, rounds
 
 

@@ -138,3 +138,17 @@ def test_cache_maintenance_validates():
     assert L.tf_commit_length(FAKE, 4, 0, -2, None, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_commit_length(None, 4, 1, 0, None, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_commit_length(None, 0, 1, 0, None, None) == T.TF_OK
+
+
+def test_collect_candidates_validates():
+    L = T.lib()
+    other = ctypes.c_void_p(0x20000)
+    ok_args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("draft", FAKE), ("na", FAKE), ("nx", FAKE), ("q", FAKE), ("B", 2), ("g1", 3), ("V", 100),
+        ("cin", FAKE), ("cout", other), ("cand", FAKE), ("cq", FAKE), ("g2", 5), ("s", None))]
+    assert L.tf_collect_candidates(*ok_args(cout=FAKE)) == T.TF_ERR_INVALID_ARG    # in place: refused
+    assert L.tf_collect_candidates(*ok_args(g2=0)) == T.TF_ERR_INVALID_ARG
+    assert L.tf_collect_candidates(*ok_args(V=0)) == T.TF_ERR_INVALID_ARG
+    assert L.tf_collect_candidates(*ok_args(q=ctypes.c_void_p(0x10004))) == T.TF_ERR_INVALID_ARG
+    assert L.tf_collect_candidates(*ok_args(draft=None)) == T.TF_ERR_INVALID_ARG
+    assert L.tf_collect_candidates(*ok_args(B=0, draft=None, q=None)) == T.TF_OK
