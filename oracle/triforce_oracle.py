@@ -272,6 +272,42 @@ def verify_attn(qs: np.ndarray, K: np.ndarray, V: np.ndarray, n: int) -> Tuple[n
     return o, lse
 
 
+def tree_masks(parent: Sequence[int]) -> List[int]:
+    """Visibility masks of a candidate tree of Q nodes given by parent
+    pointers: bit m of mask i is set when node m is node i or one of its
+    ancestors.  [blog] Force 3 evaluates the candidate tree from Force 2 in
+    one pass with tree attention; a node is conditioned on exactly its path
+    from the committed prefix.  Reading: parent[i] = -1 hangs node i off the
+    prefix; a parent outside [0, i) is read as -1 (nodes come in topological
+    order, so a valid parent always precedes its child)."""
+    Q = len(parent)
+    out = []
+    for i in range(Q):
+        m, x = 0, i
+        while x >= 0:
+            m |= 1 << x
+            p = int(parent[x])
+            x = p if 0 <= p < x else -1
+        out.append(m)
+    return out
+
+
+def verify_tree_attn(qs: np.ndarray, K: np.ndarray, V: np.ndarray, n: int,
+                     masks: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Force 3 over a candidate tree.  The last Q cache rows hold the tree's
+    nodes in order (node m at row n - Q + m); query row i sees every row
+    before them and node m when bit m of masks[i] is set.  With chain masks
+    (node i sees nodes 0..i) this is verify_attn.  qs: [Q][d]."""
+    Q, d = qs.shape
+    base = n - Q
+    o = np.zeros((Q, d), np.float64)
+    lse = np.zeros(Q, np.float64)
+    for i in range(Q):
+        vis = [t for t in range(max(0, n)) if t < base or (int(masks[i]) >> (t - base)) & 1]
+        o[i], lse[i] = attention(qs[i], K[vis], V[vis])
+    return o, lse
+
+
 # ---------------------------------------------------------------------------
 # a7  Lossless accept / reject
 # ---------------------------------------------------------------------------

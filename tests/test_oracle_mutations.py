@@ -136,6 +136,28 @@ two_level_rows_shifted = _two_level_variant(shift=1)                  # mistake:
 two_level_rows_shifted.__name__ = "two_level_rows_shifted"
 
 
+def tree_masks_no_self(parent):
+    out = []
+    for i in range(len(parent)):
+        m, x = 0, int(parent[i]) if 0 <= int(parent[i]) < i else -1   # mistake: the node itself is left out
+        while x >= 0:
+            m |= 1 << x
+            p = int(parent[x])
+            x = p if 0 <= p < x else -1
+        out.append(m)
+    return out
+
+
+def verify_tree_base_off_by_one(qs, K, V, n, masks):
+    Q, d = qs.shape
+    base = n - Q + 1                          # mistake: nodes start one row late
+    o, lse = np.zeros((Q, d)), np.zeros(Q)
+    for i in range(Q):
+        vis = [t for t in range(max(0, n)) if t < base or (int(masks[i]) >> (t - base)) & 1]
+        o[i], lse[i] = T.attention(qs[i], K[vis], V[vis])
+    return o, lse
+
+
 CASES = [
     ("verify_attn", verify_off_by_one, pins.test_verify_rows_are_prefix_attention),
     ("verify_attn", verify_off_by_one, pins.test_verify_alignment_closed_form),
@@ -149,6 +171,8 @@ CASES = [
     ("commit_length", commit_drops_one_more, pins.test_commit_length_closed_forms),
     ("commit_length", commit_drops_one_more, pins.test_full_cache_decode_loop_matches_list_model),
     ("ring_slot_of", ring_slot_one_short, pins.test_ring_slot_hand_table),
+    ("tree_masks", tree_masks_no_self, pins.test_tree_masks_hand_table),
+    ("verify_tree_attn", verify_tree_base_off_by_one, pins.test_verify_tree_chain_is_verify_and_rows_match_masked_sdpa),
     ("two_level_accept", two_level_level1_swapped, pins.test_two_level_hand_examples),
     ("two_level_accept", two_level_level1_swapped, pins.test_two_level_is_lossless_statistically),
     ("two_level_accept", two_level_draft_rows_r, pins.test_two_level_is_lossless_statistically),

@@ -193,6 +193,51 @@ def test_verify_rows_are_prefix_attention():
     np.testing.assert_allclose(o1[0], sdpa(qs[0], K, V), rtol=1e-12, atol=1e-13)
 
 
+def test_tree_masks_hand_table():
+    # node 0 off the prefix; 1 and 2 children of 0; 3 child of 1; 4 a second root
+    assert oracle.tree_masks([-1, 0, 0, 1, -1]) == [0b1, 0b11, 0b101, 0b1011, 0b10000]
+    # a chain: node i sees nodes 0..i
+    assert oracle.tree_masks([-1, 0, 1, 2]) == [0b1, 0b11, 0b111, 0b1111]
+    # parents outside [0, i) hang the node off the prefix
+    assert oracle.tree_masks([5, 0, 2, -9, 3]) == [0b1, 0b11, 0b100, 0b1000, 0b11000]
+
+
+def test_verify_tree_chain_is_verify_and_rows_match_masked_sdpa():
+    rng = np.random.default_rng(29)
+    n, Q = 150, 7
+    qs, K, V = rng.standard_normal((Q, 128)), rng.standard_normal((n, 128)), rng.standard_normal((n, 128))
+    chain = oracle.tree_masks([-1] + list(range(Q - 1)))
+    o_t, l_t = oracle.verify_tree_attn(qs, K, V, n, chain)
+    o_v, l_v = oracle.verify_attn(qs, K, V, n)
+    assert np.array_equal(o_t, o_v) and np.array_equal(l_t, l_v)
+    parent = [-1, 0, 0, 1, 2, -1, 5]
+    masks = oracle.tree_masks(parent)
+    o, lse = oracle.verify_tree_attn(qs, K, V, n, masks)
+    for i in range(Q):
+        vis = np.ones(n, bool)
+        vis[n - Q:] = False
+        x = i
+        while x >= 0:                      # the node and its ancestors, walked independently
+            vis[n - Q + x] = True
+            x = parent[x]
+        np.testing.assert_allclose(o[i], sdpa(qs[i], K, V, vis), rtol=1e-12, atol=1e-13)
+        assert abs(lse[i] - scipy.special.logsumexp((K @ qs[i] / math.sqrt(128))[vis])) < 1e-12
+    # a star (every node off the prefix) sees the prefix and itself only
+    star = oracle.tree_masks([-1] * Q)
+    o, _ = oracle.verify_tree_attn(qs, K, V, n, star)
+    for i in range(Q):
+        rows = list(range(n - Q)) + [n - Q + i]
+        np.testing.assert_allclose(o[i], sdpa(qs[i], K[rows], V[rows]), rtol=1e-12, atol=1e-13)
+    # fewer cache rows than nodes: missing nodes are simply absent
+    o, lse = oracle.verify_tree_attn(qs, K, V, 3, masks)
+    for i in range(Q):
+        vis = [t for t in range(3) if (masks[i] >> (t + Q - 3)) & 1]
+        if vis:
+            np.testing.assert_allclose(o[i], sdpa(qs[i], K[vis], V[vis]), rtol=1e-12, atol=1e-13)
+        else:
+            assert np.all(o[i] == 0) and lse[i] == -math.inf
+
+
 def test_verify_alignment_closed_form():
     # K = 0: row i averages V over its visible prefix [0, n - Q + i].
     n, Q = 5, 3
