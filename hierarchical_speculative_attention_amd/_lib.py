@@ -28,7 +28,7 @@ EXPORTS = [
     "tf_sparse_attn", "tf_sparse_attn_workspace_size", "tf_sparse_verify_attn",
     "tf_sparse_verify_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
-    "tf_append_kv", "tf_commit_length", "tf_collect_candidates",
+    "tf_append_kv", "tf_commit_length", "tf_collect_candidates", "tf_verify_tree_attn", "tf_tree_masks",
 ]
 
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "tf_append_kv": (ctypes.c_int, [vp, vp, i32, vp, vp, dp, i32, i32, i32, i32, vp, vp]),
         "tf_commit_length": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "tf_collect_candidates": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, vp]),
+        "tf_verify_tree_attn": (ctypes.c_int, [vp, i32, i32, vp, vp, dp, vp, vp, vp, vp, sz, vp]),
+        "tf_tree_masks": (ctypes.c_int, [vp, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -377,4 +379,40 @@ def collect_candidates(draft_tokens: torch.Tensor, n_accepted: torch.Tensor, nex
     _check(lib().tf_collect_candidates(_ptr(draft_tokens) if g1p1 > 1 else None, _ptr(n_accepted), _ptr(next_token),
                                        _ptr(q_rows), B, g1p1 - 1, V, _ptr(count_in), _ptr(count_out), _ptr(cand),
                                        _ptr(cand_q), gamma2, _stream(stream, q_rows.device)), "tf_collect_candidates")
+
+
+def tree_masks(parent: torch.Tensor, stream=None) -> torch.Tensor:
+    """Visibility masks (device int64 holding uint64 bits, [B][Q]) of the
+    candidate trees given by parent pointers (device int32 [B][Q])."""
+    _need(parent, "parent", torch.int32)
+    B, Q = parent.shape
+    masks = torch.empty((B, Q), dtype=torch.int64, device=parent.device)
+    _check(lib().tf_tree_masks(_ptr(parent), B, Q, _ptr(masks), _stream(stream, parent.device)), "tf_tree_masks")
+    return masks
+
+
+def verify_tree_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc, tree_mask: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None):
+    """Force 3 over a candidate tree: q [B][Hq][Q][d]; tree_mask [B][Q] (int64
+    holding the uint64 masks)."""
+    _need(q, "q", kv.dtype)
+    _need(K, "K", kv.dtype)
+    _need(V, "V", kv.dtype)
+    _need(tree_mask, "tree_mask", torch.int64)
+    B, Hq, Q = q.shape[0], q.shape[1], q.shape[2]
+    if tuple(tree_mask.shape) != (B, Q):
+        raise ValueError("tree_mask must be [B][Q]")
+    if out is None:
+        out = torch.empty((B, Hq, Q, kv.d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Q), dtype=torch.float32, device=q.device)
+    need = verify_attn_workspace_size(kv.B, Hq, kv.H, Q, kv.max_len)
+    if ws is None:
+        ws = workspace(need, q.device)
+    kd = kv.c()
+    _check(lib().tf_verify_tree_attn(_ptr(q), Hq, Q, _ptr(K), _ptr(V), ctypes.byref(kd), _ptr(tree_mask), _ptr(out),
+                                     _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, q.device)),
+           "tf_verify_tree_attn")
+    return out, lse
 

@@ -99,6 +99,7 @@ void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, 
   a.lse = lse;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.tmask = nullptr;
   a.scale_ln = 1.0f / std::sqrt((float)tfk::kHeadDim);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)tfk::kHeadDim));
 }
@@ -336,6 +337,40 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
   fill_plan(a, plan, ws);
   return check_hip(tfk::launch_attn(kv->dtype, tfk::kVerify, a, (hipStream_t)stream), "tf_verify_attn");
+}
+
+TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                                  const tf_kv_desc* kv, const uint64_t* tree_mask, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (Hq < 1 || Hq % kv->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, kv->H);
+  if (Q < 1 || Q > 64) return fail(TF_ERR_INVALID_ARG, "Q=%d must be in [1, 64]", Q);
+  if ((long)(Hq / kv->H) * Q > tfk::kMaxRows)
+    return fail(TF_ERR_UNSUPPORTED, "G*Q = %ld query rows per KV head (at most %d)", (long)(Hq / kv->H) * Q,
+                tfk::kMaxRows);
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  TRY(check_ptr(tree_mask, "tree_mask", 8));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  const tfk::SplitPlan plan =
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
+  TRY(check_ws(ws, ws_bytes, plan.total_bytes));
+  tfk::AttnArgs a;
+  fill_common(a, q, K, V, kv, Hq, Q, out, lse);
+  fill_plan(a, plan, ws);
+  a.tmask = tree_mask;
+  return check_hip(tfk::launch_attn(kv->dtype, tfk::kVerifyTree, a, (hipStream_t)stream), "tf_verify_tree_attn");
+}
+
+TF_EXPORT int tf_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* tree_mask, tf_stream_t stream) {
+  if (B < 0 || Q < 1 || Q > 64) return fail(TF_ERR_INVALID_ARG, "B=%d Q=%d (need B >= 0, 1 <= Q <= 64)", B, Q);
+  if (B == 0) return ok();
+  TRY(check_ptr(parent, "parent", 4));
+  TRY(check_ptr(tree_mask, "tree_mask", 8));
+  return check_hip(tfk::launch_tree_masks(parent, B, Q, tree_mask, (hipStream_t)stream), "tf_tree_masks");
 }
 
 // ---------------------------------------------------------------------------

@@ -1,7 +1,7 @@
 // Split-K decode attention on MFMA for gfx950: the one kernel behind
-// full-cache verification (Force 3), attention over retrieved chunks
-// (Force 2) and sink + window streaming attention (Force 1) of the TriForce
-// blog, section "1. The Three Forces of TriForce".
+// full-cache verification of a candidate chain or tree (Force 3), attention
+// over retrieved chunks (Force 2) and sink + window streaming attention
+// (Force 1) of the TriForce blog, section "1. The Three Forces of TriForce".
 //
 // Work decomposition.  Grid = (splits, KV heads, sequences).  A workgroup of
 // four waves owns `tpw` consecutive "virtual" tokens of one (sequence, KV
@@ -119,7 +119,7 @@ __device__ __forceinline__ Geo make_geo(const AttnArgs& a, const SeqDesc& d) {
   } else {
     n = min(max(n, 0), min(g.cap, a.max_len));
     g.n = n;
-    g.L = (MODE == kVerify) ? n : a.k * a.cs;
+    g.L = (MODE == kVerify || MODE == kVerifyTree) ? n : a.k * a.cs;
     g.nchunks = (n + a.cs - 1) / a.cs;
     if (MODE == kSparseTail) {
       g.lo = max(0, n - a.tail);       // first tail row
@@ -134,7 +134,7 @@ template <int MODE>
 __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, int v_end,
                                        const int* s_idx, int chunk_lo) {
   if (v >= v_end) return -1;
-  if (MODE == kVerify) return v;
+  if (MODE == kVerify || MODE == kVerifyTree) return v;
   if (MODE == kSparse || MODE == kSparseTail) {
     const int kcs = a.k * a.cs;
     if (MODE == kSparseTail && v >= kcs) return g.lo + (v - kcs);  // tail row (< n since v < L)
@@ -264,7 +264,8 @@ template <int DT, int MODE, int NQT, class Src>
 __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int t0,
                                              const typename MT<DT>::V8 (&qreg)[NQT][4],
                                              const typename MT<DT>::V8 (&sel)[2], const int (&lim)[NQT],
-                                             int lim_min, f32x4 (&acc)[NQT][8], float (&m_run)[NQT],
+                                             int lim_min, const uint64_t (&tm)[NQT], int tbase,
+                                             f32x4 (&acc)[NQT][8], float (&m_run)[NQT],
                                              float (&l_run)[NQT], float c2, int lq, int lg) {
   using M = MT<DT>;
   using V8 = typename M::V8;
@@ -273,7 +274,10 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   const unsigned mk0 = mask & 0xFFFFu, mk1 = mask >> 16;
   // Whole tile visible to every row: no per-element masking needed.
   constexpr bool kCausal = MODE == kVerify || MODE == kSparseTail;
-  const bool full = mask == 0xFFFFFFFFu && (!kCausal || t0 + 31 <= lim_min);
+  // Tree: rows below tbase (the prefix) are visible to every query row; node
+  // m = row - tbase is visible when bit m of the row's mask is set.
+  constexpr bool kTree = MODE == kVerifyTree;
+  const bool full = mask == 0xFFFFFFFFu && (!kCausal || t0 + 31 <= lim_min) && (!kTree || t0 + 31 < tbase);
   V8 ph[NQT], pl[NQT];
   V8 k0[4], k1[4];
 #pragma unroll
@@ -293,8 +297,13 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * lg + r;
-        const bool vis0 = ((mk0 >> j) & 1u) && (!kCausal || t0 + j <= lim[qt]);
-        const bool vis1 = ((mk1 >> j) & 1u) && (!kCausal || t0 + 16 + j <= lim[qt]);
+        bool vis0 = ((mk0 >> j) & 1u) && (!kCausal || t0 + j <= lim[qt]);
+        bool vis1 = ((mk1 >> j) & 1u) && (!kCausal || t0 + 16 + j <= lim[qt]);
+        if (kTree) {
+          const unsigned n0 = (unsigned)(t0 + j - tbase), n1 = (unsigned)(t0 + 16 + j - tbase);
+          vis0 = vis0 && (t0 + j < tbase || (n0 < 64u && ((tm[qt] >> n0) & 1ull)));
+          vis1 = vis1 && (t0 + 16 + j < tbase || (n1 < 64u && ((tm[qt] >> n1) & 1ull)));
+        }
         s0[r] = vis0 ? s0[r] : kNegInf;
         s1[r] = vis1 ? s1[r] : kNegInf;
       }
@@ -362,7 +371,7 @@ void attn_kernel(const AttnArgs a) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
-  constexpr bool kStaged = MODE == kVerify;
+  constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
   __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
   __shared__ float s_m[4][16];
@@ -409,8 +418,16 @@ void attn_kernel(const AttnArgs a) {
     }
   }
 
+  uint64_t tm[NQT];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int row = qt * 16 + lq;
+    tm[qt] = (MODE == kVerifyTree && row < a.rows) ? a.tmask[(size_t)b * a.Qn + row % a.Qn] : 0ull;
+  }
+
   const SeqDesc sd = load_seq(a, b);
   const Geo geo = make_geo<MODE>(a, sd);
+  const int tbase = geo.n - a.Qn;  // tree: cache row of node 0
   const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
   if (split >= nsp) return;
   const int v1 = min(geo.L, v0 + a.tpw);
@@ -476,7 +493,7 @@ void attn_kernel(const AttnArgs a) {
     load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     while (true) {
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2, lq, lg);
+      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
       t += 4 * kTile;
       if (t >= v1) break;
       mask = st.mask;
@@ -489,14 +506,14 @@ void attn_kernel(const AttnArgs a) {
     while (true) {
       load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(RegSource<DT>{A}, A.mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2,
-                                  lq, lg);
+      process_tile<DT, MODE, NQT>(RegSource<DT>{A}, A.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run,
+                                  l_run, c2, lq, lg);
       t += 4 * kTile;
       if (t >= v1) break;
       load_tile<DT, MODE>(A, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(RegSource<DT>{B}, B.mask, t, qreg, sel, lim, lim_min, acc, m_run, l_run, c2,
-                                  lq, lg);
+      process_tile<DT, MODE, NQT>(RegSource<DT>{B}, B.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run,
+                                  l_run, c2, lq, lg);
       t += 4 * kTile;
       if (t >= v1) break;
     }
@@ -681,6 +698,7 @@ static hipError_t launch_mode(int mode, const AttnArgs& a, hipStream_t stream) {
     case kSparse: return launch_nqt<DT, kSparse>(a, stream);
     case kStream: return launch_nqt<DT, kStream>(a, stream);
     case kSparseTail: return launch_nqt<DT, kSparseTail>(a, stream);
+    case kVerifyTree: return launch_nqt<DT, kVerifyTree>(a, stream);
   }
   return hipErrorInvalidValue;
 }

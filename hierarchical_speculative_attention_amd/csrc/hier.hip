@@ -1,7 +1,7 @@
-// Candidate collection between the two levels of the hierarchy's rejection
-// sampling (TriForce blog, "2. Dual Rejection Sampling": Force 2 keeps the
-// drafter's candidates with min(1, q/r) >= u1, and what it passes on is then
-// verified by Force 3 with min(1, p/q) >= u2).
+// Tree masks for Force 3, and candidate collection between the two levels of
+// the hierarchy's rejection sampling (TriForce blog, "2. Dual Rejection
+// Sampling": Force 2 keeps the drafter's candidates with min(1, q/r) >= u1,
+// and what it passes on is then verified by Force 3 with min(1, p/q) >= u2).
 //
 // After each Force 2 round (one tf_accept of gamma1 drafts against q), the
 // round emits its n_accepted kept drafts and the token it drew.  They are
@@ -40,6 +40,33 @@ __global__ __launch_bounds__(256) void collect_kernel(const int32_t* __restrict_
   } else {
     for (int i = tid; i < V; i += 256) dst[i] = src[i];
   }
+}
+
+// Visibility masks of candidate trees given by parent pointers (Force 3
+// evaluates Force 2's candidate tree with tree attention): one thread per
+// node walks to its root; bit m of the mask is set for the node itself and
+// each ancestor m.  A parent outside [0, i) hangs node i off the prefix, so
+// every walk ends within Q steps.
+__global__ __launch_bounds__(256) void tree_masks_kernel(const int32_t* __restrict__ parent, int32_t B, int32_t Q,
+                                                         uint64_t* __restrict__ masks) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long)B * Q) return;
+  const int b = (int)(gid / Q), i = (int)(gid % Q);
+  const int32_t* par = parent + (size_t)b * Q;
+  uint64_t m = 0;
+  int x = i;
+  while (x >= 0) {
+    m |= 1ull << x;
+    const int p = par[x];
+    x = (p >= 0 && p < x) ? p : -1;
+  }
+  masks[gid] = m;
+}
+
+hipError_t launch_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* masks, hipStream_t stream) {
+  const long n = (long)B * Q;
+  hipLaunchKernelGGL(tree_masks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, parent, B, Q, masks);
+  return hipGetLastError();
 }
 
 hipError_t launch_collect(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,

@@ -15,7 +15,7 @@ constexpr int kThreads = 256;          // 4 waves of 64 lanes
 constexpr int kTile = 32;              // virtual tokens per wave iteration
 constexpr int kMaxRows = 64;           // query rows per KV head (4 MFMA query tiles)
 
-enum AttnMode { kVerify = 0, kSparse = 1, kStream = 2, kSparseTail = 3 };
+enum AttnMode { kVerify = 0, kSparse = 1, kStream = 2, kSparseTail = 3, kVerifyTree = 4 };
 
 struct AttnArgs {
   const uint16_t* q;        // [B][Hq][Qn][d]
@@ -32,6 +32,8 @@ struct AttnArgs {
   int32_t tail;             // sparse with tail: most recent rows attended causally
   // stream
   int32_t n_sink, window;
+  // verification over a candidate tree
+  const uint64_t* tmask;    // [B][Qn]: bit m = the row sees tree node m (cache row n - Qn + m)
   // split-K
   int32_t tpw;              // virtual tokens per workgroup (multiple of 128)
   int32_t nsplit;           // gridDim.x
@@ -85,6 +87,8 @@ hipError_t launch_append(const uint16_t* Knew, const uint16_t* Vnew, int32_t R, 
 hipError_t launch_commit(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, const int32_t* n_accepted,
                          hipStream_t stream);
 
+// tree visibility masks from parent pointers
+hipError_t launch_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* masks, hipStream_t stream);
 // two-level accept: candidate collection
 hipError_t launch_collect(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,
                           const float* q_rows, int32_t B, int32_t gamma1, int32_t V, const int32_t* count_in,

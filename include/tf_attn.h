@@ -200,6 +200,32 @@ int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const vo
 size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len);
 
 /*
+ * a6 over a candidate tree.  [blog] Force 3 evaluates the candidate tree that
+ * Force 2 assembles in one parallel pass with tree attention.  The last Q
+ * cache rows hold the tree's nodes in order: node m is row n_b - Q + m.
+ * Query row i (0 <= i < Q) of head h sees every row below n_b - Q and node m
+ * when bit m of tree_mask[b][i] is set:
+ *   out[b][h][i] = sum over those rows j of softmax_j(q[b][h][i] . K_j / sqrt(d)) V_j
+ * (a row that sees nothing gets out = 0, lse = -inf).  Masks with bits 0..i of
+ * row i (a chain) give exactly tf_verify_attn.
+ *   tree_mask: device uint64 [B][Q] (tf_tree_masks builds it from parents).
+ *   Other arguments as for tf_verify_attn; 1 <= Q <= 64; the workspace is
+ *   tf_verify_attn_workspace_size(kv->B, Hq, kv->H, Q, kv->max_len) bytes.
+ */
+int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                        const tf_kv_desc* kv, const uint64_t* tree_mask, float* out, float* lse,
+                        void* ws, size_t ws_bytes, tf_stream_t stream);
+
+/*
+ * Tree masks from parent pointers: tree_mask[b][i] has bit m set when node m
+ * is node i or one of its ancestors.  parent: device int32 [B][Q]; parent[b]
+ * [i] = -1 hangs node i off the committed prefix, and a value outside [0, i)
+ * is read as -1 (nodes come in topological order).  tree_mask: device uint64
+ * [B][Q].  1 <= Q <= 64.
+ */
+int tf_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* tree_mask, tf_stream_t stream);
+
+/*
  * a7  Lossless accept / reject.  [blog] "2. Dual Rejection Sampling".
  * Per sequence b, with p_i = softmax(target[b][i] / T), q_i =
  * softmax(draft[b][i] / T) in fp64 (T = 0: one-hot at the lowest-index

@@ -152,3 +152,19 @@ def test_collect_candidates_validates():
     assert L.tf_collect_candidates(*ok_args(q=ctypes.c_void_p(0x10004))) == T.TF_ERR_INVALID_ARG
     assert L.tf_collect_candidates(*ok_args(draft=None)) == T.TF_ERR_INVALID_ARG
     assert L.tf_collect_candidates(*ok_args(B=0, draft=None, q=None)) == T.TF_OK
+
+
+def test_tree_entry_points_validate():
+    L = T.lib()
+    kv = desc()
+    call = lambda Q=5, tm=FAKE, Hq=4: L.tf_verify_tree_attn(FAKE, Hq, Q, FAKE, FAKE, ctypes.byref(kv), tm, FAKE, None,
+                                                            FAKE, 1 << 30, None)
+    assert call(Q=0) == T.TF_ERR_INVALID_ARG
+    assert call(Q=65) == T.TF_ERR_INVALID_ARG
+    assert call(Q=17, Hq=16) == T.TF_ERR_UNSUPPORTED          # 4 * 17 rows per KV head
+    assert call(tm=None) == T.TF_ERR_INVALID_ARG
+    assert call(tm=ctypes.c_void_p(0x10004)) == T.TF_ERR_INVALID_ARG
+    assert L.tf_tree_masks(FAKE, 2, 0, FAKE, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_tree_masks(FAKE, 2, 65, FAKE, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_tree_masks(None, 2, 5, FAKE, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_tree_masks(None, 0, 5, None, None) == T.TF_OK
