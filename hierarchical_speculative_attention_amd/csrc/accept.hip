@@ -5,24 +5,33 @@
 // is kept, draw a bonus token from the target's next row.
 //
 // Everything runs in fp64 so that every decision is taken in the same
-// precision as the fp64 reference.  Two kernels:
-//  1. row statistics, spread over (vocabulary slice, row, sequence): the
-//     largest logit of the slice (with its lowest index) and the slice's sum
-//     of exp(x / T - slice max / T);
-//  2. per sequence: merge the slices of the rows it needs, walk the chain,
-//     then draw the next token by inverse CDF.  Each thread sums the weights
-//     of its contiguous vocabulary slice; a block prefix sum in thread order
-//     locates the slice whose running sum first passes u * total, and one
-//     wave re-evaluates that slice (one entry per lane, prefix sum across
-//     lanes) to find the entry.
+// precision as the fp64 reference.  The vocabulary is cut into slices of
+// kSlice entries and the work spread over (slice, row, sequence):
+//  1. accept_stats_kernel, per (slice, row, sequence): the slice's largest
+//     logit (lowest index on ties) and sum of exp(x / T - slice max / T);
+//  2. accept_slice_kernel, per (draw slice of kDraw entries, sequence): every
+//     workgroup takes the chain decision itself (one thread per draft, from
+//     the row statistics), then sums its slice of the draw's weights --
+//     max(0, p_j - q_j) after a rejection at j, p_gamma when all drafts are
+//     kept -- and of p_j (the fallback when the residual vanishes through
+//     rounding);
+//  3. accept_final_kernel, per sequence: the draw slice whose running sum
+//     first passes u * total, then one block prefix sum over that slice's
+//     weights for the entry (inverse CDF, strict '>').
+// The draw is bound by fp64 exponentials (two per vocabulary entry): a first
+// version ran it in one workgroup per sequence (70 us at V = 32000), 4096-entry
+// draw slices 25 us; 1024-entry slices spread it over 32 workgroups.
 #include "tf_internal.h"
 
 namespace tfk {
 
-constexpr int kStatThreads = 256;
-constexpr int kStatSlice = 4096;       // vocabulary entries per statistics workgroup
-constexpr int kDrawThreads = 1024;
-constexpr int kDrawIpt = 64;           // vocabulary entries per draw thread (at most one wave)
+constexpr int kAccThreads = 256;
+constexpr int kSlice = 4096;                   // vocabulary entries per statistics slice
+constexpr int kPer = kSlice / kAccThreads;     // entries per thread within a statistics slice
+constexpr int kMaxSlices = 16;                 // V <= 65536
+constexpr int kDraw = 1024;                    // vocabulary entries per draw slice
+constexpr int kDrawPer = kDraw / kAccThreads;  // fp64 weights per thread within a draw slice
+constexpr int kMaxDraw = 64;                   // draw slices at V = 65536 (one per lane)
 
 struct SliceStat {
   float mx;   // largest logit in the slice
@@ -30,36 +39,69 @@ struct SliceStat {
   double z;   // sum over the slice of exp(x / T - mx / T)
 };
 
+struct SliceSum {  // per draw slice
+  double r;   // sum of the draw's weights over the slice
+  double p;   // sum of p_j over the slice (fallback weights)
+  int last_r; // last index with positive weight (or -1)
+  int last_p;
+};
+
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
+}
+
+// Block-wide reductions over kAccThreads threads (4 waves); fixed order.
+__device__ __forceinline__ double block_sum(double x, double* s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();
+  if (lane == 0) s[w] = x;
+  __syncthreads();
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+__device__ __forceinline__ int block_max(int x, int* s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  __syncthreads();
+  if (lane == 0) s[w] = x;
+  __syncthreads();
+  return max(max(s[0], s[1]), max(s[2], s[3]));
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 1: one workgroup per (slice, row, sequence), flattened into
 // grid.x = slice + nslices * (row + nrows * b).  Rows 0..gamma are target
-// rows, rows gamma+1 .. 2*gamma are draft rows 0..gamma-1.
+// rows, rows gamma+1 .. 2*gamma are draft rows 0..gamma-1.  The slice's
+// kPer loads per thread are issued together (index clamped into the row).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(const float* __restrict__ target,
-                                                                    const float* __restrict__ draft, int32_t gamma,
-                                                                    int32_t V, float temperature, int32_t nslices,
-                                                                    SliceStat* __restrict__ stats) {
-  __shared__ float s_v[kStatThreads / 64];
-  __shared__ int s_i[kStatThreads / 64];
-  __shared__ double s_z[kStatThreads / 64];
+__global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(const float* __restrict__ target,
+                                                                   const float* __restrict__ draft, int32_t gamma,
+                                                                   int32_t V, float temperature, int32_t nslices,
+                                                                   SliceStat* __restrict__ stats) {
+  __shared__ float s_v[kAccThreads / 64];
+  __shared__ int s_i[kAccThreads / 64];
+  __shared__ double s_z[kAccThreads / 64];
   const int nrows = 2 * gamma + 1;
   const int slice = (int)(blockIdx.x % (unsigned)nslices);
   const int r = (int)((blockIdx.x / (unsigned)nslices) % (unsigned)nrows);
   const int b = (int)(blockIdx.x / ((unsigned)nslices * (unsigned)nrows));
   const float* row = (r <= gamma) ? target + ((size_t)b * (gamma + 1) + r) * V
                                   : draft + ((size_t)b * gamma + (r - gamma - 1)) * V;
-  const int v0 = slice * kStatSlice, v1 = min(V, v0 + kStatSlice);
+  const int v0 = slice * kSlice, v1 = min(V, v0 + kSlice);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float x[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) x[k] = row[min(v0 + (int)threadIdx.x + kAccThreads * k, V - 1)];
   float bv = -__builtin_huge_valf();
   int bi = 0x7fffffff;
-  for (int v = v0 + threadIdx.x; v < v1; v += kStatThreads) {
-    const float x = row[v];
-    if (better(x, v, bv, bi)) {
-      bv = x;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int v = v0 + (int)threadIdx.x + kAccThreads * k;
+    if (v < v1 && better(x[k], v, bv, bi)) {
+      bv = x[k];
       bi = v;
     }
   }
@@ -80,23 +122,23 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(const float*
   bv = s_v[0];
   bi = s_i[0];
 #pragma unroll
-  for (int x = 1; x < kStatThreads / 64; ++x)
-    if (better(s_v[x], s_i[x], bv, bi)) {
-      bv = s_v[x];
-      bi = s_i[x];
+  for (int q = 1; q < kAccThreads / 64; ++q)
+    if (better(s_v[q], s_i[q], bv, bi)) {
+      bv = s_v[q];
+      bi = s_i[q];
     }
   double z = 0.0;
   if (temperature > 0.f) {
     const double t = (double)temperature;
     const double zm = (double)bv / t;
-    for (int v = v0 + threadIdx.x; v < v1; v += kStatThreads) z += exp((double)row[v] / t - zm);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (v0 + (int)threadIdx.x + kAccThreads * k < v1) z += exp((double)x[k] / t - zm);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
     if (lane == 0) s_z[w] = z;
     __syncthreads();
-    z = 0.0;
-#pragma unroll
-    for (int x = 0; x < kStatThreads / 64; ++x) z += s_z[x];
+    z = (s_z[0] + s_z[1]) + (s_z[2] + s_z[3]);
   }
   if (threadIdx.x == 0) {
     SliceStat st;
@@ -112,24 +154,39 @@ struct RowDist {
   int mode;     // 0 softmax(x / T), 1 greedy one-hot, 2 probabilities as given
   double zmax;  // max x / T
   double Z;     // sum of exp(x / T - zmax)
+  double invZ;  // 1 / Z (a product per entry instead of a division)
   int amax;
 };
 
+// All of the row's slice statistics are requested at once (one memory round
+// trip), then merged in slice order.
 __device__ RowDist merge_row(const SliceStat* st, int nslices, float temperature, int probs) {
   RowDist d;
   d.zmax = 0.0;
   d.Z = 1.0;
+  d.invZ = 1.0;
   d.amax = 0;
   if (probs) {
     d.mode = 2;
     return d;
   }
-  float bv = st[0].mx;
-  int bi = st[0].amax;
-  for (int s = 1; s < nslices; ++s)
-    if (better(st[s].mx, st[s].amax, bv, bi)) {
-      bv = st[s].mx;
-      bi = st[s].amax;
+  float mx[kMaxSlices];
+  int am[kMaxSlices];
+  double z[kMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s) {
+    const SliceStat x = st[min(s, nslices - 1)];
+    mx[s] = x.mx;
+    am[s] = x.amax;
+    z[s] = x.z;
+  }
+  float bv = mx[0];
+  int bi = am[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSlices; ++s)
+    if (s < nslices && better(mx[s], am[s], bv, bi)) {
+      bv = mx[s];
+      bi = am[s];
     }
   d.amax = bi;
   if (temperature == 0.f) {
@@ -141,129 +198,166 @@ __device__ RowDist merge_row(const SliceStat* st, int nslices, float temperature
   // z_v = x_v / T; division by T > 0 is monotone, so max z = (max x) / T.
   d.zmax = (double)bv / t;
   double Z = 0.0;
-  for (int s = 0; s < nslices; ++s)
-    if (st[s].z > 0.0) Z += st[s].z * exp((double)st[s].mx / t - d.zmax);
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s) {
+    if (s >= nslices) break;  // (no exponentials for absent slices)
+    if (z[s] > 0.0) Z += z[s] * exp((double)mx[s] / t - d.zmax);
+  }
   d.Z = Z;
+  d.invZ = 1.0 / Z;
   return d;
 }
 
-__device__ __forceinline__ double dist_p(const RowDist& d, const float* row, int v, float temperature) {
-  if (d.mode == 2) return (double)row[v];
+__device__ __forceinline__ double dist_of(const RowDist& d, float x, int v, double t) {
+  if (d.mode == 2) return (double)x;
   if (d.mode == 1) return v == d.amax ? 1.0 : 0.0;
-  return exp((double)row[v] / (double)temperature - d.zmax) / d.Z;
+  return exp((double)x / t - d.zmax) * d.invZ;
 }
 
-// Prefix sums over the 1024 threads in thread order (fp64): returns the
-// inclusive sum, stores the exclusive one in *excl and the block total in
-// *s_total.
-__device__ __forceinline__ double block_scan(double x, double* s_scan, double* s_total, double* excl) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+// The chain decision: the first draft i that is not kept (gamma if none).
+// Threads i < gamma test draft i in parallel.
+__device__ int chain_decision(const float* trow0, const float* drow0, const int32_t* tok, const double* u,
+                              const SliceStat* st, int gamma, int V, int nslices, float temperature, int probs,
+                              int* s_j) {
+  if (threadIdx.x == 0) *s_j = gamma;
+  __syncthreads();
+  const double t = (double)temperature;
+  for (int i = threadIdx.x; i < gamma; i += kAccThreads) {
+    const int x = tok[i];
+    bool keep = false;
+    if (x >= 0 && x < V) {  // a token outside [0, V) is never kept
+      const RowDist dp = merge_row(st + (size_t)i * nslices, nslices, temperature, probs);
+      const RowDist dq = merge_row(st + (size_t)(gamma + 1 + i) * nslices, nslices, temperature, probs);
+      const double px = dist_of(dp, trow0[(size_t)i * V + x], x, t);
+      const double qx = dist_of(dq, drow0[(size_t)i * V + x], x, t);
+      if (px > 0.0) {
+        const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
+        keep = alpha >= u[i];
+      }
+    }
+    if (!keep) atomicMin(s_j, i);
   }
-  double ex = __shfl_up(incl, 1);
-  if (lane == 0) ex = 0.0;
-  if (lane == 63) s_scan[w] = incl;
   __syncthreads();
-  double off_w = 0.0;
-  for (int x2 = 0; x2 < w; ++x2) off_w += s_scan[x2];
-  if (threadIdx.x == kDrawThreads - 1) *s_total = off_w + incl;
-  __syncthreads();
-  *excl = off_w + ex;
-  return off_w + incl;
+  return *s_j;
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: grid (B), 1024 threads.
+// Kernel 2: one workgroup per (draw slice, sequence), flattened into
+// grid.x = slice + ndraw * b.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(
+__global__ __launch_bounds__(kAccThreads) void accept_slice_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
     const double* __restrict__ uniforms, int32_t gamma, int32_t V, float temperature, int32_t probs,
-    const SliceStat* __restrict__ stats, int32_t nslices, int32_t* __restrict__ n_acc, int32_t* __restrict__ next) {
-  __shared__ double s_scan[kDrawThreads / 64];
-  __shared__ double s_tot;
+    const SliceStat* __restrict__ stats, int32_t nslices, int32_t ndraw, SliceSum* __restrict__ sums,
+    int32_t* __restrict__ js) {
   __shared__ int s_j;
-  __shared__ int s_found;
-  __shared__ int s_last;
-  const int b = blockIdx.x;
+  __shared__ double s_d[kAccThreads / 64];
+  __shared__ int s_i[kAccThreads / 64];
+  const int slice = (int)(blockIdx.x % (unsigned)ndraw);
+  const int b = (int)(blockIdx.x / (unsigned)ndraw);
   const int nrows = 2 * gamma + 1;
   const SliceStat* st = stats + (size_t)b * nrows * nslices;
   const float* trow0 = target + (size_t)b * (gamma + 1) * V;
   const float* drow0 = draft + (size_t)b * gamma * V;
-  const double* u = uniforms + (size_t)b * (gamma + 1);
-
-  // ---- the chain: one thread, a handful of exp() calls ----------------------
-  if (threadIdx.x == 0) {
-    int j = gamma;
-    for (int i = 0; i < gamma; ++i) {
-      const int x = tokens[(size_t)b * gamma + i];
-      bool keep = false;
-      if (x >= 0 && x < V) {  // a token outside [0, V) is never kept
-        const RowDist dp = merge_row(st + (size_t)i * nslices, nslices, temperature, probs);
-        const RowDist dq = merge_row(st + (size_t)(gamma + 1 + i) * nslices, nslices, temperature, probs);
-        const double px = dist_p(dp, trow0 + (size_t)i * V, x, temperature);
-        const double qx = dist_p(dq, drow0 + (size_t)i * V, x, temperature);
-        if (px > 0.0) {
-          const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
-          keep = alpha >= u[i];
-        }
-      }
-      if (!keep) {
-        j = i;
-        break;
-      }
-    }
-    s_j = j;
-  }
-  __syncthreads();
-  const int j = s_j;
-  bool residual = j < gamma;
+  const int j = chain_decision(trow0, drow0, tokens + (size_t)b * gamma, uniforms + (size_t)b * (gamma + 1), st,
+                               gamma, V, nslices, temperature, probs, &s_j);
+  const bool residual = j < gamma;
   const float* tr = trow0 + (size_t)j * V;
   const float* dr = drow0 + (size_t)(residual ? j : 0) * V;
+  const int v0 = slice * kDraw, v1 = min(V, v0 + kDraw);
+  float xp[kDrawPer], xq[kDrawPer];
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    const int v = min(v0 + (int)threadIdx.x + kAccThreads * k, V - 1);
+    xp[k] = tr[v];
+    xq[k] = residual ? dr[v] : 0.f;
+  }
   const RowDist dp = merge_row(st + (size_t)j * nslices, nslices, temperature, probs);
   const RowDist dq = residual ? merge_row(st + (size_t)(gamma + 1 + j) * nslices, nslices, temperature, probs) : dp;
-
-  // ---- pass 1: each thread sums the weights of its contiguous slice --------
-  const int ipt = (V + kDrawThreads - 1) / kDrawThreads;  // <= 64 (host-checked)
-  const int v0 = threadIdx.x * ipt, v1 = min(V, v0 + ipt);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double local = 0.0;
-  int last_pos = -1;
-  for (int v = v0; v < v1; ++v) {
-    const double p = dist_p(dp, tr, v, temperature);
-    const double r = residual ? fmax(0.0, p - dist_p(dq, dr, v, temperature)) : p;
-    if (r > 0.0) last_pos = v;
-    local += r;
+  const double t = (double)temperature;
+  double sr = 0.0, sp = 0.0;
+  int lr = -1, lp = -1;
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    const int v = v0 + (int)threadIdx.x + kAccThreads * k;
+    if (v >= v1) continue;
+    const double p = dist_of(dp, xp[k], v, t);
+    const double r = residual ? fmax(0.0, p - dist_of(dq, xq[k], v, t)) : p;
+    sr += r;
+    sp += p;
+    if (r > 0.0) lr = v;
+    if (p > 0.0) lp = v;
   }
-  double before;
-  double total = block_scan(local, s_scan, &s_tot, &before);
-  if (residual && s_tot == 0.0) {
-    // max(0, p - q) vanished (only through rounding): draw from p_j instead.
-    residual = false;
-    local = 0.0;
-    last_pos = -1;
-    for (int v = v0; v < v1; ++v) {
-      const double p = dist_p(dp, tr, v, temperature);
-      if (p > 0.0) last_pos = v;
-      local += p;
-    }
-    total = block_scan(local, s_scan, &s_tot, &before);
-  }
-  // `total` is this thread's inclusive running sum; s_tot the row's sum.
-  const double tgt = u[gamma] * s_tot;
+  sr = block_sum(sr, s_d);
+  sp = block_sum(sp, s_d);
+  lr = block_max(lr, s_i);
+  lp = block_max(lp, s_i);
   if (threadIdx.x == 0) {
-    s_found = 0x7fffffff;
-    s_last = -1;
+    SliceSum o;
+    o.r = sr;
+    o.p = sp;
+    o.last_r = lr;
+    o.last_p = lp;
+    sums[(size_t)b * ndraw + slice] = o;
+    if (slice == 0) js[b] = j;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: one workgroup per sequence.  Wave 0 finds the draw slice whose
+// running sum first passes u * total (lane s holds slice s; a prefix sum over
+// the lanes); then thread t of that slice owns its kDrawPer consecutive
+// entries, so a prefix sum in thread order is one in index order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAccThreads) void accept_final_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, const double* __restrict__ uniforms,
+    int32_t gamma, int32_t V, float temperature, int32_t probs, const SliceStat* __restrict__ stats, int32_t nslices,
+    int32_t ndraw, const SliceSum* __restrict__ sums, const int32_t* __restrict__ js, int32_t* __restrict__ n_acc,
+    int32_t* __restrict__ next) {
+  __shared__ int s_slice, s_use_r, s_found, s_last;
+  __shared__ double s_before, s_tgt;
+  __shared__ double s_w[kAccThreads / 64];
+  __shared__ int s_l[kAccThreads / 64];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = js[b];
+  if (w == 0) {
+    const SliceSum o = sums[(size_t)b * ndraw + min(lane, ndraw - 1)];
+    const bool in = lane < ndraw;
+    const double u = uniforms[(size_t)b * (gamma + 1) + gamma];
+    double wr = in ? o.r : 0.0, wp = in ? o.p : 0.0;
+    double ir = wr, ip = wp;  // inclusive prefix sums over the slices
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double yr = __shfl_up(ir, off), yp = __shfl_up(ip, off);
+      if (lane >= off) {
+        ir += yr;
+        ip += yp;
+      }
+    }
+    // the residual's total; if it vanished (rounding), draw from p_j instead
+    const double tot_r = __shfl(ir, 63);
+    const bool use_r = !(j < gamma && tot_r == 0.0);
+    const double total = use_r ? tot_r : __shfl(ip, 63);
+    const double incl = use_r ? ir : ip, ws = use_r ? wr : wp;
+    const double tgt = u * total;
+    const unsigned long long cross = __ballot(in && incl > tgt);
+    int last = in ? (use_r ? o.last_r : o.last_p) : -1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
+    const int found = cross ? (int)__builtin_ctzll(cross) : -1;
+    if (lane == 0) {
+      s_slice = found;
+      s_use_r = use_r;
+      s_tgt = tgt;
+      s_last = last;
+      s_found = 0x7fffffff;
+    }
+    if (found >= 0 && lane == found) s_before = incl - ws;
   }
   __syncthreads();
-  if (total > tgt) atomicMin(&s_found, (int)threadIdx.x);  // first slice whose end passes the target
-  atomicMax(&s_last, last_pos);
-  __syncthreads();
-  const int tstar = s_found;
-  if (tstar == 0x7fffffff) {
+  const int slice = s_slice;
+  if (slice < 0) {
     // the running sum never passes u * total (rounding): the last index with
     // positive weight
     if (threadIdx.x == 0) {
@@ -272,58 +366,104 @@ __global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(
     }
     return;
   }
-  if (threadIdx.x == tstar) s_tot = before;  // running sum before slice tstar
-  __syncthreads();
-  // ---- pass 2: one wave re-evaluates slice tstar, one element per lane ------
-  if (w == 0) {
-    const int v = tstar * ipt + lane;
-    double r = 0.0;
-    if (lane < ipt && v < V) {
-      const double p = dist_p(dp, tr, v, temperature);
-      r = residual ? fmax(0.0, p - dist_p(dq, dr, v, temperature)) : p;
-    }
-    double run = r;
+  const bool residual = j < gamma && s_use_r;
+  const int nrows = 2 * gamma + 1;
+  const SliceStat* st = stats + (size_t)b * nrows * nslices;
+  const float* tr = target + ((size_t)b * (gamma + 1) + j) * V;
+  const float* dr = draft + ((size_t)b * gamma + (residual ? j : 0)) * V;
+  const int e0 = slice * kDraw + (int)threadIdx.x * kDrawPer;
+  float xp[kDrawPer], xq[kDrawPer];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(run, off);
-      if (lane >= off) run += y;
+  for (int k = 0; k < kDrawPer; ++k) {
+    const int v = min(e0 + k, V - 1);
+    xp[k] = tr[v];
+    xq[k] = residual ? dr[v] : 0.f;
+  }
+  const RowDist dp = merge_row(st + (size_t)j * nslices, nslices, temperature, probs);
+  const RowDist dq = residual ? merge_row(st + (size_t)(gamma + 1 + j) * nslices, nslices, temperature, probs) : dp;
+  const double t = (double)temperature;
+  double wv[kDrawPer];
+  double local = 0.0;
+  int last_pos = -1;
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    const int v = e0 + k;
+    double r = 0.0;
+    if (v < V) {
+      const double p = dist_of(dp, xp[k], v, t);
+      r = residual ? fmax(0.0, p - dist_of(dq, xq[k], v, t)) : p;
     }
-    run += s_tot;
-    const unsigned long long hit = __ballot(r > 0.0 && run > tgt);
-    const unsigned long long pos = __ballot(r > 0.0);
-    if (lane == 0) {
-      n_acc[b] = j;
-      // without a crossing inside the slice (rounding), its last positive entry
-      next[b] = hit ? tstar * ipt + (int)__builtin_ctzll(hit)
-                    : (pos ? tstar * ipt + 63 - (int)__builtin_clzll(pos) : s_last);
-    }
+    wv[k] = r;
+    local += r;
+    if (r > 0.0) last_pos = v;
+  }
+  // exclusive prefix of the per-thread sums, in thread order
+  double incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_w[w] = incl;
+  __syncthreads();
+  double off_w = 0.0;
+  for (int q = 0; q < w; ++q) off_w += s_w[q];
+  double run = s_before + off_w + (incl - local);
+  const double tgt = s_tgt;
+  int hit = -1;
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    run += wv[k];
+    if (hit < 0 && wv[k] > 0.0 && run > tgt) hit = e0 + k;
+  }
+  if (hit >= 0) atomicMin(&s_found, hit);
+  const int lastp = block_max(last_pos, s_l);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    n_acc[b] = j;
+    // without a crossing inside the slice (rounding), its last positive entry
+    next[b] = s_found != 0x7fffffff ? s_found : (lastp >= 0 ? lastp : s_last);
   }
 }
 
 size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 0 || V < 1) return 0;
-  const size_t nslices = (size_t)(V + kStatSlice - 1) / kStatSlice;
-  return ((size_t)B * (2 * gamma + 1) * nslices * sizeof(SliceStat) + 255) & ~(size_t)255;
+  const size_t nslices = (size_t)(V + kSlice - 1) / kSlice;
+  const size_t ndraw = (size_t)(V + kDraw - 1) / kDraw;
+  const size_t a = ((size_t)B * (2 * gamma + 1) * nslices * sizeof(SliceStat) + 255) & ~(size_t)255;
+  const size_t b = ((size_t)B * ndraw * sizeof(SliceSum) + 255) & ~(size_t)255;
+  const size_t c = ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
+  return a + b + c;
 }
 
-int32_t accept_max_vocab() { return kDrawThreads * kDrawIpt; }
+int32_t accept_max_vocab() { return kSlice * kMaxSlices; }
 
 hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens,
                          const double* uniforms, int32_t B, int32_t gamma, int32_t V,
                          float temperature, int32_t flags, int32_t* n_acc, int32_t* next,
                          void* ws, hipStream_t stream) {
   const int probs = (flags & TF_ACCEPT_PROBS) != 0;
-  const int nslices = (V + kStatSlice - 1) / kStatSlice;
-  SliceStat* stats = (SliceStat*)ws;
+  const int nslices = (V + kSlice - 1) / kSlice;
+  const int ndraw = (V + kDraw - 1) / kDraw;
+  char* w = (char*)ws;
+  SliceStat* stats = (SliceStat*)w;
+  const size_t a = ((size_t)B * (2 * gamma + 1) * nslices * sizeof(SliceStat) + 255) & ~(size_t)255;
+  SliceSum* sums = (SliceSum*)(w + a);
+  const size_t bsz = ((size_t)B * ndraw * sizeof(SliceSum) + 255) & ~(size_t)255;
+  int32_t* js = (int32_t*)(w + a + bsz);
   if (!probs) {
     const unsigned blocks = (unsigned)nslices * (unsigned)(2 * gamma + 1) * (unsigned)B;
-    hipLaunchKernelGGL(accept_stats_kernel, dim3(blocks), dim3(kStatThreads), 0, stream, target, draft, gamma, V,
+    hipLaunchKernelGGL(accept_stats_kernel, dim3(blocks), dim3(kAccThreads), 0, stream, target, draft, gamma, V,
                        temperature, nslices, stats);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(accept_draw_kernel, dim3(B), dim3(kDrawThreads), 0, stream, target, draft, tokens, uniforms,
-                     gamma, V, temperature, probs, stats, nslices, n_acc, next);
+  hipLaunchKernelGGL(accept_slice_kernel, dim3((unsigned)ndraw * (unsigned)B), dim3(kAccThreads), 0, stream, target,
+                     draft, tokens, uniforms, gamma, V, temperature, probs, stats, nslices, ndraw, sums, js);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_final_kernel, dim3(B), dim3(kAccThreads), 0, stream, target, draft, uniforms, gamma, V,
+                     temperature, probs, stats, nslices, ndraw, sums, js, n_acc, next);
   return hipGetLastError();
 }
 

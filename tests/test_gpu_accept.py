@@ -116,3 +116,22 @@ def test_losslessness_on_gpu():
         rn, rnext, margin = oracle.accept(p32, q32, tokens[b], u[b], 1.0, probs=True)
         if margin > 1e-12:
             assert (n[b], nxt[b]) == (rn, rnext)
+
+
+@pytest.mark.parametrize("V,T", [(1, 1.0), (4097, 1.0), (4097, 0.0), (65536, 0.8), (12345, 1.0)])
+def test_vocabulary_slicing_bit_exact(V, T):
+    """Vocabularies of one entry, a nearly empty last slice, the largest
+    supported size and one between: bit-exact against the oracle."""
+    B, gamma = 12, 4
+    a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=True, seed=24 + V)
+    rng = np.random.default_rng(25)
+    tokens = a.tokens.copy()
+    for b in range(B):
+        for i in range(gamma):
+            q = oracle.distribution(a.draft[b, i], T if T > 0 else 1.0)
+            tokens[b, i] = rng.choice(V, p=q / q.sum())
+    n, nxt = run(a.target, a.draft, tokens, a.uniforms, T)
+    for b in range(B):
+        rn, rnext, margin = oracle.accept(a.target[b], a.draft[b], tokens[b], a.uniforms[b], T)
+        if margin >= 1e-12:
+            assert (n[b], nxt[b]) == (rn, rnext), b
