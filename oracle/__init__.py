@@ -6,7 +6,7 @@ from .triforce_oracle import (  # noqa: F401
     attention, sparse_token_positions, sparse_attn, sparse_verify_positions, sparse_verify_attn,
     stream_positions,
     stream_attn_masked, stream_attn_ring, verify_attn, tree_masks, verify_tree_attn, distribution,
-    inverse_cdf, accept, two_level_accept,
+    inverse_cdf, accept, tree_accept, two_level_accept,
     APPEND_OK, APPEND_NO_ROOM, APPEND_RING_TOO_SMALL, APPEND_BAD_LENGTH,
     append_full, ring_slot_of, append_ring, ring_visible, commit_length,
 )

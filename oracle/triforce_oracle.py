@@ -400,6 +400,63 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
     return j, nxt, margin
 
 
+def tree_accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], parent: Sequence[int],
+                uniforms: Sequence[float], temperature: float, probs: bool = False
+                ) -> Tuple[List[int], int, float]:
+    """Accept / reject over a candidate tree of Q nodes (Force 3 verifying
+    the tree Force 2 assembled, [blog] "1. The Three Forces of TriForce";
+    the acceptance rule and the residual of "2. Dual Rejection Sampling").
+
+    Node 0 is the last committed token; nodes 1 .. Q-1 are candidates with
+    parent[c] in [0, c) (anything else hangs c off node 0).  target[v] is the
+    target's distribution for the children of node v (Q rows); draft[v] the
+    distribution they were drafted from (Q rows; rows of leaves unused).
+    Reading (the pages give the single-candidate rule only): at node v the
+    children are tried in index order; child c with token x is kept when
+    p'(x) > 0 and u_c * q_v(x) <= p'(x), where p' starts as p_v and after
+    each rejected sibling becomes max(0, p' - q_v) renormalised (p_v again if
+    that vanishes through rounding); a kept child becomes v; when no child is
+    kept -- or v has none -- the next token is drawn from p' by inverse CDF.
+    With siblings drafted independently from q_v this keeps the target's
+    distribution; a chain tree is exactly `accept`.  uniforms[c - 1] tests
+    node c, uniforms[Q - 1] draws.  Returns (kept nodes in order, next token,
+    margin)."""
+    Q = len(parent)
+    children = [[] for _ in range(Q)]
+    for c in range(1, Q):
+        pc = int(parent[c])
+        children[pc if 0 <= pc < c else 0].append(c)
+    margin = math.inf
+    path: List[int] = []
+    v = 0
+    while True:
+        p = distribution(target[v], temperature, probs)
+        pr = p
+        kept = -1
+        if children[v]:
+            q = distribution(draft[v], temperature, probs)
+            for c in children[v]:
+                x = int(tokens[c])
+                if 0 <= x < p.shape[0] and pr[x] > 0.0:
+                    lhs = float(uniforms[c - 1]) * float(q[x])
+                    margin = min(margin, abs(lhs - float(pr[x])))
+                    if lhs <= pr[x]:
+                        kept = c
+                        break
+                r = np.maximum(0.0, pr - q)
+                z = float(r.sum())
+                pr = r / z if z > 0.0 else p
+        if kept < 0:
+            nxt = inverse_cdf(pr, float(uniforms[Q - 1]))
+            cs = np.cumsum(pr)
+            tgt = float(uniforms[Q - 1]) * float(pr.sum())
+            lo = cs[nxt - 1] if nxt > 0 else 0.0
+            margin = min(margin, abs(cs[nxt] - tgt), abs(tgt - lo))
+            return path, nxt, margin
+        path.append(kept)
+        v = kept
+
+
 # ---------------------------------------------------------------------------
 # Two-level (dual) rejection sampling across the three tiers
 # ---------------------------------------------------------------------------

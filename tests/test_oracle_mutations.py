@@ -158,6 +158,40 @@ def verify_tree_base_off_by_one(qs, K, V, n, masks):
     return o, lse
 
 
+def _tree_variant(renormalise=True, update=True):
+    def tree_accept(target, draft, tokens, parent, uniforms, temperature, probs=False):
+        Q = len(parent)
+        children = [[] for _ in range(Q)]
+        for c in range(1, Q):
+            pc = int(parent[c])
+            children[pc if 0 <= pc < c else 0].append(c)
+        path, v = [], 0
+        while True:
+            p = T.distribution(target[v], temperature, probs)
+            pr, kept = p, -1
+            if children[v]:
+                q = T.distribution(draft[v], temperature, probs)
+                for c in children[v]:
+                    x = int(tokens[c])
+                    if 0 <= x < p.shape[0] and pr[x] > 0.0 and uniforms[c - 1] * q[x] <= pr[x]:
+                        kept = c
+                        break
+                    if update:
+                        r = np.maximum(0.0, pr - q)
+                        pr = (r / r.sum() if r.sum() > 0 else p) if renormalise else r
+            if kept < 0:
+                return path, T.inverse_cdf(pr, float(uniforms[Q - 1])), 1.0
+            path.append(kept)
+            v = kept
+    return tree_accept
+
+
+tree_accept_unnormalised = _tree_variant(renormalise=False)   # mistake: residual not renormalised
+tree_accept_unnormalised.__name__ = "tree_accept_unnormalised"
+tree_accept_no_update = _tree_variant(update=False)           # mistake: siblings tested against p itself
+tree_accept_no_update.__name__ = "tree_accept_no_update"
+
+
 CASES = [
     ("verify_attn", verify_off_by_one, pins.test_verify_rows_are_prefix_attention),
     ("verify_attn", verify_off_by_one, pins.test_verify_alignment_closed_form),
@@ -172,6 +206,9 @@ CASES = [
     ("commit_length", commit_drops_one_more, pins.test_full_cache_decode_loop_matches_list_model),
     ("ring_slot_of", ring_slot_one_short, pins.test_ring_slot_hand_table),
     ("tree_masks", tree_masks_no_self, pins.test_tree_masks_hand_table),
+    ("tree_accept", tree_accept_unnormalised, pins.test_tree_accept_is_lossless_statistically),
+    ("tree_accept", tree_accept_no_update, pins.test_tree_accept_hand_examples),
+    ("tree_accept", tree_accept_no_update, pins.test_tree_accept_is_lossless_statistically),
     ("verify_tree_attn", verify_tree_base_off_by_one, pins.test_verify_tree_chain_is_verify_and_rows_match_masked_sdpa),
     ("two_level_accept", two_level_level1_swapped, pins.test_two_level_hand_examples),
     ("two_level_accept", two_level_level1_swapped, pins.test_two_level_is_lossless_statistically),

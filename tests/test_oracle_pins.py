@@ -425,6 +425,65 @@ def test_accept_with_temperature_is_lossless_statistically():
 
 
 # ---------------------------------------------------------------------------
+# accept over a candidate tree
+# ---------------------------------------------------------------------------
+
+def test_tree_accept_hand_examples():
+    with open(os.path.join(GOLDEN, "tree_accept_hand_examples.json")) as f:
+        g = json.load(f)
+    t, d = np.array(g["target"]), np.array(g["draft"])
+    for case in g["cases"]:
+        path, nxt, _ = oracle.tree_accept(t, d, case["tokens"], g["parent"], case["uniforms"], 1.0, probs=True)
+        assert (path, nxt) == (case["path"], case["next_token"]), case["name"]
+
+
+def test_tree_accept_chain_is_accept():
+    rng = np.random.default_rng(83)
+    for trial in range(300):
+        g, V = int(rng.integers(1, 7)), 30
+        T = [1.0, 0.6, 0.0][trial % 3]
+        t = rng.normal(0, 1.5, (g + 1, V))
+        d = t + rng.normal(0, 0.7, (g + 1, V))
+        tok = [0] + [int(rng.choice(V, p=oracle.distribution(d[i], T if T > 0 else 1.0))) for i in range(g)]
+        u = rng.random(g + 1)
+        n, x, _ = oracle.accept(t, d[:g], tok[1:], u, T)
+        path, y, _ = oracle.tree_accept(t, d, tok, [-1] + list(range(g)), u, T)
+        assert path == list(range(1, n + 1)) and y == x
+
+
+def _tree_lossless_setup(rng, V=6):
+    # root 0 -> nodes 1, 2, 3 (drafted i.i.d. from q0); node c in 1..3 ->
+    # two children drafted i.i.d. from q1; every depth-1 node has target p1
+    p = rng.dirichlet(np.ones(V) * 0.8, 3)
+    q = rng.dirichlet(np.ones(V) * 0.8, 2)
+    parent = [-1, 0, 0, 0, 1, 1, 2, 2, 3, 3]
+    target = np.stack([p[0], p[1], p[1], p[1]] + [p[2]] * 6)
+    draft = np.stack([q[0], q[1], q[1], q[1]] + [q[1]] * 6)
+    return p, q, parent, target, draft
+
+
+def test_tree_accept_is_lossless_statistically():
+    """Siblings drafted independently from their parent's q: the first emitted
+    token follows p_0 and, when a depth-1 node is kept, the second follows
+    p_1 (blog, '2. Dual Rejection Sampling')."""
+    rng = np.random.default_rng(89)
+    V, trials = 6, 20000
+    p, q, parent, target, draft = _tree_lossless_setup(rng, V)
+    first = np.zeros(V, np.int64)
+    second = np.zeros(V, np.int64)
+    for _ in range(trials):
+        tok = [0] + list(rng.choice(V, 3, p=q[0])) + list(rng.choice(V, 6, p=q[1]))
+        path, nxt, _ = oracle.tree_accept(target, draft, tok, parent, rng.random(10), 1.0, probs=True)
+        emitted = [tok[c] for c in path] + [nxt]
+        first[emitted[0]] += 1
+        if path:
+            second[emitted[1]] += 1
+    for counts, ref in ((first, p[0]), (second, p[1])):
+        ok, stat, crit = chi2_ok(counts, ref)
+        assert ok, (stat, crit)
+
+
+# ---------------------------------------------------------------------------
 # two-level accept r -> q -> p (dual rejection sampling)
 # ---------------------------------------------------------------------------
 
