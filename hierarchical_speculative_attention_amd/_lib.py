@@ -29,6 +29,7 @@ EXPORTS = [
     "tf_sparse_verify_attn_workspace_size", "tf_stream_attn",
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
     "tf_append_kv", "tf_commit_length", "tf_collect_candidates", "tf_verify_tree_attn", "tf_tree_masks",
+    "tf_tree_accept", "tf_tree_accept_workspace_size",
 ]
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "tf_collect_candidates": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, vp]),
         "tf_verify_tree_attn": (ctypes.c_int, [vp, i32, i32, vp, vp, dp, vp, vp, vp, vp, sz, vp]),
         "tf_tree_masks": (ctypes.c_int, [vp, i32, i32, vp, vp]),
+        "tf_tree_accept": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]),
+        "tf_tree_accept_workspace_size": (sz, [i32, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -415,4 +418,30 @@ def verify_tree_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDe
                                      _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, q.device)),
            "tf_verify_tree_attn")
     return out, lse
+
+
+def tree_accept(target: torch.Tensor, draft: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                uniforms: torch.Tensor, temperature: float, probs: bool = False,
+                ws: Optional[torch.Tensor] = None, stream=None):
+    """Accept / reject over candidate trees: target, draft [B][Q][V] fp32;
+    tokens, parent [B][Q] int32; uniforms [B][Q] fp64.  Returns
+    (n_accepted [B], path [B][Q-1], next_token [B])."""
+    _need(target, "target", torch.float32)
+    _need(tokens, "tokens", torch.int32)
+    _need(parent, "parent", torch.int32)
+    _need(uniforms, "uniforms", torch.float64)
+    B, Q, V = target.shape
+    if Q > 1:
+        _need(draft, "draft", torch.float32)
+    n_acc = torch.empty(B, dtype=torch.int32, device=target.device)
+    path = torch.empty((B, max(Q - 1, 1)), dtype=torch.int32, device=target.device)
+    nxt = torch.empty(B, dtype=torch.int32, device=target.device)
+    need = int(lib().tf_tree_accept_workspace_size(B, V))
+    if ws is None:
+        ws = workspace(need, target.device)
+    _check(lib().tf_tree_accept(_ptr(target), _ptr(draft) if Q > 1 else None, _ptr(tokens), _ptr(parent),
+                                _ptr(uniforms), B, Q, V, ctypes.c_float(temperature), TF_ACCEPT_PROBS if probs else 0,
+                                _ptr(n_acc), _ptr(path), _ptr(nxt), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(stream, target.device)), "tf_tree_accept")
+    return n_acc, path[:, :Q - 1], nxt
 

@@ -463,3 +463,36 @@ TF_EXPORT int tf_collect_candidates(const int32_t* draft_tokens, const int32_t* 
                                        count_out, cand, cand_q, gamma2, (hipStream_t)stream),
                    "tf_collect_candidates");
 }
+
+// ---------------------------------------------------------------------------
+// Accept over a candidate tree
+// ---------------------------------------------------------------------------
+TF_EXPORT size_t tf_tree_accept_workspace_size(int32_t B, int32_t V) { return tfk::tree_accept_ws_bytes(B, V); }
+
+TF_EXPORT int tf_tree_accept(const float* target, const float* draft, const int32_t* tokens, const int32_t* parent,
+                             const double* uniforms, int32_t B, int32_t Q, int32_t V, float temperature,
+                             int32_t flags, int32_t* n_accepted, int32_t* path, int32_t* next_token, void* ws,
+                             size_t ws_bytes, tf_stream_t stream) {
+  if (B < 0 || Q < 1 || V < 1) return fail(TF_ERR_INVALID_ARG, "B=%d Q=%d V=%d out of range", B, Q, V);
+  if (!(temperature >= 0.f) || std::isinf(temperature))
+    return fail(TF_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (flags & ~TF_ACCEPT_PROBS) return fail(TF_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (Q > tfk::tree_accept_max_nodes()) return fail(TF_ERR_UNSUPPORTED, "Q=%d above %d", Q, tfk::tree_accept_max_nodes());
+  if (V > tfk::tree_accept_max_vocab()) return fail(TF_ERR_UNSUPPORTED, "V=%d above %d", V, tfk::tree_accept_max_vocab());
+  if (B == 0) return ok();
+  TRY(check_ptr(target, "target", 4));
+  if (Q > 1) {
+    TRY(check_ptr(draft, "draft", 4));
+    TRY(check_ptr(path, "path", 4));
+  }
+  TRY(check_ptr(tokens, "tokens", 4));
+  TRY(check_ptr(parent, "parent", 4));
+  TRY(check_ptr(uniforms, "uniforms", 8));
+  TRY(check_ptr(n_accepted, "n_accepted", 4));
+  TRY(check_ptr(next_token, "next_token", 4));
+  TRY(check_ws(ws, ws_bytes, tfk::tree_accept_ws_bytes(B, V)));
+  return check_hip(tfk::launch_tree_accept(target, draft, tokens, parent, uniforms, B, Q, V, temperature, flags,
+                                           n_accepted, path, next_token, ws, (hipStream_t)stream),
+                   "tf_tree_accept");
+}
+

@@ -89,6 +89,14 @@ hipError_t launch_commit(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma
 
 // tree visibility masks from parent pointers
 hipError_t launch_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* masks, hipStream_t stream);
+// accept over a candidate tree
+int32_t tree_accept_max_vocab();
+int32_t tree_accept_max_nodes();
+size_t tree_accept_ws_bytes(int32_t B, int32_t V);
+hipError_t launch_tree_accept(const float* target, const float* draft, const int32_t* tokens, const int32_t* parent,
+                              const double* uniforms, int32_t B, int32_t Q, int32_t V, float temperature,
+                              int32_t flags, int32_t* n_acc, int32_t* path, int32_t* next, void* ws,
+                              hipStream_t stream);
 // two-level accept: candidate collection
 hipError_t launch_collect(const int32_t* draft_tokens, const int32_t* n_accepted, const int32_t* next_token,
                           const float* q_rows, int32_t B, int32_t gamma1, int32_t V, const int32_t* count_in,

@@ -298,6 +298,36 @@ int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, co
                      tf_stream_t stream);
 
 /*
+ * a7 over a candidate tree.  [blog] Force 3 verifies the candidate tree Force
+ * 2 assembles; acceptance and residual as in "2. Dual Rejection Sampling".
+ * Per sequence b, Q nodes: node 0 is the last committed token, nodes
+ * 1 .. Q-1 candidates with token tokens[b][c] and parent[b][c] in [0, c) (any
+ * other value hangs c off node 0).  target[b][v] holds the target's logits
+ * (or probabilities, flag TF_ACCEPT_PROBS) for the children of node v,
+ * draft[b][v] the distribution they were drafted from (rows of leaves are not
+ * read).  From node 0, the children of the current node v are tried in index
+ * order: child c with token x is kept when p'(x) > 0 and
+ * uniforms[b][c - 1] * q_v(x) <= p'(x), where p' starts as p_v and after
+ * each rejected sibling becomes max(0, p' - q_v) renormalised (p_v if that
+ * vanishes through rounding); a kept child becomes v.  When no child is kept,
+ * or v has none, next_token[b] is drawn from p' by inverse CDF with
+ * uniforms[b][Q - 1] (the rule of tf_accept).  With siblings drafted
+ * independently from q_v the emitted tokens follow the target; a chain
+ * (parent[c] = c - 1) gives exactly tf_accept.  T = 0 is greedy as there.
+ *   target, draft: device fp32 [B][Q][V]; tokens, parent: device int32
+ *   [B][Q] (tokens[b][0] not read); uniforms: device fp64 [B][Q] in (0, 1).
+ *   Outputs: n_accepted[b] = kept nodes; path[b][0 .. Q-2] = the kept nodes
+ *   in order, then -1 (NULL allowed when Q = 1); next_token[b].
+ *   ws: tf_tree_accept_workspace_size(B, V) bytes (the fp64 residual).
+ *   Limits: Q <= 64, V <= 65536.
+ */
+int tf_tree_accept(const float* target, const float* draft, const int32_t* tokens, const int32_t* parent,
+                   const double* uniforms, int32_t B, int32_t Q, int32_t V, float temperature, int32_t flags,
+                   int32_t* n_accepted, int32_t* path, int32_t* next_token, void* ws, size_t ws_bytes,
+                   tf_stream_t stream);
+size_t tf_tree_accept_workspace_size(int32_t B, int32_t V);
+
+/*
  * Two-level accept, r -> q -> p ([blog] "2. Dual Rejection Sampling": Force 2
  * keeps a drafter candidate x when min(1, q(x)/r(x)) >= u1; what Force 2
  * passes on is verified by Force 3 with min(1, p(x)/q(x)) >= u2, a rejection

@@ -168,3 +168,19 @@ def test_tree_entry_points_validate():
     assert L.tf_tree_masks(FAKE, 2, 65, FAKE, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_tree_masks(None, 2, 5, FAKE, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_tree_masks(None, 0, 5, None, None) == T.TF_OK
+
+
+def test_tree_accept_validates():
+    L = T.lib()
+    f = ctypes.c_float
+    call = lambda B=2, Q=5, V=100, t=1.0, flags=0, ws=FAKE, ws_bytes=1 << 30, draft=FAKE: L.tf_tree_accept(
+        FAKE, draft, FAKE, FAKE, FAKE, B, Q, V, f(t), flags, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+    assert call(Q=0) == T.TF_ERR_INVALID_ARG
+    assert call(Q=65) == T.TF_ERR_UNSUPPORTED
+    assert call(V=70000) == T.TF_ERR_UNSUPPORTED
+    assert call(t=-1.0) == T.TF_ERR_INVALID_ARG
+    assert call(flags=8) == T.TF_ERR_INVALID_ARG
+    assert call(draft=None) == T.TF_ERR_INVALID_ARG
+    assert call(ws=None, ws_bytes=0) == T.TF_ERR_WORKSPACE
+    assert L.tf_tree_accept_workspace_size(2, 100) >= 2 * 100 * 8
+    assert call(B=0) == T.TF_OK
