@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode attn GB/s & % HBM peak, sparse-draft+verify steps/s at 128K ctx"
+EXTRA_ROWS = 512  # room after every sequence's rows for the rows the three-tier loop appends
 HBM_PEAK_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc")
 VERIFY_SRCS = [os.path.join(CSRC, f) for f in ("attn.hip", "api.hip", "tf_internal.h")]
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers the CPU oracle baseline times")
     ap.add_argument("--ck-dtype", default="kv", choices=["kv", "fp32"])
+    ap.add_argument("--no-three-tier", action="store_true", help="skip the three-tier step loop")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device-to-device copy (a kernel of known traffic for HBM counters)")
     return ap.parse_args()
@@ -118,7 +120,7 @@ def main():
             K, V, qv, qd, lay, planted = synth.make_layer_torch(
                 lens=lens, Hq=Hq, Hkv=Hkv, d=d, dtype=W["dtype"], Q=Q, chunk_size=cs, plant=W["plant"],
                 seed=0, layer=l, device=dev, plant_fraction=W.get("plant_fraction", 0.01),
-                plant_count=W.get("plant_count", 0), zipf_s=W.get("zipf_s", 1.1))
+                plant_count=W.get("plant_count", 0), zipf_s=W.get("zipf_s", 1.1), extra_rows=EXTRA_ROWS)
             x = Layer()
             x.K, x.V, x.qv, x.qd = K, V, qv, qd.view(B, Hq, d)
             x.kv = tf.KVDesc.from_layout(lay, tdt, dev)
@@ -321,10 +323,77 @@ def main():
                                "GB_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},
         "setup_s": round(time.perf_counter() - t_setup, 1),
     }
+    if not args.no_three_tier and B == 1:
+        result["three_tier"] = three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, dev,
+                                              args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(L[:max(1, min(args.cpu_layers, layers))], lens, Hq, Hkv, d, cs, k, S,
                                               Wn, Q, layers, acc_in, tdt)
     print(json.dumps(result), flush=True)
+
+
+def three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, dev, steps, warmup, stream):
+    """The three tiers in a loop on the same target caches: a 2-layer drafter
+    (the target's head shape) on a sink + window ring drafts gamma1 = 2 tokens
+    per Force 2 round, Force 2 rounds on the retrieval cache (tail 64) run
+    until gamma2 = gamma candidates exist, Force 3 verifies them on the full
+    cache (hierarchical_speculative_attention_amd.three_tier).  Eager launches;
+    one 4-byte read-back per round and per step (the host decides the rounds).
+    Logits are synthetic: p ~ N(0, 2); q = p + N(0, 0.5); r = q + N(0, 0.5)."""
+    import torch
+    import hierarchical_speculative_attention_amd as tf
+    from hierarchical_speculative_attention_amd import synth
+    from hierarchical_speculative_attention_amd import three_tier as tt
+    n0 = lens[0]
+    g1, g2 = 2, gamma
+    seq_len = torch.tensor([n0], dtype=torch.int32, device=dev)
+    ck_len = torch.tensor([-(-n0 // cs)], dtype=torch.int32, device=dev)
+    C_cap = -(-(n0 + EXTRA_ROWS) // cs)
+    g = torch.Generator(device=dev).manual_seed(synth.torch_seed(0, 0, "extra"))
+    rnd = lambda *shape: torch.randn(*shape, generator=g, device=dev).to(tdt)
+    with torch.cuda.stream(stream):
+        target = []
+        for x in L:
+            kv = tf.KVDesc(1, Hkv, tdt, x.kv.seq_base, x.kv.seq_cap, seq_len, n0 + EXTRA_ROWS, dev)
+            ckl = synth.KVLayout.build([C_cap], Hkv, d, caps=[C_cap])
+            ckd = tf.KVDesc(1, Hkv, ck_dt, ckl.seq_base, ckl.seq_cap, ck_len, C_cap, dev)
+            ck = torch.empty(ckl.total_elems, dtype=ck_dt, device=dev)
+            tf.build_chunk_keys(x.K, kv, cs, ck, ckd, stream=stream)
+            target.append(tt.TargetLayer(x.K, x.V, kv, ck, ckd))
+        cap = S + Wn + tt.drafter_reserve(g1, g2)
+        d_len = torch.tensor([n0], dtype=torch.int32, device=dev)
+        drafter = []
+        for _ in range(2):
+            lay = synth.KVLayout.build([n0], Hkv, d, caps=[cap])
+            sd = tf.KVDesc(1, Hkv, tdt, lay.seq_base, lay.seq_cap, d_len, n0, dev)
+            drafter.append(tt.DrafterLayer(rnd(lay.total_elems), rnd(lay.total_elems), sd))
+        P = torch.randn((1, g2 + 1, vocab), generator=g, device=dev) * 2
+        Qr = (P[:, :g1 + 1] + torch.randn((1, g1 + 1, vocab), generator=g, device=dev) * 0.5).contiguous()
+        R = (Qr[:, :g1] + torch.randn((1, g1, vocab), generator=g, device=dev) * 0.5).contiguous()
+        rng = np.random.default_rng(7)
+        syn = tt.Synthetic(draft_q=L[0].qd, draft_rows=[rnd(1, Hkv, r, d) for r in (1, 2, 3)], r_rows=R,
+                           f2_q=rnd(1, Hq, g1 + 1, d), f2_rows=rnd(1, Hkv, g1 + 1, d), q_rows=Qr, f3_q=L[0].qv,
+                           one_row=rnd(1, Hkv, 1, d), p_rows=P.contiguous(),
+                           uniforms=torch.from_numpy(synth.open_uniforms(rng, 1 << 20)).to(dev))
+        step = tt.ThreeTierStep(target, drafter, syn, Hq=Hq, chunk_size=cs, k=k, tail=64, gamma1=g1, gamma2=g2,
+                                n_sink=S, window=Wn, stream=stream)
+        for _ in range(warmup):
+            step.step()
+        stream.synchronize()
+        s0, r0, e0 = step.steps, step.rounds, step.emitted
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step.step()
+        stream.synchronize()
+        el = time.perf_counter() - t0
+    n_steps, n_rounds, n_tok = step.steps - s0, step.rounds - r0, step.emitted - e0
+    return {"steps_per_s": round(n_steps / el, 3), "tokens_per_s": round(n_tok / el, 2),
+            "ms_per_step": round(el / n_steps * 1e3, 3), "rounds_per_step": round(n_rounds / n_steps, 3),
+            "tokens_per_step": round(n_tok / n_steps, 3), "steps": n_steps, "gamma1": g1, "gamma2": g2,
+            "drafter": f"2 layers x {Hkv} heads x {d}, ring {S} sinks + {Wn} window",
+            "force2": f"sparse verification of gamma1 + 1 rows over {k} chunks x {cs} rows + a 64-row causal tail",
+            "launch": "eager launches; the host reads back 4 bytes per Force 2 round and per step",
+            "logits": "synthetic: p ~ N(0,2), q = p + N(0,0.5), r = q + N(0,0.5)"}
 
 
 def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_in, tdt):

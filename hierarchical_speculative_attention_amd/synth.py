@@ -347,7 +347,7 @@ def make_accept_inputs(*, B: int, gamma: int, vocab: int = 32000, sd: float = 2.
 def make_layer_torch(*, lens: Sequence[int], Hq: int, Hkv: int, d: int, dtype: str,
                      Q: int, chunk_size: int, plant: Optional[str], seed: int, layer: int,
                      device, plant_fraction: float = 0.01, plant_count: int = 0,
-                     zipf_s: float = 1.1, K_out=None, V_out=None):
+                     zipf_s: float = 1.1, K_out=None, V_out=None, extra_rows: int = 0):
     """Generate one layer directly in device memory.
 
     Returns (K, V, q_verify, q_draft, layout, planted) with K and V flat torch
@@ -355,11 +355,13 @@ def make_layer_torch(*, lens: Sequence[int], Hq: int, Hkv: int, d: int, dtype: s
     lists the planted chunk indices (Zipf: the rank-1..3 chunks per KV head).  K_out/V_out
     may be preallocated flat views to fill (so many layers can share one big
     allocation).  The recipe is the one of make_attn_inputs; the random
-    streams differ (torch Philox instead of numpy PCG64)."""
+    streams differ (torch Philox instead of numpy PCG64).  extra_rows adds
+    room after every sequence's rows (filled with N(0, 1) values too) for
+    rows a decode loop appends."""
     import torch
     tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
     G = Hq // Hkv
-    lay = KVLayout.build(lens, Hkv, d, caps=[int(n) for n in lens])
+    lay = KVLayout.build(lens, Hkv, d, caps=[int(n) + int(extra_rows) for n in lens])
     n_el = lay.total_elems
     gk = torch.Generator(device=device).manual_seed(torch_seed(seed, layer, "K"))
     gv = torch.Generator(device=device).manual_seed(torch_seed(seed, layer, "V"))

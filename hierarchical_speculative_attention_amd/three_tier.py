@@ -1,0 +1,249 @@
+"""Three-tier decode step of hierarchical speculative decoding, composed from
+the library's C-ABI calls: Force 1 (a small drafter on a sink + window ring)
+drafts, Force 2 (the target on the retrieval-sparse cache) keeps or rejects
+each round of drafts, and once gamma2 candidates are collected Force 3 (the
+target on the full cache) verifies them in one pass (TriForce blog, "1. The
+Three Forces of TriForce"; "2. Dual Rejection Sampling" for both levels of
+acceptance).
+
+Every step of the computation runs in the library's kernels; this module only
+sequences the calls and keeps the host-side counts.  It drives one sequence
+(B = 1): how many Force 2 rounds a step needs depends on how many drafts each
+round keeps, so after each round the kept count is read back (8 bytes) and
+the host decides whether another round is needed and how many rows each cache
+gains or loses.
+
+The models' outputs -- new K/V rows, queries and logits -- are synthetic
+device tensors given by the caller (there are no weights here); the control
+flow, the cache contents and the lengths are those of the method:
+
+  round (until >= gamma2 candidates): the drafter consumes the committed
+    tokens it has not seen and the current token, then its own drafts (one
+    ring row per token, streaming attention per drafter layer, sampling from
+    its logits with tf_accept at gamma = 0); the target appends the current
+    token and the gamma1 drafts to its full cache and attends them over the
+    retrieved chunks below a causal tail (tf_sparse_verify_attn); level 1
+    tests the drafts against q (tf_accept); tf_collect_candidates appends the
+    emitted tokens with their q rows; rejected drafts leave both caches;
+  then the full cache is cut (or extended by the last drawn token) to the
+    current token plus exactly gamma2 candidates, Force 3 attends them over
+    the full cache (tf_verify_attn), level 2 tests them against p
+    (tf_accept), the rejected candidates leave both caches, and the chunk
+    keys the new rows fell into are refreshed for the next step's retrieval.
+
+Host-side counts, per step (n = committed rows before the current token):
+  a round keeps 1 + n1 rows of the target's gamma1 + 1 and 1 + min(n1,
+  gamma1 - 1) of the drafter's gamma1 new ones; a kept last draft is one the
+  drafter has not consumed (it becomes pending).  After the rounds the target
+  holds the current token and the first total - 1 emitted tokens (the chain,
+  whose device count stops at gamma2, keeps the first gamma2 of them).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import torch
+
+from . import _lib as tf
+
+
+@dataclasses.dataclass
+class TargetLayer:
+    K: torch.Tensor
+    V: torch.Tensor
+    kv: "tf.KVDesc"     # seq_len: the step's shared length array; max_len: the rows allocated
+    ck: torch.Tensor
+    ckd: "tf.KVDesc"    # seq_len: the shared chunk-count array
+
+
+@dataclasses.dataclass
+class DrafterLayer:
+    Ks: torch.Tensor
+    Vs: torch.Tensor
+    sd: "tf.KVDesc"     # seq_len: the drafter's shared logical length array
+
+
+@dataclasses.dataclass
+class Synthetic:
+    """The models' outputs: fixed device tensors, reused by every round."""
+    draft_q: torch.Tensor          # [1][Hq][d] drafter query (also the retrieval query)
+    draft_rows: List[torch.Tensor]  # draft_rows[R - 1]: [1][H][R][d] new drafter K/V rows, R = 1, 2, 3
+    r_rows: torch.Tensor           # [1][gamma1][V] drafter logits, one row per draft position
+    f2_q: torch.Tensor             # [1][Hq][gamma1 + 1][d]
+    f2_rows: torch.Tensor          # [1][H][gamma1 + 1][d]
+    q_rows: torch.Tensor           # [1][gamma1 + 1][V] Force 2 logits
+    f3_q: torch.Tensor             # [1][Hq][gamma2 + 1][d]
+    one_row: torch.Tensor          # [1][H][1][d]
+    p_rows: torch.Tensor           # [1][gamma2 + 1][V] Force 3 logits
+    uniforms: torch.Tensor         # [U] fp64 in (0, 1), consumed in order (wrapping around)
+
+
+def drafter_reserve(gamma1: int, gamma2: int) -> int:
+    """Rows a step may roll back from the drafter's ring (its slack must be at
+    least this): everything it consumed since the step began."""
+    return gamma1 + gamma2 + 3
+
+
+class ThreeTierStep:
+    def __init__(self, target: List[TargetLayer], drafter: List[DrafterLayer], syn: Synthetic, *, Hq: int,
+                 chunk_size: int, k: int, tail: int, gamma1: int, gamma2: int, n_sink: int, window: int,
+                 temperature: float = 1.0, stream: Optional[torch.cuda.Stream] = None, record: bool = False):
+        self.t, self.dr, self.syn = target, drafter, syn
+        self.record = record      # keep each round's and step's decisions (tests)
+        self.log: list = []
+        self.Hq, self.cs, self.k, self.tail = Hq, chunk_size, k, tail
+        self.g1, self.g2, self.S, self.W = gamma1, gamma2, n_sink, window
+        self.T, self.s = temperature, stream
+        kv0 = target[0].kv
+        dev = target[0].K.device
+        V = syn.q_rows.shape[-1]
+        self.seq_len = kv0.seq_len                 # shared by every target layer's descriptor
+        self.ck_len = target[0].ckd.seq_len        # shared by every chunk-key descriptor
+        self.d_len = drafter[0].sd.seq_len         # shared by every drafter layer's descriptor
+        self.c_max = target[0].ckd.max_len
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.scores = torch.empty((1, kv0.H, self.c_max), dtype=torch.float32, device=dev)
+        self.idx = [torch.empty((1, kv0.H, k), **i32) for _ in target]
+        self.o_d = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+        self.o2 = torch.empty((1, Hq, gamma1 + 1, 128), dtype=torch.float32, device=dev)
+        self.o3 = torch.empty((1, Hq, gamma2 + 1, 128), dtype=torch.float32, device=dev)
+        self.drafts = torch.empty((gamma1, 1), **i32)    # row j: draft j (a contiguous [1] per call)
+        self.drafts_row = torch.empty((1, gamma1), **i32)
+        self.na_d = torch.empty(1, **i32)
+        self.n1, self.y = torch.empty(1, **i32), torch.empty(1, **i32)
+        self.n2, self.nxt = torch.empty(1, **i32), torch.empty(1, **i32)
+        self.cnt = [torch.zeros(1, **i32), torch.zeros(1, **i32)]
+        self.cand = torch.empty((1, gamma2), **i32)
+        self.cand_q = torch.empty((1, gamma2, V), dtype=torch.float32, device=dev)
+        self.zero = torch.zeros(1, **i32)
+        self.chunk_begin = torch.empty(1, **i32)
+        self.host = torch.empty(4, dtype=torch.int32).pin_memory()
+        self.ws2 = tf.workspace(tf.sparse_verify_attn_workspace_size(1, Hq, kv0.H, gamma1 + 1, k, chunk_size, tail),
+                                dev)
+        self.ws3 = tf.workspace(tf.verify_attn_workspace_size(1, Hq, kv0.H, gamma2 + 1, kv0.max_len), dev)
+        self.wsa = tf.workspace(tf.accept_workspace_size(1, max(gamma1, gamma2), V), dev)
+        self.u_pos = 0
+        self.n = int(kv0.seq_len[0].item())            # committed rows before the current token
+        self.pending = self.n - int(drafter[0].sd.seq_len[0].item())  # committed tokens the drafter has not consumed
+        assert 0 <= self.pending <= 2
+        self.steps = self.rounds = self.emitted = 0
+
+    # -- helpers ---------------------------------------------------------------
+    def _sync(self):
+        (self.s or torch.cuda.current_stream()).synchronize()
+
+    def _u(self, n):
+        if self.u_pos + n > self.syn.uniforms.numel():
+            self.u_pos = 0
+        u = self.syn.uniforms[self.u_pos:self.u_pos + n]
+        self.u_pos += n
+        return u.view(1, n)
+
+    def _drop(self, seq_len, rows):
+        """seq_len -= rows on the device (a commit of `rows` rejected drafts)."""
+        if rows > 0:
+            tf.commit_length(seq_len, 0, rows, self.zero, stream=self.s)
+
+    def _drafter_consume(self, R):
+        """The drafter consumes R tokens: R rows on every layer's ring, then a
+        streaming attention of the last one's query per layer."""
+        rows = self.syn.draft_rows[R - 1]
+        for L in self.dr:
+            tf.append_kv(rows, rows, L.Ks, L.Vs, L.sd, ring=True, n_sink=self.S, window=self.W,
+                         reserve=drafter_reserve(self.g1, self.g2), stream=self.s)
+        tf.commit_length(self.d_len, R, stream=self.s)
+        for L in self.dr:
+            tf.stream_attn(self.syn.draft_q, L.Ks, L.Vs, L.sd, self.S, self.W, out=self.o_d, stream=self.s)
+
+    # -- one step --------------------------------------------------------------
+    def step(self) -> int:
+        """One three-tier step; returns the number of tokens it emits."""
+        s, g1, g2 = self.s, self.g1, self.g2
+        n_start = self.n
+        d_start = self.n - self.pending       # drafter's consumed length
+        # retrieval for this step, from the committed rows
+        self.ck_len.fill_(-(-n_start // self.cs))
+        for L, idx in zip(self.t, self.idx):
+            tf.score_chunks(self.syn.draft_q, self.Hq, L.ck, L.ckd, self.c_max, scores=self.scores, stream=s)
+            tf.select_topk(self.scores, self.ck_len, self.k, idx=idx, stream=s)
+        self.cnt[0].zero_()
+        cin, total, rounds = 0, 0, 0          # total: tokens the rounds emitted (the chain keeps the first gamma2)
+        d_len = d_start                        # host copy of the drafter's length
+        while total < g2:
+            rounds += 1
+            n_round = self.n
+            # Force 1: the unseen committed tokens and the current token, then its drafts
+            self._drafter_consume(1 + self.pending)
+            d_len += 1 + self.pending
+            self.pending = 0
+            for j in range(g1):
+                if j > 0:
+                    self._drafter_consume(1)
+                    d_len += 1
+                tf.accept(self.syn.r_rows[:, j:j + 1], None, None, self._u(1), self.T, n_accepted=self.na_d,
+                          next_token=self.drafts[j], ws=self.wsa, stream=s)
+            self.drafts_row.copy_(self.drafts.view(1, g1))
+            # Force 2: the current token and the drafts on the retrieval cache
+            for L in self.t:
+                tf.append_kv(self.syn.f2_rows, self.syn.f2_rows, L.K, L.V, L.kv, stream=s)
+            tf.commit_length(self.seq_len, g1 + 1, stream=s)
+            for L, idx in zip(self.t, self.idx):
+                tf.sparse_verify_attn(self.syn.f2_q, L.K, L.V, L.kv, idx, self.cs, self.tail, out=self.o2,
+                                      ws=self.ws2, stream=s)
+            tf.accept(self.syn.q_rows, self.syn.r_rows, self.drafts_row, self._u(g1 + 1), self.T,
+                      n_accepted=self.n1, next_token=self.y, ws=self.wsa, stream=s)
+            cout = 1 - cin
+            tf.collect_candidates(self.drafts_row, self.n1, self.y, self.syn.q_rows, self.cnt[cin], self.cnt[cout],
+                                  self.cand, self.cand_q, stream=s)
+            tf.commit_length(self.seq_len, 0, g1, self.n1, stream=s)   # rejected drafts leave the full cache
+            self.host[0:1].copy_(self.n1, non_blocking=True)
+            self._sync()
+            n1 = int(self.host[0])
+            total += n1 + 1
+            cin = cout
+            if self.record:
+                self.log.append(("round", self.drafts_row.cpu().numpy()[0].tolist(), n1, int(self.y.item()),
+                                 self.syn.uniforms[self.u_pos - g1 - 1:self.u_pos].cpu().numpy()))
+            self.n = n_round + 1 + n1
+            # the drafter consumed the current token and drafts 1 .. g1 - 1
+            drop = (g1 - 1) - min(n1, g1 - 1)
+            self._drop(self.d_len, drop)
+            d_len -= drop
+            self.pending = self.n - d_len
+        # the full cache holds the current token and the first total - 1
+        # emitted tokens: keep the current token and exactly gamma2 candidates
+        if total == g2:
+            for L in self.t:
+                tf.append_kv(self.syn.one_row, self.syn.one_row, L.K, L.V, L.kv, stream=s)
+            tf.commit_length(self.seq_len, 1, stream=s)
+        else:
+            self._drop(self.seq_len, total - 1 - g2)
+        # Force 3: the current token and the candidates on the full cache
+        for L in self.t:
+            tf.verify_attn(self.syn.f3_q, L.K, L.V, L.kv, out=self.o3, ws=self.ws3, stream=s)
+        tf.accept(self.syn.p_rows, self.cand_q, self.cand, self._u(g2 + 1), self.T, n_accepted=self.n2,
+                  next_token=self.nxt, ws=self.wsa, stream=s)
+        tf.commit_length(self.seq_len, 0, g2, self.n2, stream=s)
+        # chunk keys of the chunks the step's rows fell into
+        self.chunk_begin.fill_(n_start // self.cs)
+        for L in self.t:
+            tf.build_chunk_keys(L.K, L.kv, self.cs, L.ck, L.ckd, chunk_begin=self.chunk_begin,
+                                max_chunks=(g2 + 1) // self.cs + 2, stream=s)
+        self.host[2:3].copy_(self.n2, non_blocking=True)
+        self._sync()
+        n2 = int(self.host[2])
+        if self.record:
+            self.log.append(("step", self.cand.cpu().numpy()[0].tolist(), n2, int(self.nxt.item()),
+                             self.syn.uniforms[self.u_pos - g2 - 1:self.u_pos].cpu().numpy(),
+                             self.cand_q.cpu().numpy()[0]))
+        self.n = n_start + 1 + n2
+        # the drafter keeps what it consumed of the committed tokens
+        keep = min(d_len, self.n)
+        self._drop(self.d_len, d_len - keep)
+        self.pending = self.n - keep
+        self.steps += 1
+        self.rounds += rounds
+        self.emitted += n2 + 1
+        return n2 + 1
