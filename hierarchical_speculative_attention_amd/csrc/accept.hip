@@ -31,7 +31,6 @@ constexpr int kPer = kSlice / kAccThreads;     // entries per thread within a st
 constexpr int kMaxSlices = 16;                 // V <= 65536
 constexpr int kDraw = 1024;                    // vocabulary entries per draw slice
 constexpr int kDrawPer = kDraw / kAccThreads;  // fp64 weights per thread within a draw slice
-constexpr int kMaxDraw = 64;                   // draw slices at V = 65536 (one per lane)
 
 struct SliceStat {
   float mx;   // largest logit in the slice

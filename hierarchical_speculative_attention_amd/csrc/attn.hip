@@ -590,9 +590,17 @@ void attn_kernel(const AttnArgs a) {
 // group's (max, sum) pairs and its 32 accumulator rows are all requested
 // before any is used, so a group costs one memory round trip; groups are
 // folded with an online rescale.  The first group is requested before the
-// sequence geometry is read: every split index below the planned split count
+// sequence geometry is known: every split index below the planned split count
 // lies inside the workspace, and splits past this sequence's own count are
 // dropped by selection (their contents are never combined arithmetically).
+// Lane s of the wave holds split s's (max, sum); every other lane reads them
+// with readlane (a scalar operand, no LDS round trip: shuffles through LDS
+// made the merge's arithmetic cost more than its loads), and the group's
+// max, weighted sum and accumulators are folded in split order.
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   constexpr int kGroup = 32;
@@ -602,20 +610,32 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   const size_t bh = (size_t)b * a.Hkv + hk;
   const size_t pbase = bh * a.nsplit * a.rows_pad + row;
   const float2* ml = (const float2*)a.part_ml;
+  SeqDesc sd;
+  sd.base = 0;  // not used by the geometry
+  sd.cap = a.seq_cap[b];
+  sd.len = a.seq_len[b];
 
   float2 mlv;
   float2 v[kGroup];
+  // Loads are unconditional, from split indices clamped into [0, bound):
+  // a conditional load becomes a branch of its own and waits on its result.
   auto load_group = [&](int s0, int bound) {
-    const int sl = s0 + (lane & (kGroup - 1));
-    mlv = sl < bound ? ml[pbase + (size_t)sl * a.rows_pad] : make_float2(kNegInf, 0.f);
+    const int sl = min(s0 + (lane & (kGroup - 1)), bound - 1);
+    mlv = ml[pbase + (size_t)sl * a.rows_pad];
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
-      v[u] = (s0 + u < bound) ? *(const float2*)(a.part_o + (pbase + (size_t)(s0 + u) * a.rows_pad) * kHeadDim + 2 * lane)
-                              : make_float2(0.f, 0.f);
+      v[u] = *(const float2*)(a.part_o + (pbase + (size_t)min(s0 + u, bound - 1) * a.rows_pad) * kHeadDim + 2 * lane);
   };
   load_group(0, a.nsplit);
+  // Every load above is consumed here, before the geometry decides whether
+  // this row merges at all: otherwise the compiler sinks the group's loads
+  // past that branch and the descriptor read and the group become two
+  // serial round trips instead of one.
+  asm volatile("" : : "v"(sd.cap), "v"(sd.len), "v"(mlv.x), "v"(mlv.y));
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) asm volatile("" : : "v"(v[u].x), "v"(v[u].y));
 
-  const Geo geo = make_geo<MODE>(a, load_seq(a, b));
+  const Geo geo = make_geo<MODE>(a, sd);
   const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
   if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
 
@@ -626,22 +646,22 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
       if (s0 + u >= nsp) v[u] = make_float2(0.f, 0.f);
-    float gm = mlv.x;
+    float gm = kNegInf;
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+    for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, lane_f(mlv.x, u));
     const float Mn = fmaxf(Mx, gm);
     if (Mn == kNegInf) continue;  // nothing seen yet
     const float r = (Mx == kNegInf) ? 0.f : fast_exp2((Mx - Mn) * c2);
     const float e = (mlv.x == kNegInf) ? 0.f : fast_exp2((mlv.x - Mn) * c2);
-    float le = (lane < kGroup) ? e * mlv.y : 0.f;
+    float le = 0.f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) le += __shfl_xor(le, off);
+    for (int u = 0; u < kGroup; ++u) le += lane_f(e, u) * lane_f(mlv.y, u);
     Ls = Ls * r + le;
     o0 *= r;
     o1 *= r;
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      const float eu = __shfl(e, u);
+      const float eu = lane_f(e, u);
       o0 += eu * v[u].x;
       o1 += eu * v[u].y;
     }
