@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     KVDesc, TfError, accept, build_chunk_keys, score_chunks, select_topk, sparse_attn,
     sparse_verify_attn, sparse_verify_attn_workspace_size,
     stream_attn, verify_attn, workspace, verify_attn_workspace_size,
-    sparse_attn_workspace_size, accept_workspace_size, lib, append_kv, commit_length,
+    sparse_attn_workspace_size, accept_workspace_size, tree_accept_workspace_size, lib, append_kv, commit_length,
     collect_candidates, tree_masks, verify_tree_attn, tree_accept,
     TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_WORKSPACE, TF_ERR_HIP,
     TF_APPEND_OK, TF_APPEND_NO_ROOM, TF_APPEND_RING_TOO_SMALL, TF_APPEND_BAD_LENGTH,

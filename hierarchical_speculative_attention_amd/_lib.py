@@ -171,6 +171,10 @@ def accept_workspace_size(B, gamma, V) -> int:
     return int(lib().tf_accept_workspace_size(B, gamma, V))
 
 
+def tree_accept_workspace_size(B, V) -> int:
+    return int(lib().tf_tree_accept_workspace_size(B, V))
+
+
 # ---------------------------------------------------------------------------
 # Entry points
 # ---------------------------------------------------------------------------
@@ -436,7 +440,7 @@ def tree_accept(target: torch.Tensor, draft: torch.Tensor, tokens: torch.Tensor,
     n_acc = torch.empty(B, dtype=torch.int32, device=target.device)
     path = torch.empty((B, max(Q - 1, 1)), dtype=torch.int32, device=target.device)
     nxt = torch.empty(B, dtype=torch.int32, device=target.device)
-    need = int(lib().tf_tree_accept_workspace_size(B, V))
+    need = tree_accept_workspace_size(B, V)
     if ws is None:
         ws = workspace(need, target.device)
     _check(lib().tf_tree_accept(_ptr(target), _ptr(draft) if Q > 1 else None, _ptr(tokens), _ptr(parent),

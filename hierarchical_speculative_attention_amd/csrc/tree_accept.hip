@@ -11,36 +11,54 @@
 // becomes v; when no child is kept, or v has none, the next token is drawn
 // from p' by inverse CDF.  With one child per node this is tf_accept.
 //
-// The walk is sequential per sequence (which child is kept decides the next
-// rows), so one 1024-thread workgroup per sequence runs it; thread t owns the
-// contiguous vocabulary range [t * ipt, (t + 1) * ipt).  The residual p' is
-// kept in fp64 in a caller workspace (one row of V doubles per sequence,
-// L2-resident) as stored weights times a running scale, so renormalising costs
-// no pass; probabilities are recomputed in fp64 from the logits.  (Holding it
-// in registers instead, with the draft probabilities, needed about four
-// registers per entry and spilled heavily at V = 32000.)  Everything is fp64
-// so decisions are taken in the oracle's precision.
+// Two kernels.  (1) tree_stats_kernel, spread over (sequence, 2048-entry
+// slice, row): for every target and draft row and every slice, the largest
+// logit, its lowest index and the sum of exp(x / T - that max) in fp64.
+// (2) tree_accept_kernel, one 1024-thread workgroup per sequence (the walk is
+// sequential: which child is kept decides the next rows): merging a row's
+// slice statistics gives its max and normaliser, so p_v(x) and q_v(x) at one
+// token cost one exponential and testing a child needs no pass over the
+// vocabulary.  Full passes are made only where the rule needs a whole row: a
+// rejection (p' = max(0, p' - q_v), kept in a caller workspace as fp64 weights
+// times a running scale, with q_v stored beside it when a further sibling may
+// need it) and the final draw.  Thread t owns entries t, t + 1024, ...: every
+// pass is coalesced, with eight entries' loads in flight per thread.  The
+// final draw splits the vocabulary into 16 contiguous segments (one per wave):
+// segment totals give the segment where the CDF passes u * total, and that
+// segment's wave scans it in order.  Everything is fp64, so decisions are
+// taken in the oracle's precision.
 #include "tf_internal.h"
 
 namespace tfk {
 
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / 64;
-constexpr int kTreeMaxIpt = 64;                 // V <= 65536
+constexpr int kTreeBatch = 4;                   // fp32 entries per thread per batch
+constexpr int kTreeBatchD = 4;                  // fp64 entries per thread per batch
+constexpr int kTreeMaxVocab = 65536;
 constexpr int kTreeMaxQ = 64;
+constexpr int kTreeSlice = 2048;                // vocabulary entries per statistics slice
+constexpr int kStatThreads = 256;
+constexpr int kStatIpt = kTreeSlice / kStatThreads;
 
-struct TreeDist {
-  int mode;     // 0 softmax(x / T), 1 greedy one-hot, 2 probabilities as given
-  double zmax;  // max x / T
-  double invZ;  // 1 / sum exp(x / T - zmax)
-  int amax;     // lowest index of the largest entry
+// Statistics of one slice of one row: largest logit, its lowest index, and
+// sum over the slice of exp(x / T - max / T) (0 for greedy rows).
+struct SliceStat {
+  double ssum;
+  float bmax;
+  int amax;
 };
+static_assert(sizeof(SliceStat) == 16, "slice statistics are 16 bytes");
 
-__device__ __forceinline__ double tree_val(const TreeDist& d, float x, int v, double t) {
-  if (d.mode == 2) return (double)x;
-  if (d.mode == 1) return v == d.amax ? 1.0 : 0.0;
-  return exp((double)x / t - d.zmax) * d.invZ;
-}
+// How a row turns into a distribution: softmax(x / T) (mode 0: exp(x / T -
+// zmax) * invZ), greedy one-hot at the lowest index of the largest logit
+// (mode 1), or probabilities as given (mode 2).
+struct RowStat {
+  int mode;
+  double zmax;
+  double invZ;
+  int amax;
+};
 
 struct TreeShared {
   double d[kTreeWaves];
@@ -48,6 +66,84 @@ struct TreeShared {
   int i[kTreeWaves];
 };
 
+__device__ __forceinline__ double scaled(float x, double t, bool div) { return div ? (double)x / t : (double)x; }
+
+// ---- (1) slice statistics -------------------------------------------------
+__global__ __launch_bounds__(kStatThreads) void tree_stats_kernel(const float* __restrict__ target,
+                                                                  const float* __restrict__ draft, int32_t Q,
+                                                                  int32_t V, int32_t nslice, float temperature,
+                                                                  SliceStat* __restrict__ stats) {
+  __shared__ float s_f[kStatThreads / 64];
+  __shared__ int s_i[kStatThreads / 64];
+  __shared__ double s_d[kStatThreads / 64];
+  const int b = blockIdx.x / nslice, sl = blockIdx.x % nslice, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* row = r < Q ? target + ((size_t)b * Q + r) * V : draft + ((size_t)b * Q + (r - Q)) * V;
+  const int v0 = sl * kTreeSlice, v1 = min(V, v0 + kTreeSlice);
+  float x[kStatIpt];
+#pragma unroll
+  for (int j = 0; j < kStatIpt; ++j) x[j] = row[min(v0 + j * kStatThreads + tid, v1 - 1)];
+  float bv = -__builtin_huge_valf();
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kStatIpt; ++j) {
+    const int e = v0 + j * kStatThreads + tid;
+    if (e < v1 && (x[j] > bv || (x[j] == bv && e < bi))) {
+      bv = x[j];
+      bi = e;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    s_f[w] = bv;
+    s_i[w] = bi;
+  }
+  __syncthreads();
+  bv = s_f[0];
+  bi = s_i[0];
+#pragma unroll
+  for (int q = 1; q < kStatThreads / 64; ++q)
+    if (s_f[q] > bv || (s_f[q] == bv && s_i[q] < bi)) {
+      bv = s_f[q];
+      bi = s_i[q];
+    }
+  double local = 0.0;
+  if (temperature != 0.f && bv > -__builtin_huge_valf()) {
+    const double t = (double)temperature;
+    const bool div = t != 1.0;
+    const double m = scaled(bv, t, div);
+#pragma unroll
+    for (int j = 0; j < kStatIpt; ++j) {
+      const int e = v0 + j * kStatThreads + tid;
+      if (e < v1) local += exp(scaled(x[j], t, div) - m);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  if (lane == 0) s_d[w] = local;
+  __syncthreads();
+  if (tid == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int q = 0; q < kStatThreads / 64; ++q) sum += s_d[q];
+    SliceStat st;
+    st.ssum = sum;
+    st.bmax = bv;
+    st.amax = bi;
+    const int slot = r < Q ? r : kTreeMaxQ + (r - Q);  // draft rows from slot kTreeMaxQ on
+    stats[((size_t)b * 2 * kTreeMaxQ + slot) * nslice + sl] = st;
+  }
+}
+
+// ---- (2) the walk ---------------------------------------------------------
 // Block reductions in a fixed order (16 wave partials summed by every thread).
 __device__ __forceinline__ double tree_sum(double x, TreeShared& sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -75,185 +171,412 @@ __device__ __forceinline__ int tree_max_int(int x, TreeShared& sh) {
   return m;
 }
 
-// Distribution parameters of one row (logits, or probabilities with probs).
-__device__ TreeDist tree_dist(const float* row, int v0, int v1, float temperature, int probs, TreeShared& sh) {
-  TreeDist d;
-  d.zmax = 0.0;
-  d.invZ = 1.0;
-  d.amax = 0;
-  if (probs) {
-    d.mode = 2;
-    return d;
-  }
-  float bv = -__builtin_huge_valf();
-  int bi = 0x7fffffff;
-  for (int v = v0; v < v1; ++v) {
-    const float x = row[v];
-    if (x > bv || (x == bv && v < bi)) {
-      bv = x;
-      bi = v;
-    }
-  }
+// Every row's distribution from its slices, into s_rs (target row v at slot
+// v, draft row v at slot kTreeMaxQ + v).  Wave w merges rows w, w + 16, ...;
+// lane s holds slice s (at most 32 slices).  The largest logit's lowest index
+// wins ties.
+__device__ void merge_rows(const SliceStat* st, int nslice, int nt, int nd, float temperature, int probs,
+                           RowStat* s_rs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (ov > bv || (ov == bv && oi < bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  __syncthreads();
-  if (lane == 0) {
-    sh.f[w] = bv;
-    sh.i[w] = bi;
-  }
-  __syncthreads();
-  bv = sh.f[0];
-  bi = sh.i[0];
-#pragma unroll
-  for (int q = 1; q < kTreeWaves; ++q)
-    if (sh.f[q] > bv || (sh.f[q] == bv && sh.i[q] < bi)) {
-      bv = sh.f[q];
-      bi = sh.i[q];
-    }
-  d.amax = bi;
-  if (temperature == 0.f) {
-    d.mode = 1;
-    return d;
-  }
-  d.mode = 0;
   const double t = (double)temperature;
-  d.zmax = (double)bv / t;
-  double z = 0.0;
-  for (int v = v0; v < v1; ++v) z += exp((double)row[v] / t - d.zmax);
-  d.invZ = 1.0 / tree_sum(z, sh);
-  return d;
+  const bool div = t != 1.0;
+  for (int r = w; r < nt + nd; r += kTreeWaves) {
+    const int slot = r < nt ? r : kTreeMaxQ + (r - nt);
+    RowStat d;
+    d.zmax = 0.0;
+    d.invZ = 1.0;
+    d.amax = 0;
+    if (probs) {
+      d.mode = 2;
+    } else {
+      const bool ok = lane < nslice;
+      const SliceStat x = st[(size_t)slot * nslice + min(lane, nslice - 1)];
+      float bv = ok ? x.bmax : -__builtin_huge_valf();
+      int bi = ok ? x.amax : 0x7fffffff;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      d.amax = bi;
+      if (temperature == 0.f) {
+        d.mode = 1;
+      } else {
+        d.mode = 0;
+        d.zmax = scaled(bv, t, div);
+        double z = (ok && x.bmax > -__builtin_huge_valf()) ? x.ssum * exp(scaled(x.bmax, t, div) - d.zmax) : 0.0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+        d.invZ = 1.0 / z;
+      }
+    }
+    if (lane == 0) s_rs[slot] = d;
+  }
+}
+
+template <int MODE, bool kDiv>
+__device__ __forceinline__ double prob_t(float x, int e, const RowStat& d, double t) {
+  if (MODE == 2) return (double)x;
+  if (MODE == 1) return e == d.amax ? 1.0 : 0.0;
+  return exp(scaled(x, t, kDiv) - d.zmax) * d.invZ;
+}
+
+// Probability of entry e (runtime mode; one token at a time).
+__device__ __forceinline__ double prob1(const float* row, int e, const RowStat& d, double t) {
+  const float x = row[e];
+  if (d.mode == 2) return (double)x;
+  if (d.mode == 1) return e == d.amax ? 1.0 : 0.0;
+  return exp(scaled(x, t, t != 1.0) - d.zmax) * d.invZ;
+}
+
+// First rejection at a node: p' = max(0, p_v - q_v) from the logits, written to
+// pr (and q_v to qb when store_q); returns this thread's sum.  The next
+// batch's loads are issued before the current batch is used (past the end they
+// read entry V - 1, unused).
+template <int MODE, bool kDiv>
+__device__ double first_reject_t(const float* trow, const float* drow, const RowStat& dp, const RowStat& dq,
+                                 double t, int V, double* pr, double* qb, bool store_q) {
+  constexpr int kStep = kTreeThreads * kTreeBatch;
+  const int tid = threadIdx.x;
+  double local = 0.0;
+  float xp[kTreeBatch], xq[kTreeBatch];
+#pragma unroll
+  for (int j = 0; j < kTreeBatch; ++j) {
+    const int e = min(j * kTreeThreads + tid, V - 1);
+    xp[j] = trow[e];
+    xq[j] = drow[e];
+  }
+  for (int e0 = 0; e0 < V; e0 += kStep) {
+    float np[kTreeBatch], nq[kTreeBatch];
+#pragma unroll
+    for (int j = 0; j < kTreeBatch; ++j) {
+      const int e = min(e0 + kStep + j * kTreeThreads + tid, V - 1);
+      np[j] = trow[e];
+      nq[j] = drow[e];
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatch; ++j) {
+      const int e = e0 + j * kTreeThreads + tid;
+      if (e < V) {
+        const double q = prob_t<MODE, kDiv>(xq[j], e, dq, t);
+        const double r = fmax(0.0, prob_t<MODE, kDiv>(xp[j], e, dp, t) - q);
+        pr[e] = r;
+        if (store_q) qb[e] = q;
+        local += r;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatch; ++j) {
+      xp[j] = np[j];
+      xq[j] = nq[j];
+    }
+  }
+  return local;
+}
+
+__device__ double first_reject(const float* trow, const float* drow, const RowStat& dp, const RowStat& dq, double t,
+                               int V, double* pr, double* qb, bool store_q) {
+  if (dp.mode == 2) return first_reject_t<2, false>(trow, drow, dp, dq, t, V, pr, qb, store_q);
+  if (dp.mode == 1) return first_reject_t<1, false>(trow, drow, dp, dq, t, V, pr, qb, store_q);
+  return t == 1.0 ? first_reject_t<0, false>(trow, drow, dp, dq, t, V, pr, qb, store_q)
+                  : first_reject_t<0, true>(trow, drow, dp, dq, t, V, pr, qb, store_q);
+}
+
+// A further rejection at the node: p' = max(0, pr * scale - qb), written back
+// (loads pipelined as in first_reject_t).
+__device__ double next_reject(double* pr, const double* qb, int V, double scale) {
+  constexpr int kStep = kTreeThreads * kTreeBatchD;
+  const int tid = threadIdx.x;
+  double local = 0.0;
+  double pv[kTreeBatchD], qv[kTreeBatchD];
+#pragma unroll
+  for (int j = 0; j < kTreeBatchD; ++j) {
+    const int e = min(j * kTreeThreads + tid, V - 1);
+    pv[j] = pr[e];
+    qv[j] = qb[e];
+  }
+  for (int e0 = 0; e0 < V; e0 += kStep) {
+    double np[kTreeBatchD], nq[kTreeBatchD];
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) {
+      const int e = min(e0 + kStep + j * kTreeThreads + tid, V - 1);
+      np[j] = pr[e];
+      nq[j] = qb[e];
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) {
+      const int e = e0 + j * kTreeThreads + tid;
+      if (e < V) {
+        const double r = fmax(0.0, pv[j] * scale - qv[j]);
+        pr[e] = r;
+        local += r;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) {
+      pv[j] = np[j];
+      qv[j] = nq[j];
+    }
+  }
+  return local;
+}
+
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Values of p' over this wave's segment [s0, s1), 64 entries per step.
+template <int MODE, bool kDiv, bool kStored>
+struct DrawSrc {
+  const float* trow;
+  const double* pr;
+  RowStat d;
+  double t, scale;
+  int V;
+  __device__ __forceinline__ void load(int e, float& x, double& y) const {
+    const int ec = min(e, V - 1);
+    if (kStored)
+      y = pr[ec];
+    else
+      x = trow[ec];
+  }
+  __device__ __forceinline__ double value(int e, float x, double y) const {
+    return kStored ? y * scale : prob_t<MODE, kDiv>(x, e, d, t);
+  }
+};
+
+// Sum of p' over [a, b) by one wave (64 entries per step, kTreeBatchD steps per
+// batch, the next batch's loads issued before the current one is used), and
+// the last positive entry there.
+template <class Src>
+__device__ __forceinline__ double wave_range_sum(const Src& src, int a, int b, int& last_pos) {
+  const int lane = threadIdx.x & 63;
+  double part = 0.0;
+  float x[kTreeBatchD];
+  double y[kTreeBatchD];
+#pragma unroll
+  for (int j = 0; j < kTreeBatchD; ++j) src.load(a + 64 * j + lane, x[j], y[j]);
+  for (int i0 = a; i0 < b; i0 += 64 * kTreeBatchD) {
+    float nx[kTreeBatchD];
+    double ny[kTreeBatchD];
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) src.load(i0 + 64 * (kTreeBatchD + j) + lane, nx[j], ny[j]);
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) {
+      const int e = i0 + 64 * j + lane;
+      if (e < b) {
+        const double v = src.value(e, x[j], y[j]);
+        part += v;
+        if (v > 0.0) last_pos = max(last_pos, e);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatchD; ++j) {
+      x[j] = nx[j];
+      y[j] = ny[j];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  return part;
+}
+
+// The first of 16 wave partials (in sh.d) whose running sum, from base,
+// passes tgt; -1 if none.  *before = the running sum ahead of it.
+__device__ __forceinline__ int first_passing(const TreeShared& sh, double base, double tgt, double* before) {
+  int wx = -1;
+  double run = base;
+  *before = base;
+#pragma unroll
+  for (int q = 0; q < kTreeWaves; ++q) {
+    if (wx < 0 && run + sh.d[q] > tgt) {
+      wx = q;
+      *before = run;
+    }
+    run += sh.d[q];
+  }
+  return wx;
+}
+
+// Inverse CDF over p' with target fraction uf (strict '>': the first entry
+// whose inclusive running sum passes uf * total; when rounding keeps the sum
+// from passing it, the last positive entry of the range being searched).  The
+// vocabulary is narrowed in three steps: 16 segments (one per wave), 16
+// pieces of the segment the CDF passes the target in (one per wave), then the
+// wave of the piece scans it in order.
+template <class Src>
+__device__ int draw(const Src& src, int V, double uf, TreeShared& sh, int* s_found) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int seg = (V + kTreeThreads - 1) / kTreeThreads * 64;  // a multiple of 64; 16 segments cover V
+  int last1 = -1;
+  const double part1 = wave_range_sum(src, w * seg, min(V, w * seg + seg), last1);
+  __syncthreads();
+  if (lane == 0) sh.d[w] = part1;
+  if (tid == 0) *s_found = 0x7fffffff;
+  __syncthreads();
+  double total = 0.0;
+#pragma unroll
+  for (int q = 0; q < kTreeWaves; ++q) total += sh.d[q];
+  const double tgt = uf * total;
+  double before;
+  const int wx = first_passing(sh, 0.0, tgt, &before);
+  const int lastV = tree_max_int(last1, sh);
+  if (wx < 0) return lastV;
+  // pieces of segment wx
+  const int a0 = wx * seg, a1 = min(V, a0 + seg);
+  const int piece = (seg + kTreeWaves - 1) / kTreeWaves;
+  const int p0 = min(a1, a0 + w * piece), p1 = min(a1, p0 + piece);
+  int last2 = -1;
+  const double part2 = wave_range_sum(src, p0, p1, last2);
+  __syncthreads();
+  if (lane == 0) sh.d[w] = part2;
+  __syncthreads();
+  double before2;
+  const int wy = first_passing(sh, before, tgt, &before2);
+  const int lastS = tree_max_int(last2, sh);  // the segment's last positive entry
+  if (wy < 0) return lastS;
+  if (w == wy) {
+    double run = before2;
+    bool done = false;
+    int lastP = -1;
+    for (int i0 = p0; i0 < p1 && !done; i0 += 64) {
+      float x;
+      double y;
+      src.load(i0 + lane, x, y);
+      const int e = i0 + lane;
+      const double v = e < p1 ? src.value(e, x, y) : 0.0;
+      const double incl = wave_incl_scan(v, lane);
+      const unsigned long long hit = __ballot(v > 0.0 && run + incl > tgt);
+      const unsigned long long pos = __ballot(v > 0.0);
+      if (pos != 0ull) lastP = i0 + 63 - __builtin_clzll(pos);
+      if (hit != 0ull) {
+        if (lane == 0) *s_found = i0 + __builtin_ctzll(hit);
+        done = true;
+      }
+      run += __shfl(incl, 63);
+    }
+    if (!done && lane == 0) *s_found = lastP;  // the piece's last positive entry
+  }
+  __syncthreads();
+  return *s_found;
+}
+
+template <int MODE, bool kDiv>
+__device__ int draw_node(bool stored, const float* trow, const double* pr, const RowStat& d, double t, double scale,
+                         int V, double uf, TreeShared& sh, int* s_found) {
+  if (stored) return draw(DrawSrc<MODE, kDiv, true>{trow, pr, d, t, scale, V}, V, uf, sh, s_found);
+  return draw(DrawSrc<MODE, kDiv, false>{trow, pr, d, t, scale, V}, V, uf, sh, s_found);
 }
 
 __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
-    const int32_t* __restrict__ parent, const double* __restrict__ uniforms, int32_t Q, int32_t V, float temperature,
-    int32_t probs, double* __restrict__ resid, int32_t* __restrict__ n_acc, int32_t* __restrict__ path,
-    int32_t* __restrict__ next) {
+    const int32_t* __restrict__ parent, const double* __restrict__ uniforms, int32_t Q, int32_t V, int32_t nslice,
+    float temperature, int32_t probs, double* __restrict__ ws, const SliceStat* __restrict__ stats,
+    int32_t* __restrict__ n_acc, int32_t* __restrict__ path, int32_t* __restrict__ next) {
   __shared__ int s_par[kTreeMaxQ], s_tok[kTreeMaxQ];
+  __shared__ RowStat s_rs[2 * kTreeMaxQ];
   __shared__ TreeShared sh;
-  __shared__ double s_px, s_qx;
   __shared__ int s_found;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int ipt = (V + kTreeThreads - 1) / kTreeThreads;
-  const int v0 = min(V, tid * ipt), v1 = min(V, v0 + ipt);
   const double t = (double)temperature;
-  double* pr = resid + (size_t)b * V;  // p' = pr[v] * scale
+  double* pr = ws + (size_t)b * 2 * V;  // p' = pr[e] * scale once a rejection happened
+  double* qb = pr + V;                  // q_v, stored for a further sibling
+  const SliceStat* st = stats + (size_t)b * 2 * kTreeMaxQ * nslice;
   if (tid < Q) {
     const int p = parent[(size_t)b * Q + tid];
     s_par[tid] = (tid > 0 && p >= 0 && p < tid) ? p : (tid > 0 ? 0 : -1);
     s_tok[tid] = tokens[(size_t)b * Q + tid];
   }
+  merge_rows(st, nslice, Q, Q > 1 ? Q : 0, temperature, probs, s_rs);
   __syncthreads();
   const double* u = uniforms + (size_t)b * Q;
   int v = 0, npath = 0;
+  bool stored = false;  // p' = p_v (false) or pr * scale (true)
   double scale = 1.0;
+  RowStat dp;
   while (true) {
-    // p' = p_v, the target's distribution for the children of v
     const float* trow = target + ((size_t)b * Q + v) * V;
-    const TreeDist dp = tree_dist(trow, v0, v1, temperature, probs, sh);
-    for (int e = v0; e < v1; ++e) pr[e] = tree_val(dp, trow[e], e, t);
-    scale = 1.0;
+    dp = s_rs[v];
+    stored = false;
     int kept = -1;
-    bool has_child = false;
-    for (int c = v + 1; c < Q; ++c) has_child = has_child || s_par[c] == v;
-    if (has_child) {
+    int n_child = 0;
+    for (int c = v + 1; c < Q; ++c) n_child += s_par[c] == v;
+    if (n_child > 0) {
       const float* drow = draft + ((size_t)b * Q + v) * V;
-      const TreeDist dq = tree_dist(drow, v0, v1, temperature, probs, sh);
+      const RowStat dq = s_rs[kTreeMaxQ + v];
       for (int c = v + 1; c < Q; ++c) {
         if (s_par[c] != v) continue;
+        --n_child;  // siblings still to try after c
         const int x = s_tok[c];
         const bool valid = x >= 0 && x < V;
-        __syncthreads();  // this thread's own pr writes are visible to itself; the owner of x reads its own
-        if (valid && x >= v0 && x < v1) {
-          s_px = pr[x] * scale;
-          s_qx = tree_val(dq, drow[x], x, t);
-        }
-        __syncthreads();
-        const double px = s_px, qx = s_qx;
+        // every thread evaluates the test itself (pr entries of other threads
+        // are visible: the last pass ended with a block reduction)
+        const double px = !valid ? 0.0 : stored ? pr[x] * scale : prob1(trow, x, dp, t);
+        const double qx = !valid ? 0.0 : prob1(drow, x, dq, t);
         if (valid && px > 0.0 && u[c - 1] * qx <= px) {
           kept = c;
           break;
         }
         // rejected: p' = max(0, p' - q_v) renormalised (p_v if it vanished)
-        double local = 0.0;
-        for (int e = v0; e < v1; ++e) {
-          const double r = fmax(0.0, pr[e] * scale - tree_val(dq, drow[e], e, t));
-          pr[e] = r;
-          local += r;
+        double local;
+        if (!stored) {
+          local = first_reject(trow, drow, dp, dq, t, V, pr, qb, n_child > 0);
+        } else {
+          local = next_reject(pr, qb, V, scale);
         }
         const double Z = tree_sum(local, sh);
-        if (Z > 0.0) {
-          scale = 1.0 / Z;
-        } else {
-          for (int e = v0; e < v1; ++e) pr[e] = tree_val(dp, trow[e], e, t);
-          scale = 1.0;
-        }
+        stored = Z > 0.0;
+        scale = stored ? 1.0 / Z : 1.0;
       }
     }
     if (kept < 0) break;
     if (tid == 0) path[(size_t)b * (Q - 1) + npath] = kept;
     ++npath;
     v = kept;
-    __syncthreads();  // every thread done with this node's rows before pr is rewritten
+    __syncthreads();  // the node's reads of pr / qb are done before the next node writes them
   }
-  // draw the next token from p' (inverse CDF with u[Q - 1], strict '>')
-  double local = 0.0;
-  int last_pos = -1;
-  for (int e = v0; e < v1; ++e) {
-    const double r = pr[e] * scale;
-    local += r;
-    if (r > 0.0) last_pos = e;
-  }
-  double incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+
+  // Draw the next token from p' with u[Q - 1]; p' entries of every thread are
+  // read, so all its writes must be visible first.
   __syncthreads();
-  if (lane == 63) sh.d[w] = incl;
-  if (tid == 0) s_found = 0x7fffffff;
-  __syncthreads();
-  double off_w = 0.0, total = 0.0;
-#pragma unroll
-  for (int q = 0; q < kTreeWaves; ++q) {
-    if (q < w) off_w += sh.d[q];
-    total += sh.d[q];
-  }
-  const double tgt = u[Q - 1] * total;
-  double run = off_w + (incl - local);
-  for (int e = v0; e < v1; ++e) {
-    const double r = pr[e] * scale;
-    run += r;
-    if (r > 0.0 && run > tgt) {
-      atomicMin(&s_found, e);
-      break;
-    }
-  }
-  const int last = tree_max_int(last_pos, sh);  // (its barriers also order the atomicMin before the read)
+  const float* trow = target + ((size_t)b * Q + v) * V;
+  const double uf = u[Q - 1];
+  int nx;
+  if (dp.mode == 2)
+    nx = draw_node<2, false>(stored, trow, pr, dp, t, scale, V, uf, sh, &s_found);
+  else if (dp.mode == 1)
+    nx = draw_node<1, false>(stored, trow, pr, dp, t, scale, V, uf, sh, &s_found);
+  else if (t == 1.0)
+    nx = draw_node<0, false>(stored, trow, pr, dp, t, scale, V, uf, sh, &s_found);
+  else
+    nx = draw_node<0, true>(stored, trow, pr, dp, t, scale, V, uf, sh, &s_found);
   if (tid == 0) {
     n_acc[b] = npath;
-    // the running sum never passing u * total (rounding): the last positive entry
-    next[b] = s_found != 0x7fffffff ? s_found : last;
+    next[b] = nx;
   }
   for (int i = npath + tid; i < Q - 1; i += kTreeThreads) path[(size_t)b * (Q - 1) + i] = -1;
 }
 
-int32_t tree_accept_max_vocab() { return kTreeThreads * kTreeMaxIpt; }
+int32_t tree_accept_max_vocab() { return kTreeMaxVocab; }
 int32_t tree_accept_max_nodes() { return kTreeMaxQ; }
+
+static size_t tree_rows_bytes(int32_t B, int32_t V) {
+  return ((size_t)B * 2 * V * sizeof(double) + 255) & ~(size_t)255;
+}
 
 size_t tree_accept_ws_bytes(int32_t B, int32_t V) {
   if (B < 1 || V < 1) return 0;
-  return ((size_t)B * V * sizeof(double) + 255) & ~(size_t)255;
+  const size_t nslice = (V + kTreeSlice - 1) / kTreeSlice;
+  return tree_rows_bytes(B, V) + (size_t)B * 2 * kTreeMaxQ * nslice * sizeof(SliceStat);
 }
 
 hipError_t launch_tree_accept(const float* target, const float* draft, const int32_t* tokens, const int32_t* parent,
@@ -261,8 +584,18 @@ hipError_t launch_tree_accept(const float* target, const float* draft, const int
                               int32_t flags, int32_t* n_acc, int32_t* path, int32_t* next, void* ws,
                               hipStream_t stream) {
   const int probs = (flags & TF_ACCEPT_PROBS) != 0;
+  const int nslice = (V + kTreeSlice - 1) / kTreeSlice;
+  SliceStat* stats = (SliceStat*)((char*)ws + tree_rows_bytes(B, V));
+  if (!probs) {
+    // target rows 0 .. Q-1, then draft rows Q .. 2Q-1 (none when Q = 1)
+    const dim3 grid((unsigned)B * nslice, Q > 1 ? 2 * Q : Q);
+    hipLaunchKernelGGL(tree_stats_kernel, grid, dim3(kStatThreads), 0, stream, target, draft, Q, V, nslice,
+                       temperature, stats);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(tree_accept_kernel, dim3(B), dim3(kTreeThreads), 0, stream, target, draft, tokens, parent,
-                     uniforms, Q, V, temperature, probs, (double*)ws, n_acc, path, next);
+                     uniforms, Q, V, nslice, temperature, probs, (double*)ws, stats, n_acc, path, next);
   return hipGetLastError();
 }
 

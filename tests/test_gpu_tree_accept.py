@@ -36,7 +36,7 @@ def draft_tokens(rng, draft, parent, T, V):
 
 
 @pytest.mark.parametrize("T,probs,V", [(1.0, False, 32000), (float(np.float32(0.6)), False, 5000), (0.0, False, 777),
-                                       (1.0, True, 50)])
+                                       (1.0, True, 50), (1.0, False, 65536)])
 def test_tree_accept_matches_oracle(T, probs, V):
     rng = np.random.default_rng(121 + V)
     B, Q = 24, 9
