@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn GB/s & % HBM peak, sparse-draft+verify steps/s at 128K ctx"
 EXTRA_ROWS = 512  # room after every sequence's rows for the rows the three-tier loop appends
 HBM_PEAK_GBPS = 8000.0
+WARM_REPLAYS = 5      # untimed replays of each per-kernel graph
+KERNEL_REPS = 20      # timed replays of each per-kernel graph
+COPY_REPS = 10        # timed 1 GiB device-to-device copies (the secondary peak)
+SMALL_REPS = 8        # calls per graph for the once-per-step calls (accept), so the graph launch is amortised
 CSRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc")
 VERIFY_SRCS = [os.path.join(CSRC, f) for f in ("attn.hip", "api.hip", "tf_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_traffic.txt")
@@ -47,8 +51,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers the CPU oracle baseline times")
     ap.add_argument("--ck-dtype", default="kv", choices=["kv", "fp32"])
     ap.add_argument("--no-three-tier", action="store_true", help="skip the three-tier step loop")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 1 GiB device-to-device copy (a kernel of known traffic for HBM counters)")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the per-call timing of sparse verification, tree verification / accept and appends")
     return ap.parse_args()
 
 
@@ -218,9 +222,12 @@ def main():
         torch.cuda.synchronize()
         # timed region 1: graph replays (the reported value)
         t0 = time.perf_counter()
+        step_t = []
         for _ in range(args.steps):
+            ts = time.perf_counter()
             graph.replay()
             readback()
+            step_t.append(time.perf_counter() - ts)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         # timed region 2: the same steps launched eagerly, HIP events around
@@ -236,31 +243,44 @@ def main():
 
     # ---- per-kernel breakdown: one graph per kernel kind, one launch per layer
     names = ["chunk_refresh", "score", "topk", "sparse", "stream", "verify", "accept"]
-    us = {}
+    us, dist = {}, {}
     with torch.cuda.stream(stream):
         for n in names:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 if n == "accept":
-                    accept_call()
+                    for _ in range(SMALL_REPS):
+                        accept_call()
                 else:
                     for x in L:
                         dict(layer_calls(x))[n]()
-            g.replay()
-            stream.synchronize()
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            a_.record(stream)
-            for _ in range(reps):
+            for _ in range(WARM_REPLAYS):
                 g.replay()
-            b_.record(stream)
             stream.synchronize()
-            us[n] = a_.elapsed_time(b_) * 1e3 / (reps * (1 if n == "accept" else layers))
-        if args.copy_calibration:
-            src = torch.empty(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB read + 1 GiB written
-            dst = torch.empty_like(src)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(KERNEL_REPS + 1)]
+            evs[0].record(stream)
+            for r in range(KERNEL_REPS):
+                g.replay()
+                evs[r + 1].record(stream)
+            stream.synchronize()
+            per = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 for r in range(KERNEL_REPS)])
+            per /= SMALL_REPS if n == "accept" else layers      # us per call, one value per replay
+            us[n] = float(per.mean())
+            dist[n] = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+                       "p90": float(np.percentile(per, 90))}
+        # secondary peak: a 1 GiB device-to-device copy (1 GiB read + 1 GiB written)
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
             dst.copy_(src)
-            stream.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(COPY_REPS):
+            dst.copy_(src)
+        c1.record(stream)
+        stream.synchronize()
+        copy_gbps = 2 * src.numel() * src.element_size() * COPY_REPS / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
     verify_avg_s = us["verify"] * 1e-6
 
     # ---- algorithmic bytes --------------------------------------------------
@@ -278,8 +298,9 @@ def main():
         "verify": Hkv * tokens_total * 2 * row + B * Hq * Q * (row + d * 4 + 4),
         "accept": B * (2 * gamma + 1) * vocab * 4,
     }
-    kernels = {n: {"us": round(us[n], 2), "GB_s": round(by[n] / (us[n] * 1e-6) / 1e9, 1),
-                   "bytes": int(by[n])} for n in names}
+    kernels = {n: {"us": round(us[n], 2), "us_median": round(dist[n]["median"], 2),
+                   "us_p10": round(dist[n]["p10"], 2), "us_p90": round(dist[n]["p90"], 2),
+                   "GB_s": round(by[n] / (us[n] * 1e-6) / 1e9, 1), "bytes": int(by[n])} for n in names}
     step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
     verify_bytes = by["verify"]
     achieved = verify_bytes / verify_avg_s / 1e9
@@ -294,6 +315,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "step_ms": {"median": round(float(np.median(step_t)) * 1e3, 3),
+                    "p10": round(float(np.percentile(step_t, 10)) * 1e3, 3),
+                    "p90": round(float(np.percentile(step_t, 90)) * 1e3, 3)},
         "launch": "HIP graph of the whole step, replayed; n_accepted/next_token read back each step",
         "eager_steps_per_s": round(args.steps / elapsed_eager, 3),
         "higher_is_better": True,
@@ -313,16 +337,26 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(verify_bytes),
                      "avg_launch_us": round(verify_avg_s * 1e6, 2),
-                     "timing": "HIP events on the launch stream around 5 replays of a graph of the step's "
-                               "verify launches (one per layer, back to back)",
-                     "eager_avg_launch_us": round(verify_eager_avg_s * 1e6, 2)},
+                     "timing": f"HIP events on the launch stream around each of {KERNEL_REPS} replays of a graph "
+                               "of the step's verify launches (one per layer, back to back); mean over replays",
+                     "eager_avg_launch_us": round(verify_eager_avg_s * 1e6, 2),
+                     "copy_GB_s": round(copy_gbps, 1),
+                     "frac_of_copy": round(achieved / copy_gbps, 4)},
         "kernels": kernels,
-        "kernels_timing": "per kind: a HIP graph of its launches for every layer, replayed 5x between events",
+        "kernels_timing": f"per kind: a HIP graph of its launches for every layer ({SMALL_REPS} calls for the "
+                          f"accept), {WARM_REPLAYS} warm replays, "
+                          f"then {KERNEL_REPS} replays each between HIP events; us = mean per launch, "
+                          "median / p10 / p90 over the replays",
         "sparse_draft_pass_us": round(us["score"] + us["topk"] + us["sparse"], 2),
         "prefill_chunk_keys": {"ms_all_layers": round(prefill_ms, 3),
                                "GB_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},
         "setup_s": round(time.perf_counter() - t_setup, 1),
     }
+    if not args.no_next_rows:
+        result["next_rows"] = next_rows_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, idx, acc_in, dev, stream)
+        result["next_rows_timing"] = (f"per call: a HIP graph of one call per layer ({SMALL_REPS} in all for the "
+                                      f"tree accept), {WARM_REPLAYS} warm replays, then {KERNEL_REPS} replays "
+                                      "each between HIP events; us per call")
     if not args.no_three_tier and B == 1:
         result["three_tier"] = three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, dev,
                                               args.steps, args.warmup, stream)
@@ -330,6 +364,119 @@ def main():
         result["cpu_baseline"] = cpu_baseline(L[:max(1, min(args.cpu_layers, layers))], lens, Hq, Hkv, d, cs, k, S,
                                               Wn, Q, layers, acc_in, tdt)
     print(json.dumps(result), flush=True)
+
+
+def time_graph(fn, stream, per_replay):
+    """Mean / median / p10 / p90 microseconds per call of fn (a function that
+    enqueues per_replay calls), captured once as a HIP graph and replayed
+    between HIP events on the launch stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    for _ in range(WARM_REPLAYS):
+        g.replay()
+    stream.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(KERNEL_REPS + 1)]
+    evs[0].record(stream)
+    for r in range(KERNEL_REPS):
+        g.replay()
+        evs[r + 1].record(stream)
+    stream.synchronize()
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 for r in range(KERNEL_REPS)]) / per_replay
+    return {"us": round(float(per.mean()), 2), "us_median": round(float(np.median(per)), 2),
+            "us_p10": round(float(np.percentile(per, 10)), 2), "us_p90": round(float(np.percentile(per, 90)), 2)}
+
+
+def next_rows_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, idx, acc, dev, stream):
+    """The calls the three-tier loop adds, each timed on its own over every
+    layer (graph of one launch per layer, like the step's kernels):
+    sparse verification of gamma1 + 1 = 3 rows over the selected chunks below
+    a 64-row causal tail (Force 2 verifying the drafter), verification over a
+    7-node candidate tree, accept over that tree (V = 32000), appending
+    gamma + 1 rows to the full cache and one row to the streaming ring, the
+    length commit and the tree masks."""
+    import torch
+    import hierarchical_speculative_attention_amd as tf
+    B = len(lens)
+    layers = len(L)
+    row = d * 2
+    g1, tail = 2, 64
+    Qt = gamma + 1
+    out = {}
+    with torch.cuda.stream(stream):
+        # sparse verification (the selection of the step's last layer serves every layer)
+        q3 = [x.qv[:, :, :g1 + 1].contiguous() for x in L]
+        ws = tf.workspace(tf.sparse_verify_attn_workspace_size(B, Hq, Hkv, g1 + 1, k, cs, tail), dev)
+        o3 = torch.empty((B, Hq, g1 + 1, d), dtype=torch.float32, device=dev)
+        l3 = torch.empty((B, Hq, g1 + 1), dtype=torch.float32, device=dev)
+        r = time_graph(lambda: [tf.sparse_verify_attn(q, x.K, x.V, x.kv, idx, cs, tail, out=o3, lse=l3, ws=ws,
+                                                      stream=stream) for q, x in zip(q3, L)], stream, layers)
+        sel = idx.cpu().numpy()
+        rows = 0
+        for b, n in enumerate(lens):
+            lo = max(0, n - tail)
+            for g in range(Hkv):
+                for c in sel[b, g]:
+                    if c >= 0:
+                        rows += max(0, min(lo, (int(c) + 1) * cs) - int(c) * cs)
+                rows += n - lo
+        by = rows * 2 * row + B * Hkv * k * 4 + B * Hq * (g1 + 1) * (row + d * 4 + 4)
+        out["sparse_verify"] = dict(r, bytes=int(by), GB_s=round(by / (r["us"] * 1e-6) / 1e9, 1), bound="hbm",
+                                    shape=f"{g1 + 1} rows x {Hq} heads over {k} chunks x {cs} + a {tail}-row tail")
+        # verification over a candidate tree
+        parent = torch.tensor([[-1, 0, 0, 1, 1, 2, 2][:Qt] + [-1] * max(0, Qt - 7)] * B, dtype=torch.int32,
+                              device=dev)
+        tm = tf.tree_masks(parent, stream=stream)
+        ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Qt, max(lens)), dev)
+        ov = torch.empty((B, Hq, Qt, d), dtype=torch.float32, device=dev)
+        lv = torch.empty((B, Hq, Qt), dtype=torch.float32, device=dev)
+        r = time_graph(lambda: [tf.verify_tree_attn(x.qv, x.K, x.V, x.kv, tm, out=ov, lse=lv, ws=ws_v,
+                                                    stream=stream) for x in L], stream, layers)
+        by = Hkv * sum(lens) * 2 * row + B * Hq * Qt * (row + d * 4 + 4) + B * Qt * 8
+        out["verify_tree"] = dict(r, bytes=int(by), GB_s=round(by / (r["us"] * 1e-6) / 1e9, 1), bound="hbm",
+                                  shape=f"{Qt}-node tree (parents {parent[0].tolist()}) x {Hq} heads over the full cache")
+        # accept over the tree
+        tgt = torch.from_numpy(acc.target).to(dev)
+        drf = torch.from_numpy(acc.draft).to(dev)
+        V = tgt.shape[-1]
+        drf_t = torch.cat([drf, drf[:, :1]], 1)[:, :Qt].contiguous()
+        tok = torch.from_numpy(acc.tokens).to(dev)
+        tok_t = torch.cat([tok, tok[:, :1]], 1)[:, :Qt].contiguous()
+        uni = torch.from_numpy(acc.uniforms).to(dev)[:, :Qt].contiguous()
+        ws_t = tf.workspace(tf.tree_accept_workspace_size(B, V), dev)
+        r = time_graph(lambda: [tf.tree_accept(tgt, drf_t, tok_t, parent, uni, 1.0, ws=ws_t, stream=stream)
+                                for _ in range(SMALL_REPS)], stream, SMALL_REPS)
+        by = B * 2 * Qt * V * 4
+        out["tree_accept"] = dict(r, bytes=int(by), GB_s=round(by / (r["us"] * 1e-6) / 1e9, 1), bound="latency",
+                                  shape=f"{Qt}-node tree, vocabulary {V}, fp64 inside")
+        # cache maintenance: rows written past the committed lengths, which stay unchanged
+        g = torch.Generator(device=dev).manual_seed(11)
+        kn = torch.randn((B, Hkv, Qt, d), generator=g, device=dev).to(L[0].K.dtype)
+        vn = torch.randn((B, Hkv, Qt, d), generator=g, device=dev).to(L[0].K.dtype)
+        st = torch.empty(B, dtype=torch.int32, device=dev)
+        r = time_graph(lambda: [tf.append_kv(kn, vn, x.K, x.V, x.kv, status=st, stream=stream) for x in L], stream,
+                       layers)
+        by = 2 * 2 * B * Hkv * Qt * row
+        out["append_full"] = dict(r, bytes=int(by), GB_s=round(by / (r["us"] * 1e-6) / 1e9, 1), bound="latency",
+                                  shape=f"{Qt} rows x {Hkv} heads into the full cache")
+        k1, v1 = kn[:, :, :1].contiguous(), vn[:, :, :1].contiguous()
+        r = time_graph(lambda: [tf.append_kv(k1, v1, x.Ks, x.Vs, x.sd, ring=True, n_sink=S, window=Wn, reserve=1,
+                                             status=st, stream=stream) for x in L], stream, layers)
+        by = 2 * 2 * B * Hkv * row
+        out["append_ring"] = dict(r, bytes=int(by), GB_s=round(by / (r["us"] * 1e-6) / 1e9, 1), bound="latency",
+                                  shape=f"1 row x {Hkv} heads into the {S} + {Wn} ring")
+        ok = bool((st == 0).all().item())
+        lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+        na = torch.zeros(B, dtype=torch.int32, device=dev)
+        r = time_graph(lambda: [tf.commit_length(lens_t, 0, 0, na, stream=stream) for _ in range(layers)], stream,
+                       layers)
+        out["commit_length"] = dict(r, bound="latency", shape=f"{B} sequence length(s)")
+        r = time_graph(lambda: [tf.tree_masks(parent, stream=stream) for _ in range(layers)], stream, layers)
+        out["tree_masks"] = dict(r, bound="latency", shape=f"{B} tree(s) of {Qt} nodes")
+    if not ok:
+        raise RuntimeError("append_kv reported a status other than TF_APPEND_OK")
+    return out
 
 
 def three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, dev, steps, warmup, stream):
@@ -396,6 +543,17 @@ def three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, 
             "logits": "synthetic: p ~ N(0,2), q = p + N(0,0.5), r = q + N(0,0.5)"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_in, tdt):
     """The fp64 oracle timed on this host over a bounded sample of the step:
     the given layers (every head of every sequence) plus one accept, scaled to
@@ -450,7 +608,7 @@ def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_i
     nl = len(sample_layers)
     t_step = t_layers / nl * layers + t_acc
     return {"value": round(1.0 / t_step, 6), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "sample": f"fp64 numpy oracle on {nl} of the {layers} layers (all {Hkv} KV heads x {Hq} query heads, "
                       f"{len(lens)} sequence(s)) + 1 accept, {t_layers + t_acc:.1f} s timed, scaled to "
                       f"{layers} layers ({t_layers / nl:.2f} s per layer); chunk-key prefill untimed"}

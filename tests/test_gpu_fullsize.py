@@ -120,7 +120,7 @@ def test_llama2_7b_128k_layer():
     run_full("llama2-7b-128k-1layer", Q=7, budget=4096, samples=[(0, 0), (0, 17), (0, 31)])
 
 
-@pytest.mark.parametrize("budget,gamma", [(2048, 4), (4096, 6), (4096, 8), (2048, 8)])
+@pytest.mark.parametrize("budget,gamma", [(2048, 4), (2048, 6), (2048, 8), (4096, 4), (4096, 6), (4096, 8)])
 def test_ragged_batch(budget, gamma):
     run_full("ragged-b8-16k-128k", Q=gamma + 1, budget=budget, samples=[(0, 3), (3, 30), (7, 12)])
 
