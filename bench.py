@@ -91,7 +91,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is not sharded "
-                                   "across GPUs (see DESIGN.md for how it would shard)",
+                                   "across GPUs (it would shard by KV head: every call is independent "
+                                   "per sequence and KV head)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
