@@ -109,3 +109,33 @@ def test_tree_accept_is_lossless_on_gpu():
         nz = exp > 0
         stat = ((counts[nz] - exp[nz]) ** 2 / exp[nz]).sum()
         assert stat < scipy.stats.chi2.ppf(1 - 1e-3, nz.sum() - 1), stat
+
+
+@pytest.mark.parametrize("V", [1, 63, 64, 65, 1025, 2049, 4097])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tree_accept_edge_shapes(V, T):
+    """Vocabularies at the draw's segment and the statistics' slice
+    boundaries, a single node (a pure draw from p_0), two nodes, and greedy
+    rows full of tied maxima (ties go to the lowest index)."""
+    rng = np.random.default_rng(125 + V + int(T))
+    B = 6
+    for Q in (1, 2, 5):
+        if T == 0.0:
+            target = rng.integers(0, 3, (B, Q, V)).astype(np.float32)   # many tied maxima
+            draft = rng.integers(0, 3, (B, Q, V)).astype(np.float32)
+        else:
+            target = rng.normal(0, 2, (B, Q, V)).astype(np.float32)
+            draft = (target + rng.normal(0, 0.8, (B, Q, V))).astype(np.float32)
+        parents = [random_tree(rng, Q) for _ in range(B)]
+        tokens = np.array([draft_tokens(rng, draft[b], parents[b], T, V) for b in range(B)], np.int32)
+        u = synth.open_uniforms(rng, (B, Q))
+        n, path, nxt = tf.tree_accept(d(target), d(draft), d(tokens), d(np.array(parents, np.int32)), d(u), T)
+        torch.cuda.synchronize()
+        n, path, nxt = n.cpu().numpy(), path.cpu().numpy(), nxt.cpu().numpy()
+        for b in range(B):
+            rp, rx, margin = oracle.tree_accept(target[b], draft[b], tokens[b], parents[b], u[b], T)
+            if margin < 1e-12:
+                continue
+            assert int(n[b]) == len(rp) and int(nxt[b]) == rx, (Q, b)
+            if Q > 1:
+                assert list(path[b, :n[b]]) == rp and np.all(path[b, n[b]:] == -1), (Q, b)
