@@ -96,13 +96,13 @@ hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs
 }
 
 // ---------------------------------------------------------------------------
-// a2: grid (ceil(c_max / (64 * kCPL)), H, B), 256 threads.  Each wave scores
-// 16 * kCPL consecutive chunks; its load instruction i covers chunks
+// a2: grid (ceil(c_max / (16 * kCPL)), H, B), 256 threads.  Each wave scores
+// 4 * kCPL consecutive chunks; its load instruction i covers chunks
 // 4 i .. 4 i + 3 of its range, 1 KB of contiguous memory (16 lanes per
 // 256-byte key).  The 16 partial dot products of a key are reduced across
 // its 16 lanes.
 // ---------------------------------------------------------------------------
-constexpr int kCPL = 8;  // chunks per lane group, loads in flight together
+constexpr int kCPL = 4;  // keys per lane group (loads in flight together); 8 and 16 measured slower
 
 template <int CK_DT>
 __global__ __launch_bounds__(256) void score_kernel(
