@@ -299,9 +299,16 @@ def main():
         "verify": Hkv * tokens_total * 2 * row + B * Hq * Q * (row + d * 4 + 4),
         "accept": B * (2 * gamma + 1) * vocab * 4,
     }
-    kernels = {n: {"us": round(us[n], 2), "us_median": round(dist[n]["median"], 2),
-                   "us_p10": round(dist[n]["p10"], 2), "us_p90": round(dist[n]["p90"], 2),
-                   "GB_s": round(by[n] / (us[n] * 1e-6) / 1e9, 1), "bytes": int(by[n])} for n in names}
+    bound = {"chunk_refresh": "latency", "score": "hbm", "topk": "latency", "sparse": "hbm", "stream": "latency",
+             "verify": "hbm", "accept": "latency"}
+    kernels = {}
+    for n in names:
+        gbs = by[n] / (us[n] * 1e-6) / 1e9
+        kernels[n] = {"us": round(us[n], 2), "us_median": round(dist[n]["median"], 2),
+                      "us_p10": round(dist[n]["p10"], 2), "us_p90": round(dist[n]["p90"], 2),
+                      "GB_s": round(gbs, 1), "bytes": int(by[n]), "bound": bound[n]}
+        if bound[n] == "hbm":
+            kernels[n]["frac"] = round(gbs / HBM_PEAK_GBPS, 4)
     step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
     verify_bytes = by["verify"]
     achieved = verify_bytes / verify_avg_s / 1e9
@@ -361,6 +368,9 @@ def main():
     if not args.no_three_tier and B == 1:
         result["three_tier"] = three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, dev,
                                               args.steps, args.warmup, stream)
+    if not args.no_cpu_baseline and not args.no_next_rows and B == 1:
+        result["next_rows_cpu_baseline"] = next_rows_cpu_baseline(L[0], lens[0], Hq, Hkv, d, cs, idx, gamma, acc_in,
+                                                                  tdt)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(L[:max(1, min(args.cpu_layers, layers))], lens, Hq, Hkv, d, cs, k, S,
                                               Wn, Q, layers, acc_in, tdt)
@@ -477,6 +487,9 @@ def next_rows_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, idx, acc, dev, strea
         out["tree_masks"] = dict(r, bound="latency", shape=f"{B} tree(s) of {Qt} nodes")
     if not ok:
         raise RuntimeError("append_kv reported a status other than TF_APPEND_OK")
+    for v in out.values():
+        if v.get("bound") == "hbm":
+            v["frac"] = round(v["GB_s"] / HBM_PEAK_GBPS, 4)
     return out
 
 
@@ -542,6 +555,51 @@ def three_tier_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, vocab, tdt, ck_dt, 
             "force2": f"sparse verification of gamma1 + 1 rows over {k} chunks x {cs} rows + a 64-row causal tail",
             "launch": "eager launches; the host reads back 4 bytes per Force 2 round and per step",
             "logits": "synthetic: p ~ N(0,2), q = p + N(0,0.5), r = q + N(0,0.5)"}
+
+
+def next_rows_cpu_baseline(x, n, Hq, Hkv, d, cs, idx, gamma, acc, tdt):
+    """The fp64 oracle's versions of the NEXT-row calls, timed on this host on
+    a bounded sample and scaled to one call: sparse verification on 4 of the
+    KV heads, tree verification on 2 (its row lists are built in Python),
+    one tree accept.  Widening the cache to fp64 is not timed."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    to_bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    dt = "bf16" if tdt == torch.bfloat16 else "fp16"
+    G = Hq // Hkv
+    Kb, Vb, qv = to_bits(x.K), to_bits(x.V), to_bits(x.qv)
+    base, cap = int(x.kv.seq_base[0].item()), int(x.kv.seq_cap[0].item())
+    sel = idx.cpu().numpy()
+    parent = [-1, 0, 0, 1, 1, 2, 2][:gamma + 1] + [-1] * max(0, gamma + 1 - 7)
+    masks = oracle.tree_masks(parent)
+    out = {}
+    for name, heads in (("sparse_verify", 4), ("verify_tree", 2)):
+        t = 0.0
+        for g in range(heads):
+            off = base + g * cap * d
+            K = oracle.widen(Kb[off:off + n * d].reshape(n, d), dt)
+            V = oracle.widen(Vb[off:off + n * d].reshape(n, d), dt)
+            for j in range(G):
+                qs = oracle.widen(qv[0, g * G + j], dt)
+                t0 = time.perf_counter()
+                if name == "sparse_verify":
+                    oracle.sparse_verify_attn(qs[:3], K, V, n, sel[0, g].tolist(), cs, 64)
+                else:
+                    oracle.verify_tree_attn(qs, K, V, n, masks)
+                t += time.perf_counter() - t0
+        out[name] = {"us": round(t / heads * Hkv * 1e6, 1), "sample": f"{heads} of {Hkv} KV heads, scaled"}
+    Qt = gamma + 1
+    drf = np.concatenate([acc.draft, acc.draft[:, :1]], 1)[0, :Qt]
+    tok = np.concatenate([acc.tokens, acc.tokens[:, :1]], 1)[0, :Qt]
+    t0 = time.perf_counter()
+    oracle.tree_accept(acc.target[0], drf, tok, parent, acc.uniforms[0, :Qt], 1.0)
+    out["tree_accept"] = {"us": round((time.perf_counter() - t0) * 1e6, 1), "sample": "one call"}
+    return {"calls": out, "kind": "oracle", "cores": int(threads), "unit": "us per call"}
 
 
 def cpu_model():
