@@ -61,6 +61,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxSparseTpw = kSparseMaxTpw;      // virtual tokens per sparse workgroup (host-capped)
 constexpr int kMaxSparseIdx = kMaxSparseTpw + 2;  // chunk slots one sparse workgroup can touch
+constexpr int kMaxFlatSeqs = 1024;  // ragged verification batches up to this size use the flat grid
+constexpr int kFlatMaxWgs = 2048;   // flat grid: workgroups (each takes every 2048th item)
 
 // Sequence geometry of one (b) for a mode: virtual length and what a
 // virtual token maps to.
@@ -363,25 +365,20 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   }
 }
 
-// One query tile fits two waves per SIMD (<= 256 registers, no spills);
-// more query tiles run one wave per SIMD.
+// One work item: split `split` of KV head hk of sequence b, by the whole
+// workgroup (the LDS arrays are the kernel's).
 template <int DT, int MODE, int NQT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
-void attn_kernel(const AttnArgs a) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const int hk, const int split, int* s_idx,
+                                          unsigned char* s_stage, float (*s_m)[16], float (*s_l)[16]) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
-  __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
-  __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
-  __shared__ float s_m[4][16];
-  __shared__ float s_l[4][16];
   float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int v0 = split * a.tpw;
 
   // Loads that need only the arguments (chunk slots, query rows) are issued
@@ -583,6 +580,73 @@ void attn_kernel(const AttnArgs a) {
   }
 }
 
+// Items of a ragged batch: sequence b has Hkv * max(1, ceil(L_b / tpw)) of
+// them (L_b its virtual length), head-major then split; s_pre[b] = the items
+// of sequences 0 .. b-1.  Computed by wave 0 from the device-resident lengths.
+template <int MODE>
+__device__ __forceinline__ void flat_prefix(const AttnArgs& a, int* s_pre) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  int carry = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    int items = 0;
+    if (b < a.B) {
+      SeqDesc sd;
+      sd.base = 0;
+      sd.cap = a.seq_cap[b];
+      sd.len = a.seq_len[b];
+      const Geo g = make_geo<MODE>(a, sd);
+      items = a.Hkv * max(1, (g.L + a.tpw - 1) / a.tpw);
+    }
+    int incl = items;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (b < a.B) s_pre[b + 1] = carry + incl;
+    carry += __shfl(incl, 63);
+  }
+  if (lane == 0) s_pre[0] = 0;
+}
+
+// One query tile fits two waves per SIMD (<= 256 registers, no spills);
+// more query tiles run one wave per SIMD.  Either one work item per
+// workgroup (grid = splits x KV heads x sequences), or, for the verification
+// of a ragged batch (FLAT), a one-dimensional grid whose workgroups take
+// items i, i + gridDim.x, ... of the batch's actual items: with a grid sized
+// for the longest sequence, the items of short sequences would leave most
+// workgroups empty and, since workgroups go to the XCDs in index order, load
+// the XCDs unevenly.
+template <int DT, int MODE, int NQT, bool FLAT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
+void attn_kernel(const AttnArgs a) {
+  constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
+  __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
+  __shared__ float s_m[4][16];
+  __shared__ float s_l[4][16];
+  __shared__ int s_pre[FLAT ? kMaxFlatSeqs + 1 : 1];
+  if (FLAT) {
+    flat_prefix<MODE>(a, s_pre);
+    __syncthreads();
+    const int total = s_pre[a.B];
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+      int lo = 0, hi = a.B;  // the sequence: largest b with s_pre[b] <= item
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pre[mid] <= item) lo = mid; else hi = mid;
+      }
+      const int per = (s_pre[lo + 1] - s_pre[lo]) / a.Hkv;  // splits of sequence lo
+      const int r = item - s_pre[lo];
+      attn_item<DT, MODE, NQT>(a, lo, r / per, r % per, s_idx, s_stage, s_m, s_l);
+    }
+  } else {
+    attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, s_idx, s_stage, s_m, s_l);
+  }
+}
+
 // Merge of the split partials of every (sequence, KV head, query row) whose
 // sequence needed more than one split: one wave per row, two dims per lane,
 // splits in order.  Runs as its own launch so that no device-wide fence is
@@ -694,21 +758,39 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
   return p;
 }
 
-template <int DT, int MODE>
-static hipError_t launch_nqt(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(a.nsplit, a.Hkv, a.B), block(kThreads);
+template <int DT, int MODE, bool FLAT>
+static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.nsplit, a.Hkv, a.B), block(kThreads);
+  if (FLAT) {
+    const long most = (long)a.B * a.Hkv * a.nsplit;  // items when every sequence is as long as the longest
+    grid = dim3((unsigned)min(most, (long)kFlatMaxWgs), 1, 1);
+  }
   const int nqt = (a.rows + 15) / 16;
   switch (nqt) {
-    case 1: hipLaunchKernelGGL((attn_kernel<DT, MODE, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<DT, MODE, 2>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((attn_kernel<DT, MODE, 3>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<DT, MODE, 4>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_kernel<DT, MODE, 1, FLAT>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<DT, MODE, 2, FLAT>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((attn_kernel<DT, MODE, 3, FLAT>), grid, block, 0, stream, a); break;
+    case 4:
+      if constexpr (FLAT) return hipErrorInvalidValue;  // not launched flat
+      else hipLaunchKernelGGL((attn_kernel<DT, MODE, 4, FLAT>), grid, block, 0, stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL((combine_kernel<MODE>), dim3(a.rows, a.Hkv, a.B), dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+// Verification of a ragged batch takes the flat grid; everything else one
+// item per workgroup.
+template <int DT, int MODE>
+static hipError_t launch_nqt(const AttnArgs& a, hipStream_t stream) {
+  if constexpr (MODE == kVerify || MODE == kVerifyTree) {
+    // (four query tiles keep one item per workgroup: the item loop would spill there)
+    if (a.B > 1 && a.B <= kMaxFlatSeqs && a.rows <= 48) return launch_tiles<DT, MODE, true>(a, stream);
+  }
+  return launch_tiles<DT, MODE, false>(a, stream);
 }
 
 template <int DT>
