@@ -365,6 +365,158 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   }
 }
 
+// Verification with 4 query tiles, rows split over the waves: wave w owns
+// query tile w over the item's whole token range and holds the register state
+// of one tile (190 registers: two waves per SIMD; four tiles in one wave took
+// 500 registers, one wave per SIMD, and copied the accumulators between
+// register files every tile).  Measured against all tiles in every wave: 4
+// tiles 252 -> 239 us, 3 tiles equal, 2 tiles 349 -> 366 us (the tile's
+// V-operand products are repeated by every owning wave), so only 4 tiles take
+// this path.  Each 32-token K/V tile is fetched by all four
+// waves together, 16 rows each (1 KB per instruction), kRowRing tiles in
+// flight per workgroup, staged in two shared slabs and consumed after a
+// barrier by every owning wave.  A slab is rewritten two tiles later, after
+// the barrier that follows its last reads.
+constexpr int kRowRing = 4;
+
+template <int DT, int MODE, int NQT>
+__device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, const int hk, const int split,
+                                               unsigned char* s_stage, float (*s_m)[16], float (*s_l)[16]) {
+  using M = MT<DT>;
+  using V8 = typename M::V8;
+  using S = typename M::S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int lq = lane & 15, lg = lane >> 4;
+  const bool owner = w < NQT;  // (with fewer query tiles than waves, the rest would only fetch)
+  const int qt = owner ? w : 0;
+  const int v0 = split * a.tpw;
+  const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
+  const int row = qt * 16 + lq;
+  V8 qreg[1][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (owner && row < a.rows) x = *(const u32x4*)(a.q + (qrow0 + row) * kHeadDim + 32 * s + 8 * lg);
+    qreg[0][s] = __builtin_bit_cast(V8, x);
+  }
+  uint64_t tm[1];
+  tm[0] = (MODE == kVerifyTree && owner && row < a.rows) ? a.tmask[(size_t)b * a.Qn + row % a.Qn] : 0ull;
+
+  const SeqDesc sd = load_seq(a, b);
+  const Geo geo = make_geo<MODE>(a, sd);
+  const int tbase = geo.n - a.Qn;  // tree: cache row of node 0
+  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+  if (split >= nsp) return;
+  const int v1 = min(geo.L, v0 + a.tpw);
+  const size_t base = (size_t)sd.base + (size_t)hk * (size_t)geo.cap * kHeadDim;
+  const uint16_t* __restrict__ Kb = a.K + base;
+  const uint16_t* __restrict__ Vb = a.V + base;
+
+  int lim[1];
+  lim[0] = (MODE == kVerify) ? geo.n - a.Qn + (row % a.Qn) : 0x7fffffff;
+  const int lim_min = (MODE == kVerify) ? geo.n - a.Qn : 0x7fffffff;
+  V8 sel[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[h][e] = (S)((8 * lg + e == 16 * h + lq) ? 1.0f : 0.0f);
+  f32x4 acc[1][8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) acc[0][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[1] = {kNegInf}, l_run[1] = {0.f};
+  const float c2 = a.scale_log2;
+
+  // this wave's part of a tile: slab rows 16 w .. 16 w + 15 (K rows 0-31, then V rows 0-31)
+  const uint16_t* src = w >= 2 ? Vb : Kb;
+  const int rbase = 16 * (w & 1);  // first tile row this wave fetches
+  auto fetch = [&](u32x4 (&r)[4], int t0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // rows that hold nothing read row 0 (in bounds) and are masked
+      const int rv = map_row<MODE>(a, geo, t0 + rbase + 4 * i + (lane >> 4), v1, nullptr, 0);
+      r[i] = __builtin_nontemporal_load((const u32x4*)(src + (size_t)(rv < 0 ? 0 : rv) * kHeadDim + 8 * (lane & 15)));
+    }
+  };
+  auto stage = [&](const u32x4 (&r)[4], unsigned char* slab) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(u32x4*)(slab + (16 * w + 4 * i + (lane >> 4)) * kPitch + 16 * (lane & 15)) = r[i];
+  };
+  // (an item with no rows fetches nothing: the sequence may have no row 0)
+  const int ntiles = v1 > v0 ? (v1 - v0 + kTile - 1) / kTile : 0;
+  u32x4 R[kRowRing][4];
+  if (ntiles > 0) {
+#pragma unroll
+    for (int j = 0; j < kRowRing; ++j) fetch(R[j], v0 + kTile * j);
+  }
+  for (int i0 = 0; i0 < ntiles; i0 += kRowRing) {
+#pragma unroll
+    for (int j = 0; j < kRowRing; ++j) {
+      const int i = i0 + j;
+      if (i >= ntiles) break;
+      const int t = v0 + kTile * i;
+      unsigned char* slab = s_stage + (j & 1) * kStageBytes;  // i and j have the same parity
+      stage(R[j], slab);
+      fetch(R[j], t + kTile * kRowRing);
+      const unsigned mask =
+          (unsigned)(__ballot(map_row<MODE>(a, geo, t + (lane & 31), v1, nullptr, 0) >= 0) & 0xFFFFFFFFull);
+      __syncthreads();
+      if (owner) {
+        __builtin_amdgcn_sched_barrier(0);
+        process_tile<DT, MODE, 1>(SlabSource<DT>{slab + lq * kPitch + 16 * lg}, mask, t, qreg, sel, lim, lim_min, tm,
+                                  tbase, acc, m_run, l_run, c2, lq, lg);
+      }
+    }
+  }
+  __syncthreads();  // every slab consumed: the results reuse them
+
+  // each owning wave's rows are complete for this split
+  float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
+  float lsum = l_run[0];
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (owner) {
+    if (lg == 0) {
+      s_m[w][lq] = m_run[0];
+      s_l[w][lq] = lsum;
+    }
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) *(f32x4*)&s_o[w][lq][16 * bb + 4 * lg] = acc[0][bb];
+  }
+  __syncthreads();
+  const size_t bh = (size_t)b * a.Hkv + hk;
+  const int q = tid >> 4;          // 0..15
+  const int dc = (tid & 15) * 8;   // 8 dims per thread
+#pragma unroll
+  for (int t2 = 0; t2 < NQT; ++t2) {
+    const int r2 = t2 * 16 + q;
+    if (r2 < a.rows) {
+      const float Mx = s_m[t2][q], Ls = s_l[t2][q];
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = s_o[t2][q][dc + j];
+      if (nsp == 1) {
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        float* dst = a.out + (qrow0 + r2) * kHeadDim + dc;
+        *(f32x4*)dst = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *(f32x4*)(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        if (a.lse && dc == 0) a.lse[qrow0 + r2] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
+      } else {
+        const size_t pr = (bh * a.nsplit + split) * a.rows_pad + r2;
+        float* dst = a.part_o + pr * kHeadDim + dc;
+        *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
+        *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        if (dc == 0) {
+          a.part_ml[pr * 2 + 0] = Mx;
+          a.part_ml[pr * 2 + 1] = Ls;
+        }
+      }
+    }
+  }
+  __syncthreads();  // (LDS reused by the next item of a flat grid)
+}
+
 // One work item: split `split` of KV head hk of sequence b, by the whole
 // workgroup (the LDS arrays are the kernel's).
 template <int DT, int MODE, int NQT>
@@ -374,6 +526,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
+  if constexpr (kStaged && NQT == 4) {
+    attn_item_rows<DT, MODE, NQT>(a, b, hk, split, s_stage, s_m, s_l);
+    return;
+  }
   float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
 
   const int tid = threadIdx.x;
@@ -620,11 +776,17 @@ __device__ __forceinline__ void flat_prefix(const AttnArgs& a, int* s_pre) {
 // workgroups empty and, since workgroups go to the XCDs in index order, load
 // the XCDs unevenly.
 template <int DT, int MODE, int NQT, bool FLAT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT == 4)) ? 2 : 1,
+    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT == 4)) ? 2 : 1)))
 void attn_kernel(const AttnArgs a) {
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
+  // verification: four wave-private slabs, or the two shared slabs of the
+  // row-split item (4 query tiles)
+  constexpr int kStageLds = !kStaged ? kMergeBytes : (NQT == 4 ? 2 * kStageBytes : 4 * kStageBytes);
+  static_assert(kMergeBytes <= 2 * kStageBytes, "results must fit in two slabs");
   __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
-  __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStaged ? 4 * kStageBytes : kMergeBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStageLds];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
   __shared__ int s_pre[FLAT ? kMaxFlatSeqs + 1 : 1];
@@ -770,10 +932,7 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((attn_kernel<DT, MODE, 1, FLAT>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((attn_kernel<DT, MODE, 2, FLAT>), grid, block, 0, stream, a); break;
     case 3: hipLaunchKernelGGL((attn_kernel<DT, MODE, 3, FLAT>), grid, block, 0, stream, a); break;
-    case 4:
-      if constexpr (FLAT) return hipErrorInvalidValue;  // not launched flat
-      else hipLaunchKernelGGL((attn_kernel<DT, MODE, 4, FLAT>), grid, block, 0, stream, a);
-      break;
+    case 4: hipLaunchKernelGGL((attn_kernel<DT, MODE, 4, FLAT>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -787,8 +946,7 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
 template <int DT, int MODE>
 static hipError_t launch_nqt(const AttnArgs& a, hipStream_t stream) {
   if constexpr (MODE == kVerify || MODE == kVerifyTree) {
-    // (four query tiles keep one item per workgroup: the item loop would spill there)
-    if (a.B > 1 && a.B <= kMaxFlatSeqs && a.rows <= 48) return launch_tiles<DT, MODE, true>(a, stream);
+    if (a.B > 1 && a.B <= kMaxFlatSeqs) return launch_tiles<DT, MODE, true>(a, stream);
   }
   return launch_tiles<DT, MODE, false>(a, stream);
 }
