@@ -243,19 +243,46 @@ __device__ __forceinline__ void load_tile(Tile<DT>& T, const AttnArgs& a, const 
 
 // Operand sources for process_tile: k(u, s) / v(u, s) give the MFMA operand
 // of subtile u, k-step s (row 16 u + lane % 16, dims 32 s + 8 (lane / 16) ..).
+//
+// A staged tile also gives the value operand of the P.V product directly,
+// vt(bb): V^T for dims 16 bb .. 16 bb + 15 with the 32 tokens on the k axis,
+// in the order the P operand has them (lane (i, g) element j: token 4 g + j,
+// then 16 + 4 g + j - 4).  The transposing LDS read (ds_read_b64_tr_b16) gives
+// lane i of each 16-lane group element i % 4 of the 8 bytes that lane
+// 4 k + i / 4 of the group addressed, as its k-th element; so lane l of group g
+// addresses token 4 g + l / 4, dims 16 bb + 4 (l % 4) .. + 3, and two reads, 16
+// tokens apart, fill the operand (the lane layout was read off the chip).
+// Without a staged tile, V is moved onto the k axis by a product with a 0/1
+// selection matrix (an exact copy either way).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
 template <int DT>
 struct SlabSource {
-  const unsigned char* kp;  // slab + (lane % 16) * kPitch + 16 (lane / 16)
+  static constexpr bool kTrV = true;
+  const unsigned char* kp;   // slab + (lane % 16) * kPitch + 16 (lane / 16)
+  const unsigned char* vtp;  // slab + (kTile + 4 (lane / 16) + (lane % 16) / 4) * kPitch + 8 (lane % 4)
+  __device__ __forceinline__ SlabSource(const unsigned char* slab, int lane)
+      : kp(slab + (lane & 15) * kPitch + 16 * (lane >> 4)),
+        vtp(slab + (kTile + 4 * (lane >> 4) + ((lane & 15) >> 2)) * kPitch + 8 * (lane & 3)) {}
   __device__ __forceinline__ typename MT<DT>::V8 k(int u, int s) const {
     return __builtin_bit_cast(typename MT<DT>::V8, *(const u32x4*)(kp + u * 16 * kPitch + 64 * s));
   }
   __device__ __forceinline__ typename MT<DT>::V8 v(int u, int s) const {
     return __builtin_bit_cast(typename MT<DT>::V8, *(const u32x4*)(kp + (kTile + u * 16) * kPitch + 64 * s));
   }
+  __device__ __forceinline__ typename MT<DT>::V8 vt(int bb) const {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtp + 32 * bb));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtp + 16 * kPitch + 32 * bb));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(typename MT<DT>::V8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+  }
 };
 
 template <int DT>
 struct RegSource {
+  static constexpr bool kTrV = false;
   const Tile<DT>& T;
   __device__ __forceinline__ typename MT<DT>::V8 k(int u, int s) const { return u ? T.k1[s] : T.k0[s]; }
   __device__ __forceinline__ typename MT<DT>::V8 v(int u, int s) const { return u ? T.v1[s] : T.v0[s]; }
@@ -340,26 +367,38 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
     pl[qt] = lo;
     l_run[qt] += psum;
   }
-  // Values: move tokens onto the k axis, then O^T += V^T . P^T.
+  // Values: tokens on the k axis, then O^T += V^T . P^T.
+  if constexpr (Src::kTrV) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const V8 v0 = src.v(0, s);
-    const V8 v1 = src.v(1, s);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int bb = 2 * s + h;
-      const f32x4 t0v = M::mma(v0, sel[h], zero4);
-      const f32x4 t1v = M::mma(v1, sel[h], zero4);
-      V8 av;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        av[r] = (S)t0v[r];
-        av[4 + r] = (S)t1v[r];
-      }
+    for (int bb = 0; bb < 8; ++bb) {
+      const V8 av = src.vt(bb);
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
         acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
         acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const V8 v0 = src.v(0, s);
+      const V8 v1 = src.v(1, s);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int bb = 2 * s + h;
+        const f32x4 t0v = M::mma(v0, sel[h], zero4);
+        const f32x4 t1v = M::mma(v1, sel[h], zero4);
+        V8 av;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          av[r] = (S)t0v[r];
+          av[4 + r] = (S)t1v[r];
+        }
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          acc[qt][bb] = M::mma(av, ph[qt], acc[qt][bb]);
+          acc[qt][bb] = M::mma(av, pl[qt], acc[qt][bb]);
+        }
       }
     }
   }
@@ -464,7 +503,7 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
       __syncthreads();
       if (owner) {
         __builtin_amdgcn_sched_barrier(0);
-        process_tile<DT, MODE, 1>(SlabSource<DT>{slab + lq * kPitch + 16 * lg}, mask, t, qreg, sel, lim, lim_min, tm,
+        process_tile<DT, MODE, 1>(SlabSource<DT>(slab, lane), mask, t, qreg, sel, lim, lim_min, tm,
                                   tbase, acc, m_run, l_run, c2, lq, lg);
       }
     }
@@ -638,7 +677,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   int t = v0 + kTile * w;
   if (kStaged && t < v1) {
     unsigned char* slab = s_stage + w * kStageBytes;
-    const SlabSource<DT> src{slab + lq * kPitch + 16 * lg};
+    const SlabSource<DT> src(slab, lane);
     Stage st;
     load_stage<MODE>(st, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
     unsigned mask = st.mask;
