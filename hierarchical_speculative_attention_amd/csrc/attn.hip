@@ -404,14 +404,14 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   }
 }
 
-// Verification with 4 query tiles, rows split over the waves: wave w owns
-// query tile w over the item's whole token range and holds the register state
-// of one tile (190 registers: two waves per SIMD; four tiles in one wave took
-// 500 registers, one wave per SIMD, and copied the accumulators between
-// register files every tile).  Measured against all tiles in every wave: 4
-// tiles 252 -> 239 us, 3 tiles equal, 2 tiles 349 -> 366 us (the tile's
-// V-operand products are repeated by every owning wave), so only 4 tiles take
-// this path.  Each 32-token K/V tile is fetched by all four
+// Verification with 3-4 query tiles, rows split over the waves: wave w < NQT
+// owns query tile w over the item's whole token range and holds the register
+// state of one tile (~180 registers: two waves per SIMD; all tiles in one wave
+// took 410-500 registers, one wave per SIMD, and copied the accumulators
+// between register files every tile).  Measured against all tiles in every
+// wave (with the transposing V reads): 3 tiles 379 -> 363 us, 4 tiles faster
+// too; 2 tiles about equal, so they keep the per-wave path.  Each 32-token K/V
+// tile is fetched by all four
 // waves together, 16 rows each (1 KB per instruction), kRowRing tiles in
 // flight per workgroup, staged in two shared slabs and consumed after a
 // barrier by every owning wave.  A slab is rewritten two tiles later, after
@@ -565,7 +565,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
-  if constexpr (kStaged && NQT == 4) {
+  if constexpr (kStaged && NQT >= 3) {
     attn_item_rows<DT, MODE, NQT>(a, b, hk, split, s_stage, s_m, s_l);
     return;
   }
@@ -816,13 +816,13 @@ __device__ __forceinline__ void flat_prefix(const AttnArgs& a, int* s_pre) {
 // the XCDs unevenly.
 template <int DT, int MODE, int NQT, bool FLAT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT == 4)) ? 2 : 1,
-    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT == 4)) ? 2 : 1)))
+    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT >= 3)) ? 2 : 1,
+    (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT >= 3)) ? 2 : 1)))
 void attn_kernel(const AttnArgs a) {
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
   // verification: four wave-private slabs, or the two shared slabs of the
   // row-split item (4 query tiles)
-  constexpr int kStageLds = !kStaged ? kMergeBytes : (NQT == 4 ? 2 * kStageBytes : 4 * kStageBytes);
+  constexpr int kStageLds = !kStaged ? kMergeBytes : (NQT >= 3 ? 2 * kStageBytes : 4 * kStageBytes);
   static_assert(kMergeBytes <= 2 * kStageBytes, "results must fit in two slabs");
   __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStageLds];
