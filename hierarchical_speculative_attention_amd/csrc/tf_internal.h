@@ -36,7 +36,7 @@ struct AttnArgs {
   const uint64_t* tmask;    // [B][Qn]: bit m = the row sees tree node m (cache row n - Qn + m)
   // split-K
   int32_t tpw;              // virtual tokens per workgroup (multiple of 128)
-  int32_t nsplit;           // gridDim.x
+  int32_t nsplit;           // splits of the longest sequence (partial-buffer stride; the 3-D grid's x)
   int32_t rows_pad;         // 16 * query tiles
   float* out;               // [B][Hq][Qn][d]
   float* lse;               // [B][Hq][Qn] or null
