@@ -142,10 +142,12 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
   } else {
     u32x4 x[kCPL];
+    // (a wave wholly past C -- padding of a shorter sequence -- loads nothing)
+    const bool any = c_wave < C;
 #pragma unroll
     for (int i = 0; i < kCPL; ++i) {
       x[i] = u32x4{0u, 0u, 0u, 0u};
-      if (C > 0) {  // chunks past C read chunk C - 1 (in bounds) and are masked below
+      if (any) {  // chunks past C read chunk C - 1 (in bounds) and are masked below
         const int c = min(c_wave + 4 * i + grp, C - 1);
         x[i] = __builtin_nontemporal_load(
             (const u32x4*)((const uint16_t*)ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part));
