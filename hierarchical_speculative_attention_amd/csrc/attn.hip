@@ -171,10 +171,18 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
 // reads are free of bank conflicts.  One tile is in flight while the staged
 // one is consumed.
 //
-// Direct (sparse and streaming: a few tiles per wave, latency-bound).  Loads
+// Staged, two deep (sparse: a few gathered tiles per wave, latency-bound).
+// The same 1 KB-per-instruction loads and slab, but two register stages
+// alternate so that a wave's first two tiles are in flight at once (one
+// memory round trip for both); with the value operand read transposed from
+// the slab this beat loading straight into the operand layout (sparse pass
+// 21.5 -> 20.4 us per 128K layer; the gathers of 2 KB runs stream better in
+// 1 KB instructions than in 16 rows x 64 bytes).
+//
+// Direct (streaming: 256 ring rows per head, one workgroup per head).  Loads
 // go straight into the MFMA operand layout (lane (t, g): dims 32 s + 8 g ..
-// +8 of token t) and two tiles are in flight at once, so a wave pays one
-// memory round trip for its first two tiles.
+// +8 of token t) and two tiles are in flight at once; staging measured slower
+// here (8.6 -> 8.9 us).
 constexpr int kPitch = 272;                  // LDS bytes per staged 256-byte row
 constexpr int kStageRows = 2 * kTile;        // 32 key rows, then 32 value rows
 constexpr int kStageBytes = kStageRows * kPitch;
@@ -675,7 +683,32 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   // outstanding.  LDS operations of one wave complete in order, so a slab is
   // rewritten only after the previous tile's operand reads.
   int t = v0 + kTile * w;
-  if (kStaged && t < v1) {
+  constexpr bool kStaged2 = (MODE == kSparse || MODE == kSparseTail) && NQT <= 2;
+  if (kStaged2 && t < v1) {
+    // two register stages alternate into the slab; the next-but-one tile's
+    // loads are issued while the staged one is consumed
+    unsigned char* slab = s_stage + w * kStageBytes;
+    const SlabSource<DT> src(slab, lane);
+    Stage sa, sb;
+    load_stage<MODE>(sa, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
+    load_stage<MODE>(sb, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+    while (true) {
+      unsigned mask = sa.mask;
+      write_stage(sa, slab, lane);
+      if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
+      mask = sb.mask;
+      write_stage(sb, slab, lane);
+      if (t + 8 * kTile < v1) load_stage<MODE>(sb, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
+      t += 4 * kTile;
+      if (t >= v1) break;
+    }
+  } else if (kStaged && t < v1) {
     unsigned char* slab = s_stage + w * kStageBytes;
     const SlabSource<DT> src(slab, lane);
     Stage st;
@@ -692,7 +725,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
       write_stage(st, slab, lane);
       load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     }
-  } else if (!kStaged && t < v1) {
+  } else if (!kStaged && !kStaged2 && t < v1) {
     Tile<DT> A, B;
     load_tile<DT, MODE>(A, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
     while (true) {
@@ -710,7 +743,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
       if (t >= v1) break;
     }
   }
-  if (kStaged) __syncthreads();  // every slab consumed: the merge reuses them
+  if (kStaged || kStaged2) __syncthreads();  // every slab consumed: the merge reuses them
 
   // ---- merge the four waves (per query tile) -------------------------------
   const size_t bh = (size_t)b * a.Hkv + hk;
@@ -820,9 +853,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT >= 3)) ? 2 : 1)))
 void attn_kernel(const AttnArgs a) {
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
-  // verification: four wave-private slabs, or the two shared slabs of the
-  // row-split item (4 query tiles)
-  constexpr int kStageLds = !kStaged ? kMergeBytes : (NQT >= 3 ? 2 * kStageBytes : 4 * kStageBytes);
+  // four wave-private slabs (verify and sparse with up to two query tiles),
+  // the two shared slabs of the row split (verify, 3-4 tiles), or the merge
+  // buffer alone (direct loads)
+  constexpr bool kSlabs4 = (kStaged && NQT <= 2) || ((MODE == kSparse || MODE == kSparseTail) && NQT <= 2);
+  constexpr int kStageLds = kSlabs4 ? 4 * kStageBytes : (kStaged ? 2 * kStageBytes : kMergeBytes);
   static_assert(kMergeBytes <= 2 * kStageBytes, "results must fit in two slabs");
   __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStageLds];
