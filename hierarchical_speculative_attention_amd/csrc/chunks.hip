@@ -60,11 +60,23 @@ __global__ __launch_bounds__(256) void chunk_keys_kernel(
   const int lo = c * cs, hi = min(n, lo + cs);
   const uint16_t* src = K + kbase[b] + ((size_t)g * cap + lo) * kHeadDim + 8 * part;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < hi - lo; ++t) {
-    float f[8];
-    widen8(IN_DT, __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * kHeadDim)), f);
+  // rows in batches of 8 loads issued together (row index clamped into the
+  // chunk, surplus rows not added), summed in row order
+  const int rows = hi - lo;
+  for (int t0 = 0; t0 < rows; t0 += 8) {
+    u32x4 x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] += f[j];
+    for (int u = 0; u < 8; ++u)
+      x[u] = __builtin_nontemporal_load((const u32x4*)(src + (size_t)min(t0 + u, rows - 1) * kHeadDim));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (t0 + u < rows) {
+        float f[8];
+        widen8(IN_DT, x[u], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] += f[j];
+      }
+    }
   }
   const float cnt = (float)(hi - lo);
 #pragma unroll
