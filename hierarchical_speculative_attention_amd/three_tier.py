@@ -89,9 +89,17 @@ def drafter_reserve(gamma1: int, gamma2: int) -> int:
 class ThreeTierStep:
     def __init__(self, target: List[TargetLayer], drafter: List[DrafterLayer], syn: Synthetic, *, Hq: int,
                  chunk_size: int, k: int, tail: int, gamma1: int, gamma2: int, n_sink: int, window: int,
-                 temperature: float = 1.0, stream: Optional[torch.cuda.Stream] = None, record: bool = False):
+                 temperature: float = 1.0, stream: Optional[torch.cuda.Stream] = None, record: bool = False,
+                 graphs: bool = False):
         self.t, self.dr, self.syn = target, drafter, syn
         self.record = record      # keep each round's and step's decisions (tests)
+        # graphs: the fixed call sequences (retrieval, a round for each count of
+        # unseen tokens and chain-count parity, Force 3) are captured once as HIP
+        # graphs and replayed; the host still decides the rounds between them
+        self.graphs = graphs
+        if graphs and stream is None:
+            stream = torch.cuda.Stream(target[0].K.device)   # graphs are captured on a side stream
+        self._g = {}
         self.log: list = []
         self.Hq, self.cs, self.k, self.tail = Hq, chunk_size, k, tail
         self.g1, self.g2, self.S, self.W = gamma1, gamma2, n_sink, window
@@ -118,12 +126,17 @@ class ThreeTierStep:
         self.cand = torch.empty((1, gamma2), **i32)
         self.cand_q = torch.empty((1, gamma2, V), dtype=torch.float32, device=dev)
         self.zero = torch.zeros(1, **i32)
+        self.status = torch.empty(1, **i32)             # append status, never read (lengths are host-checked)
         self.chunk_begin = torch.empty(1, **i32)
         self.host = torch.empty(4, dtype=torch.int32).pin_memory()
         self.ws2 = tf.workspace(tf.sparse_verify_attn_workspace_size(1, Hq, kv0.H, gamma1 + 1, k, chunk_size, tail),
                                 dev)
         self.ws3 = tf.workspace(tf.verify_attn_workspace_size(1, Hq, kv0.H, gamma2 + 1, kv0.max_len), dev)
         self.wsa = tf.workspace(tf.accept_workspace_size(1, max(gamma1, gamma2), V), dev)
+        # uniforms of a round (gamma1 drafter draws, then gamma1 + 1 for level 1) and of
+        # Force 3 (gamma2 + 1), staged in fixed buffers so that graphs can replay them
+        self.u_round = torch.empty((1, 2 * gamma1 + 1), dtype=torch.float64, device=dev)
+        self.u_f3 = torch.empty((1, gamma2 + 1), dtype=torch.float64, device=dev)
         self.u_pos = 0
         self.n = int(kv0.seq_len[0].item())            # committed rows before the current token
         self.pending = self.n - int(drafter[0].sd.seq_len[0].item())  # committed tokens the drafter has not consumed
@@ -152,98 +165,142 @@ class ThreeTierStep:
         rows = self.syn.draft_rows[R - 1]
         for L in self.dr:
             tf.append_kv(rows, rows, L.Ks, L.Vs, L.sd, ring=True, n_sink=self.S, window=self.W,
-                         reserve=drafter_reserve(self.g1, self.g2), stream=self.s)
+                         reserve=drafter_reserve(self.g1, self.g2), status=self.status, stream=self.s)
         tf.commit_length(self.d_len, R, stream=self.s)
         for L in self.dr:
             tf.stream_attn(self.syn.draft_q, L.Ks, L.Vs, L.sd, self.S, self.W, out=self.o_d, stream=self.s)
 
-    # -- one step --------------------------------------------------------------
-    def step(self) -> int:
-        """One three-tier step; returns the number of tokens it emits."""
-        s, g1, g2 = self.s, self.g1, self.g2
-        n_start = self.n
-        d_start = self.n - self.pending       # drafter's consumed length
-        # retrieval for this step, from the committed rows
-        self.ck_len.fill_(-(-n_start // self.cs))
+    def _run(self, key, body):
+        """body() now, eagerly, or as the replay of its graph (captured on first use)."""
+        if not self.graphs:
+            body()
+            return
+        g = self._g.get(key)
+        if g is None:
+            s = self.s
+            s.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                body()
+            self._g[key] = g
+        g.replay()
+
+    # -- the bodies --------------------------------------------------------------
+    def _retrieval(self):
         for L, idx in zip(self.t, self.idx):
-            tf.score_chunks(self.syn.draft_q, self.Hq, L.ck, L.ckd, self.c_max, scores=self.scores, stream=s)
-            tf.select_topk(self.scores, self.ck_len, self.k, idx=idx, stream=s)
-        self.cnt[0].zero_()
-        cin, total, rounds = 0, 0, 0          # total: tokens the rounds emitted (the chain keeps the first gamma2)
-        d_len = d_start                        # host copy of the drafter's length
-        while total < g2:
-            rounds += 1
-            n_round = self.n
-            # Force 1: the unseen committed tokens and the current token, then its drafts
-            self._drafter_consume(1 + self.pending)
-            d_len += 1 + self.pending
-            self.pending = 0
-            for j in range(g1):
-                if j > 0:
-                    self._drafter_consume(1)
-                    d_len += 1
-                tf.accept(self.syn.r_rows[:, j:j + 1], None, None, self._u(1), self.T, n_accepted=self.na_d,
-                          next_token=self.drafts[j], ws=self.wsa, stream=s)
-            self.drafts_row.copy_(self.drafts.view(1, g1))
-            # Force 2: the current token and the drafts on the retrieval cache
-            for L in self.t:
-                tf.append_kv(self.syn.f2_rows, self.syn.f2_rows, L.K, L.V, L.kv, stream=s)
-            tf.commit_length(self.seq_len, g1 + 1, stream=s)
-            for L, idx in zip(self.t, self.idx):
-                tf.sparse_verify_attn(self.syn.f2_q, L.K, L.V, L.kv, idx, self.cs, self.tail, out=self.o2,
-                                      ws=self.ws2, stream=s)
-            tf.accept(self.syn.q_rows, self.syn.r_rows, self.drafts_row, self._u(g1 + 1), self.T,
-                      n_accepted=self.n1, next_token=self.y, ws=self.wsa, stream=s)
-            cout = 1 - cin
-            tf.collect_candidates(self.drafts_row, self.n1, self.y, self.syn.q_rows, self.cnt[cin], self.cnt[cout],
-                                  self.cand, self.cand_q, stream=s)
-            tf.commit_length(self.seq_len, 0, g1, self.n1, stream=s)   # rejected drafts leave the full cache
-            self.host[0:1].copy_(self.n1, non_blocking=True)
-            self._sync()
-            n1 = int(self.host[0])
-            total += n1 + 1
-            cin = cout
-            if self.record:
-                self.log.append(("round", self.drafts_row.cpu().numpy()[0].tolist(), n1, int(self.y.item()),
-                                 self.syn.uniforms[self.u_pos - g1 - 1:self.u_pos].cpu().numpy()))
-            self.n = n_round + 1 + n1
-            # the drafter consumed the current token and drafts 1 .. g1 - 1
-            drop = (g1 - 1) - min(n1, g1 - 1)
-            self._drop(self.d_len, drop)
-            d_len -= drop
-            self.pending = self.n - d_len
-        # the full cache holds the current token and the first total - 1
-        # emitted tokens: keep the current token and exactly gamma2 candidates
-        if total == g2:
-            for L in self.t:
-                tf.append_kv(self.syn.one_row, self.syn.one_row, L.K, L.V, L.kv, stream=s)
-            tf.commit_length(self.seq_len, 1, stream=s)
-        else:
-            self._drop(self.seq_len, total - 1 - g2)
-        # Force 3: the current token and the candidates on the full cache
+            tf.score_chunks(self.syn.draft_q, self.Hq, L.ck, L.ckd, self.c_max, scores=self.scores, stream=self.s)
+            tf.select_topk(self.scores, self.ck_len, self.k, idx=idx, stream=self.s)
+
+    def _round(self, pend, cin):
+        """Force 1 drafts gamma1 tokens (after consuming 1 + pend tokens), Force 2
+        verifies them, level 1 tests them and the chain collects what they emit."""
+        s, g1 = self.s, self.g1
+        self._drafter_consume(1 + pend)
+        for j in range(g1):
+            if j > 0:
+                self._drafter_consume(1)
+            tf.accept(self.syn.r_rows[:, j:j + 1], None, None, self.u_round[:, j:j + 1], self.T,
+                      n_accepted=self.na_d, next_token=self.drafts[j], ws=self.wsa, stream=s)
+        self.drafts_row.copy_(self.drafts.view(1, g1))
+        for L in self.t:
+            tf.append_kv(self.syn.f2_rows, self.syn.f2_rows, L.K, L.V, L.kv, status=self.status, stream=s)
+        tf.commit_length(self.seq_len, g1 + 1, stream=s)
+        for L, idx in zip(self.t, self.idx):
+            tf.sparse_verify_attn(self.syn.f2_q, L.K, L.V, L.kv, idx, self.cs, self.tail, out=self.o2,
+                                  ws=self.ws2, stream=s)
+        tf.accept(self.syn.q_rows, self.syn.r_rows, self.drafts_row, self.u_round[:, g1:], self.T,
+                  n_accepted=self.n1, next_token=self.y, ws=self.wsa, stream=s)
+        tf.collect_candidates(self.drafts_row, self.n1, self.y, self.syn.q_rows, self.cnt[cin], self.cnt[1 - cin],
+                              self.cand, self.cand_q, stream=s)
+        tf.commit_length(self.seq_len, 0, g1, self.n1, stream=s)   # rejected drafts leave the full cache
+
+    def _extend_one(self):
+        for L in self.t:
+            tf.append_kv(self.syn.one_row, self.syn.one_row, L.K, L.V, L.kv, status=self.status, stream=self.s)
+        tf.commit_length(self.seq_len, 1, stream=self.s)
+
+    def _force3(self):
+        """Force 3 on the full cache, level 2, the rejected candidates' rollback and
+        the refresh of the chunk keys the step's rows fell into."""
+        s, g2 = self.s, self.g2
         for L in self.t:
             tf.verify_attn(self.syn.f3_q, L.K, L.V, L.kv, out=self.o3, ws=self.ws3, stream=s)
-        tf.accept(self.syn.p_rows, self.cand_q, self.cand, self._u(g2 + 1), self.T, n_accepted=self.n2,
+        tf.accept(self.syn.p_rows, self.cand_q, self.cand, self.u_f3, self.T, n_accepted=self.n2,
                   next_token=self.nxt, ws=self.wsa, stream=s)
         tf.commit_length(self.seq_len, 0, g2, self.n2, stream=s)
-        # chunk keys of the chunks the step's rows fell into
-        self.chunk_begin.fill_(n_start // self.cs)
         for L in self.t:
             tf.build_chunk_keys(L.K, L.kv, self.cs, L.ck, L.ckd, chunk_begin=self.chunk_begin,
                                 max_chunks=(g2 + 1) // self.cs + 2, stream=s)
-        self.host[2:3].copy_(self.n2, non_blocking=True)
-        self._sync()
-        n2 = int(self.host[2])
-        if self.record:
-            self.log.append(("step", self.cand.cpu().numpy()[0].tolist(), n2, int(self.nxt.item()),
-                             self.syn.uniforms[self.u_pos - g2 - 1:self.u_pos].cpu().numpy(),
-                             self.cand_q.cpu().numpy()[0]))
-        self.n = n_start + 1 + n2
-        # the drafter keeps what it consumed of the committed tokens
-        keep = min(d_len, self.n)
-        self._drop(self.d_len, d_len - keep)
+
+    def _stage_uniforms(self, dst, counts):
+        """Copy the next uniforms (taken as _u(c) for each c in counts, in order) into dst."""
+        parts = [self._u(c) for c in counts]
+        dst.copy_(torch.cat(parts, 1) if len(parts) > 1 else parts[0])
+
+    # -- one step --------------------------------------------------------------
+    def step(self) -> int:
+        """One three-tier step; returns the number of tokens it emits."""
+        g1, g2 = self.g1, self.g2
+        n_start = self.n
+        d_start = self.n - self.pending       # drafter's consumed length
+        with torch.cuda.stream(self.s) if self.s is not None else _nullcontext():
+            # retrieval for this step, from the committed rows
+            self.ck_len.fill_(-(-n_start // self.cs))
+            self._run("retrieval", self._retrieval)
+            self.cnt[0].zero_()
+            cin, total, rounds = 0, 0, 0      # total: tokens the rounds emitted (the chain keeps the first gamma2)
+            d_len = d_start                    # host copy of the drafter's length
+            while total < g2:
+                rounds += 1
+                n_round = self.n
+                self._stage_uniforms(self.u_round, [1] * g1 + [g1 + 1])
+                pend = self.pending
+                self._run(("round", pend, cin), lambda: self._round(pend, cin))
+                self.host[0:1].copy_(self.n1, non_blocking=True)   # the kept count (outside any graph)
+                d_len += g1 + pend            # the current token, the unseen ones, drafts 1 .. g1 - 1
+                self.pending = 0
+                self._sync()
+                n1 = int(self.host[0])
+                total += n1 + 1
+                cin = 1 - cin
+                if self.record:
+                    self.log.append(("round", self.drafts_row.cpu().numpy()[0].tolist(), n1, int(self.y.item()),
+                                     self.u_round.cpu().numpy()[0, g1:]))
+                self.n = n_round + 1 + n1
+                # the drafter consumed the current token and drafts 1 .. g1 - 1
+                drop = (g1 - 1) - min(n1, g1 - 1)
+                self._drop(self.d_len, drop)
+                d_len -= drop
+                self.pending = self.n - d_len
+            # the full cache holds the current token and the first total - 1
+            # emitted tokens: keep the current token and exactly gamma2 candidates
+            if total == g2:
+                self._run("extend", self._extend_one)
+            else:
+                self._drop(self.seq_len, total - 1 - g2)
+            self._stage_uniforms(self.u_f3, [g2 + 1])
+            self.chunk_begin.fill_(n_start // self.cs)
+            self._run("force3", self._force3)
+            self.host[2:3].copy_(self.n2, non_blocking=True)
+            self._sync()
+            n2 = int(self.host[2])
+            if self.record:
+                self.log.append(("step", self.cand.cpu().numpy()[0].tolist(), n2, int(self.nxt.item()),
+                                 self.u_f3.cpu().numpy()[0], self.cand_q.cpu().numpy()[0]))
+            self.n = n_start + 1 + n2
+            # the drafter keeps what it consumed of the committed tokens
+            keep = min(d_len, self.n)
+            self._drop(self.d_len, d_len - keep)
         self.pending = self.n - keep
         self.steps += 1
         self.rounds += rounds
         self.emitted += n2 + 1
         return n2 + 1
+
+
+class _nullcontext:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def build(n0=3000, H=4, layers=2, d_layers=2, cs=8, k=16, g1=2, g2=5, V=64, S=4, W=28, seed=131):
+def build(n0=3000, H=4, layers=2, d_layers=2, cs=8, k=16, g1=2, g2=5, V=64, S=4, W=28, seed=131, graphs=False):
     g = torch.Generator(device=DEV).manual_seed(seed)
     rnd = lambda *shape: torch.randn(*shape, generator=g, device=DEV).to(torch.bfloat16)
     extra = 64 * (g1 + g2 + 4)
@@ -53,13 +53,14 @@ def build(n0=3000, H=4, layers=2, d_layers=2, cs=8, k=16, g1=2, g2=5, V=64, S=4,
         q_rows=Qr.contiguous(), f3_q=rnd(1, H, g2 + 1, 128), one_row=rnd(1, H, 1, 128), p_rows=P.contiguous(),
         uniforms=torch.from_numpy(synth.open_uniforms(rng, 4096)).to(DEV))
     step = tt.ThreeTierStep(target, drafter, syn, Hq=H, chunk_size=cs, k=k, tail=16, gamma1=g1, gamma2=g2, n_sink=S,
-                            window=W, record=True)
+                            window=W, record=True, graphs=graphs)
     return step, syn
 
 
-def test_three_tier_steps_match_oracle_and_lengths():
+@pytest.mark.parametrize("graphs", [False, True], ids=["eager", "graphs"])
+def test_three_tier_steps_match_oracle_and_lengths(graphs):
     g1, g2 = 2, 5
-    step, syn = build(g1=g1, g2=g2)
+    step, syn = build(g1=g1, g2=g2, graphs=graphs)
     R = syn.r_rows.cpu().numpy()[0]
     Qr = syn.q_rows.cpu().numpy()[0]
     P = syn.p_rows.cpu().numpy()[0]
@@ -92,3 +93,30 @@ def test_three_tier_steps_match_oracle_and_lengths():
         step.log.clear()
     assert step.emitted > step.steps     # some candidates were kept
     assert total_rounds > step.steps     # some steps needed more than one round
+
+
+def test_three_tier_graphs_replay_the_eager_steps():
+    """Replayed graphs (with eager work and host reads between replays) take
+    every decision of the eager launches and leave the same caches."""
+    logs, outs = [], []
+    for graphs in (False, True):
+        step, _ = build(g1=3, g2=6, seed=77, graphs=graphs)
+        entries = []
+        for _ in range(30):
+            step.step()
+            torch.cuda.synchronize()
+            entries.append((step.n, step.pending, int(step.seq_len.item()), int(step.d_len.item())))
+            for e in step.log:
+                entries.append((e[0], e[1], e[2], e[3]))
+            step.log.clear()
+        logs.append(entries)
+        # the written parts: rows below the length (each head), built chunk keys, the whole ring
+        n, H = step.n, step.t[0].kv.H
+        rows = lambda x, cap, m: x.view(H, cap, 128)[:, :m].cpu()
+        outs.append([step.o3.cpu(), step.o2.cpu(), step.o_d.cpu()]
+                    + [rows(x.ck, x.ckd.max_len, -(-n // step.cs)) for x in step.t]
+                    + [rows(t, x.K.numel() // (H * 128), n) for x in step.t for t in (x.K, x.V)]
+                    + [t.cpu() for x in step.dr for t in (x.Ks, x.Vs)])
+    assert logs[0] == logs[1]
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
