@@ -976,10 +976,15 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
                       int32_t max_tpw) {
   SplitPlan p;
-  int32_t tpw = max_tpw;
   const long heads = (long)B * Hkv;
-  while (tpw > 128 && heads * (((long)max_virtual + tpw - 1) / tpw) < target_wgs) tpw >>= 1;
-  p.tpw = tpw;
+  const long per_head = target_wgs / heads;  // splits per (sequence, KV head) that keep the grid within target
+  long tpw = max_tpw;
+  if (per_head >= 1) {
+    long fit = ((long)max_virtual + per_head - 1) / per_head;
+    fit = max(128L, (fit + kTile - 1) / kTile * kTile);
+    if (fit < tpw) tpw = fit;
+  }
+  p.tpw = (int32_t)tpw;
   p.nsplit = (int32_t)(((long)max_virtual + tpw - 1) / tpw);
   if (p.nsplit < 1) p.nsplit = 1;
   p.rows_pad = ((rows + 15) / 16) * 16;

@@ -54,8 +54,10 @@ struct SplitPlan {
   size_t part_o_bytes, part_ml_bytes, total_bytes;
 };
 
-// Virtual tokens per workgroup: a power of two in [128, max_tpw], the largest
-// that still gives at least target_wgs workgroups.
+// Virtual tokens per workgroup: the fewest (a multiple of the tile, at least
+// 128, at most max_tpw) that keep the grid within target_wgs workgroups, the
+// number resident at once.  A grid a little past that would leave its last
+// workgroups to start only when the first ones finish.
 constexpr int32_t kVerifyMaxTpw = 4096;
 constexpr int32_t kSparseMaxTpw = 1024;
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
