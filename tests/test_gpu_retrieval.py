@@ -106,6 +106,30 @@ def test_scores_parity(Hq, Hkv, ck_dtype):
             assert np.all(np.isneginf(s[b, g, C:]))
 
 
+@pytest.mark.parametrize("ck_dtype", ["bf16", "fp16"])
+def test_scores_ragged_rows(ck_dtype):
+    # 64 rows of a c_max = 8200 score array: full rows, a row of 3 chunks and
+    # an empty one (all -inf), the grid's last workgroup of each row partial
+    B, H, c_max = 4, 16, 8200
+    C = [8192, 8000, 3, 0]
+    lay = synth.KVLayout.build(C, H, 128, caps=[max(c, 1) for c in C])
+    g = torch.Generator().manual_seed(21)
+    ck_host = torch.randn(lay.total_elems, generator=g).to(TDT[ck_dtype])
+    q_host = torch.randn((B, H, 128), generator=g).to(TDT[ck_dtype])
+    s = tf.score_chunks(q_host.cuda(), H, ck_host.cuda(), desc(lay, ck_dtype), c_max)
+    torch.cuda.synchronize()
+    s = s.cpu().double().numpy()
+    ck_bits, q_bits = host_bits(ck_host), host_bits(q_host)
+    for b in range(B):
+        for h in range(H):
+            kbar = oracle.widen(lay.head(ck_bits, b, h), ck_dtype)
+            qg = oracle.widen(q_bits[b, h:h + 1], ck_dtype)
+            ref = oracle.chunk_scores(qg, kbar)
+            scale = np.linalg.norm(qg) * np.linalg.norm(kbar, axis=1) + 1e-3
+            assert np.all(np.abs(s[b, h, :C[b]] - ref) <= 1e-5 * scale), (b, h)
+            assert np.all(np.isneginf(s[b, h, C[b]:])), (b, h)
+
+
 def run_topk(scores_np, n_chunks, k):
     s = torch.from_numpy(np.ascontiguousarray(scores_np, np.float32)).cuda()
     idx = tf.select_topk(s, torch.tensor(n_chunks, dtype=torch.int32, device="cuda"), k)
