@@ -164,6 +164,8 @@ TF_EXPORT int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq, const 
     return fail(TF_ERR_INVALID_ARG, "16-bit chunk keys must share the query dtype");
   if (Hq < 1 || Hq % ckd->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, ckd->H);
   if (c_max < 1) return fail(TF_ERR_INVALID_ARG, "c_max must be >= 1");
+  // (the key loads address a head's row with 32-bit byte offsets)
+  if (c_max > (1 << 22)) return fail(TF_ERR_UNSUPPORTED, "c_max %d above 1<<22", c_max);
   if (ckd->max_len > c_max) return fail(TF_ERR_INVALID_ARG, "ckd->max_len %d exceeds c_max %d", ckd->max_len, c_max);
   if (ckd->B == 0) return ok();
   TRY(check_ptr(q, "q", 16));

@@ -108,23 +108,34 @@ hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs
 }
 
 // ---------------------------------------------------------------------------
-// a2: grid (ceil(c_max / (16 * kCPL)), H, B), 256 threads.  Each wave scores
-// 4 * kCPL consecutive chunks; its load instruction i covers chunks
-// 4 i .. 4 i + 3 of its range, 1 KB of contiguous memory (16 lanes per
-// 256-byte key).  The 16 partial dot products of a key are reduced across
-// its 16 lanes.
+// a2, 16-bit chunk keys: workgroups of four waves; wave j of the grid scores
+// blocks j, j + (waves in the grid), ... of 16 consecutive chunks (4 KB of
+// keys) of its row, two blocks in flight.  Load instruction i of a block
+// covers chunks 4 i .. 4 i + 3 of it, 1 KB of contiguous memory (16 lanes per
+// 256-byte key); the 16 partial dot products of a key are reduced across its
+// 16 lanes.  Keys are read through a buffer descriptor whose size is the
+// row's C keys: a load past it returns zeros without touching memory, so
+// every wave issues the same loads whatever C is, its waits stay exact, and a
+// block of padding costs only its -inf stores.  The grid is capped at
+// kScoreWgs workgroups: one block per wave for 32 rows of 16384 chunks or 8
+// rows of 32768, several for a batch (a grid of one workgroup per 64 chunks of
+// the longest row would be mostly padding for the shorter sequences and
+// bound by the dispatch of its workgroups).
 // ---------------------------------------------------------------------------
-constexpr int kCPL = 4;  // keys per lane group (loads in flight together); 8 and 16 measured slower
+constexpr int kScoreWaves = 4;
+constexpr int kScoreLoads = 4;                 // 16-byte loads per lane per block
+constexpr int kScoreBlock = 4 * kScoreLoads;   // chunks per block
+constexpr int kScoreWgs = 8192;
 
 template <int CK_DT>
-__global__ __launch_bounds__(256) void score_kernel(
-    const uint16_t* __restrict__ q, int32_t q_dtype, int32_t Hq, int32_t H, const void* __restrict__ ck,
+__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
+    const uint16_t* __restrict__ q, int32_t q_dtype, int32_t Hq, int32_t H, const uint16_t* __restrict__ ck,
     const int64_t* __restrict__ cbase, const int32_t* __restrict__ ccap, const int32_t* __restrict__ clen,
     int32_t c_max_len, float* __restrict__ scores, int32_t c_max) {
   const int b = blockIdx.z, g = blockIdx.y;
   const int G = Hq / H;
   const int part = threadIdx.x & 15;        // 16-byte piece of a 256-byte key
-  const int grp = (threadIdx.x >> 4) & 3;   // key of the wave instruction
+  const int grp = (threadIdx.x >> 4) & 3;   // key of the load instruction
   const int w = threadIdx.x >> 6;
   const int cap = ccap[b];
   const int C = min(max(clen[b], 0), min(cap, c_max_len));
@@ -136,59 +147,105 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) qs[j] += f[j];
   }
-  const int c_wave = (blockIdx.x * 4 + w) * (4 * kCPL);  // first chunk of this wave
-  float dot[kCPL];
-  if (CK_DT == TF_DTYPE_FP32) {
+  const uint16_t* keys = ck + (size_t)cbase[b] + (size_t)g * cap * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)keys, (short)0, C * (int)(kHeadDim * sizeof(uint16_t)), 0x00020000);
+  float* out = scores + ((size_t)b * H + g) * c_max;
+  const int nblk = (c_max + kScoreBlock - 1) / kScoreBlock;
+  const int stride = gridDim.x * kScoreWaves;
+  const unsigned lane_off = (unsigned)grp * 256u + 16u * part;
+  auto fetch = [&](int blk, u32x4 (&x)[kScoreLoads]) {
 #pragma unroll
-    for (int i = 0; i < kCPL; ++i) {
-      const int c = c_wave + 4 * i + grp;
-      float acc = 0.f;
-      if (c < C) {
-        const float* row = (const float*)ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
-        const f32x4 x0 = __builtin_nontemporal_load((const f32x4*)row);
-        const f32x4 x1 = __builtin_nontemporal_load((const f32x4*)(row + 4));
-        acc = qs[0] * x0[0] + qs[1] * x0[1] + qs[2] * x0[2] + qs[3] * x0[3];
-        acc = fmaf(qs[4], x1[0], fmaf(qs[5], x1[1], fmaf(qs[6], x1[2], fmaf(qs[7], x1[3], acc))));
-      }
-      dot[i] = acc;
-    }
-  } else {
-    u32x4 x[kCPL];
-    // (a wave wholly past C -- padding of a shorter sequence -- loads nothing)
-    const bool any = c_wave < C;
+    for (int i = 0; i < kScoreLoads; ++i)  // (cache policy 2: nontemporal)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)blk * (kScoreLoads * 1024u) + i * 1024u + lane_off,
+                                                   0, 2);
+  };
+  auto score = [&](int blk, const u32x4 (&x)[kScoreLoads]) {
+    float dot[kScoreLoads];
 #pragma unroll
-    for (int i = 0; i < kCPL; ++i) {
-      x[i] = u32x4{0u, 0u, 0u, 0u};
-      if (any) {  // chunks past C read chunk C - 1 (in bounds) and are masked below
-        const int c = min(c_wave + 4 * i + grp, C - 1);
-        x[i] = __builtin_nontemporal_load(
-            (const u32x4*)((const uint16_t*)ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kCPL; ++i) {
+    for (int i = 0; i < kScoreLoads; ++i) {
       float f[8];
       widen8(CK_DT, x[i], f);
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc = fmaf(qs[j], f[j], acc);
-      dot[i] = (c_wave + 4 * i + grp < C) ? acc : 0.f;
+      acc += __shfl_xor(acc, 8, 16);
+      acc += __shfl_xor(acc, 4, 16);
+      acc += __shfl_xor(acc, 2, 16);
+      acc += __shfl_xor(acc, 1, 16);
+      dot[i] = acc;
     }
-  }
+    // lane `part` of key group `grp` writes chunk blk * kScoreBlock + 4 part + grp
+    if (part < kScoreLoads) {
+      float v = dot[0];
 #pragma unroll
-  for (int i = 0; i < kCPL; ++i) {
-    float v = dot[i];
-    v += __shfl_xor(v, 8, 16);
-    v += __shfl_xor(v, 4, 16);
-    v += __shfl_xor(v, 2, 16);
-    v += __shfl_xor(v, 1, 16);
-    dot[i] = v;
+      for (int i = 1; i < kScoreLoads; ++i)
+        if (part == i) v = dot[i];
+      const int c = blk * kScoreBlock + 4 * part + grp;
+      if (c < c_max) out[c] = (c < C) ? v : -__builtin_huge_valf();
+    }
+  };
+  int blk = blockIdx.x * kScoreWaves + w;
+  u32x4 xa[kScoreLoads], xb[kScoreLoads];
+  fetch(blk, xa);
+  // (a wave with one block issues no second batch: out-of-range loads still
+  // occupy the wave, measured 0.4-1 us slower per launch at one block per wave)
+  if (blk + stride < nblk) fetch(blk + stride, xb);
+  while (true) {
+    if (blk >= nblk) break;
+    score(blk, xa);
+    fetch(blk + 2 * stride, xa);
+    blk += stride;
+    if (blk >= nblk) break;
+    score(blk, xb);
+    fetch(blk + 2 * stride, xb);
+    blk += stride;
   }
-  // lane `part` of key group `grp` writes chunk c_wave + 4 part + grp
-  if (part < kCPL) {
+}
+
+// a2, fp32 chunk keys: grid (ceil(c_max / 64), H, B), 256 threads; each wave
+// scores 16 consecutive chunks, 4 per lane group.
+__global__ __launch_bounds__(256) void score_kernel_f32(
+    const uint16_t* __restrict__ q, int32_t q_dtype, int32_t Hq, int32_t H, const float* __restrict__ ck,
+    const int64_t* __restrict__ cbase, const int32_t* __restrict__ ccap, const int32_t* __restrict__ clen,
+    int32_t c_max_len, float* __restrict__ scores, int32_t c_max) {
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int G = Hq / H;
+  const int part = threadIdx.x & 15;
+  const int grp = (threadIdx.x >> 4) & 3;
+  const int w = threadIdx.x >> 6;
+  const int cap = ccap[b];
+  const int C = min(max(clen[b], 0), min(cap, c_max_len));
+  float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < G; ++h) {
+    float f[8];
+    widen8(q_dtype, *(const u32x4*)(q + ((size_t)b * Hq + (size_t)g * G + h) * kHeadDim + 8 * part), f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qs[j] += f[j];
+  }
+  const int c_wave = (blockIdx.x * 4 + w) * 16;
+  float dot[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = c_wave + 4 * i + grp;
+    float acc = 0.f;
+    if (c < C) {
+      const float* row = ck + (size_t)cbase[b] + ((size_t)g * cap + c) * kHeadDim + 8 * part;
+      const f32x4 x0 = __builtin_nontemporal_load((const f32x4*)row);
+      const f32x4 x1 = __builtin_nontemporal_load((const f32x4*)(row + 4));
+      acc = qs[0] * x0[0] + qs[1] * x0[1] + qs[2] * x0[2] + qs[3] * x0[3];
+      acc = fmaf(qs[4], x1[0], fmaf(qs[5], x1[1], fmaf(qs[6], x1[2], fmaf(qs[7], x1[3], acc))));
+    }
+    acc += __shfl_xor(acc, 8, 16);
+    acc += __shfl_xor(acc, 4, 16);
+    acc += __shfl_xor(acc, 2, 16);
+    acc += __shfl_xor(acc, 1, 16);
+    dot[i] = acc;
+  }
+  if (part < 4) {
     float v = dot[0];
 #pragma unroll
-    for (int i = 1; i < kCPL; ++i)
+    for (int i = 1; i < 4; ++i)
       if (part == i) v = dot[i];
     const int c = c_wave + 4 * part + grp;
     if (c < c_max) scores[((size_t)b * H + g) * c_max + c] = (c < C) ? v : -__builtin_huge_valf();
@@ -197,21 +254,22 @@ __global__ __launch_bounds__(256) void score_kernel(
 
 hipError_t launch_scores(const uint16_t* q, int32_t q_dtype, int32_t Hq, const void* ck,
                          const tf_kv_desc& ckd, float* scores, int32_t c_max, hipStream_t stream) {
-  const dim3 grid((c_max + 16 * kCPL - 1) / (16 * kCPL), ckd.H, ckd.B), block(256);  // 4 waves x 4 keys x kCPL
-  switch (ckd.dtype) {
-    case TF_DTYPE_BF16:
-      hipLaunchKernelGGL(score_kernel<TF_DTYPE_BF16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
-                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
-      break;
-    case TF_DTYPE_FP16:
-      hipLaunchKernelGGL(score_kernel<TF_DTYPE_FP16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
-                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
-      break;
-    default:
-      hipLaunchKernelGGL(score_kernel<TF_DTYPE_FP32>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, ck,
-                         ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
-      break;
+  if (ckd.dtype == TF_DTYPE_FP32) {
+    const dim3 grid((c_max + 63) / 64, ckd.H, ckd.B), block(256);
+    hipLaunchKernelGGL(score_kernel_f32, grid, block, 0, stream, q, q_dtype, Hq, ckd.H, (const float*)ck,
+                       ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
+    return hipGetLastError();
   }
+  const long heads = (long)ckd.H * ckd.B;
+  const int nblk = (c_max + kScoreBlock - 1) / kScoreBlock;
+  const int nx = (int)min(max(1L, (long)kScoreWgs / heads), (long)(nblk + kScoreWaves - 1) / kScoreWaves);
+  const dim3 grid(nx, ckd.H, ckd.B), block(kScoreWaves * 64);
+  if (ckd.dtype == TF_DTYPE_BF16)
+    hipLaunchKernelGGL(score_kernel<TF_DTYPE_BF16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H,
+                       (const uint16_t*)ck, ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
+  else
+    hipLaunchKernelGGL(score_kernel<TF_DTYPE_FP16>, grid, block, 0, stream, q, q_dtype, Hq, ckd.H,
+                       (const uint16_t*)ck, ckd.seq_base, ckd.seq_cap, ckd.seq_len, ckd.max_len, scores, c_max);
   return hipGetLastError();
 }
 

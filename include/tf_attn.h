@@ -108,6 +108,7 @@ int tf_build_chunk_keys(const void* K, const tf_kv_desc* kv, int32_t chunk_size,
  *            unless ckd->dtype is TF_DTYPE_FP32.
  *   ck     : device, described by ckd (seq_len = chunk counts, max_len <= c_max).
  *   scores : device fp32 [B][H][c_max].
+ * c_max above 1 << 22 (4,194,304 chunks) returns TF_ERR_UNSUPPORTED.
  */
 int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq,
                     const void* ck, const tf_kv_desc* ckd,

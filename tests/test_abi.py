@@ -93,6 +93,7 @@ def test_other_entry_points_validate():
     assert L.tf_score_chunks(FAKE, T.TF_DTYPE_BF16, 6, FAKE, ctypes.byref(kv), FAKE, 200, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_score_chunks(FAKE, T.TF_DTYPE_BF16, 4, FAKE, ctypes.byref(kv), FAKE, 50, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_score_chunks(FAKE, T.TF_DTYPE_FP16, 4, FAKE, ctypes.byref(kv), FAKE, 200, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_score_chunks(FAKE, T.TF_DTYPE_BF16, 4, FAKE, ctypes.byref(kv), FAKE, (1 << 22) + 1, None) == T.TF_ERR_UNSUPPORTED
     assert L.tf_select_topk(FAKE, 1, 4, 100, FAKE, 0, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_select_topk(FAKE, 1, 4, (1 << 20) + 1, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_UNSUPPORTED
     assert L.tf_select_topk(None, 1, 4, 100, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG

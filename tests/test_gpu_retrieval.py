@@ -108,8 +108,9 @@ def test_scores_parity(Hq, Hkv, ck_dtype):
 
 @pytest.mark.parametrize("ck_dtype", ["bf16", "fp16"])
 def test_scores_ragged_rows(ck_dtype):
-    # 64 rows of a c_max = 8200 score array: full rows, a row of 3 chunks and
-    # an empty one (all -inf), the grid's last workgroup of each row partial
+    # 64 rows of a c_max = 8200 score array: more 16-chunk blocks per row than
+    # waves in the grid for it, so waves score several blocks, the last round
+    # ragged; a row of 3 chunks and an empty one are -inf past their keys
     B, H, c_max = 4, 16, 8200
     C = [8192, 8000, 3, 0]
     lay = synth.KVLayout.build(C, H, 128, caps=[max(c, 1) for c in C])
