@@ -9,18 +9,24 @@
 // kSlice entries and the work spread over (slice, row, sequence):
 //  1. accept_stats_kernel, per (slice, row, sequence): the slice's largest
 //     logit (lowest index on ties) and sum of exp(x / T - slice max / T);
-//  2. accept_slice_kernel, per (draw slice of kDraw entries, sequence): every
+//  2. accept_slice_kernel (accept_slice_small_kernel for 1 .. kFastGamma
+//     drafts), per (draw slice of kDraw entries, sequence): every
 //     workgroup takes the chain decision itself (one thread per draft, from
 //     the row statistics), then sums its slice of the draw's weights --
 //     max(0, p_j - q_j) after a rejection at j, p_gamma when all drafts are
 //     kept -- and of p_j (the fallback when the residual vanishes through
 //     rounding);
+//     and stores the slice's weights of both kinds;
 //  3. accept_final_kernel, per sequence: the draw slice whose running sum
 //     first passes u * total, then one block prefix sum over that slice's
-//     weights for the entry (inverse CDF, strict '>').
+//     stored weights for the entry (inverse CDF, strict '>').
 // The draw is bound by fp64 exponentials (two per vocabulary entry): a first
 // version ran it in one workgroup per sequence (70 us at V = 32000), 4096-entry
-// draw slices 25 us; 1024-entry slices spread it over 32 workgroups.
+// draw slices 25 us; 1024-entry slices spread it over 32 workgroups.  The
+// final kernel once recomputed its slice's weights (two row merges and two
+// exponentials per entry after the slice was found); reading the stored
+// weights instead took it from 10.5 to 5.3 us, and the small-chain form of
+// kernel 2 (below) the call from 34.6 to 19.7 us (gamma = 6, V = 32000).
 #include "tf_internal.h"
 
 namespace tfk {
@@ -77,9 +83,11 @@ __device__ __forceinline__ int block_max(int x, int* s) {
 // kPer loads per thread are issued together (index clamped into the row).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(const float* __restrict__ target,
-                                                                   const float* __restrict__ draft, int32_t gamma,
+                                                                   const float* __restrict__ draft,
+                                                                   const int32_t* __restrict__ tokens, int32_t gamma,
                                                                    int32_t V, float temperature, int32_t nslices,
-                                                                   SliceStat* __restrict__ stats) {
+                                                                   SliceStat* __restrict__ stats,
+                                                                   float* __restrict__ xlog) {
   __shared__ float s_v[kAccThreads / 64];
   __shared__ int s_i[kAccThreads / 64];
   __shared__ double s_z[kAccThreads / 64];
@@ -91,6 +99,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(const float* 
                                   : draft + ((size_t)b * gamma + (r - gamma - 1)) * V;
   const int v0 = slice * kSlice, v1 = min(V, v0 + kSlice);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the drafted token this row is tested at (target rows 0 .. gamma-1, every draft row)
+  const int xt = (r == gamma) ? -1 : tokens[(size_t)b * gamma + (r < gamma ? r : r - gamma - 1)];
   float x[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) x[k] = row[min(v0 + (int)threadIdx.x + kAccThreads * k, V - 1)];
@@ -145,6 +155,15 @@ __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(const float* 
     st.amax = bi;
     st.z = z;
     stats[((size_t)b * nrows + r) * nslices + slice] = st;
+  }
+  // the row's logit at its drafted token, from the thread holding that entry
+  if (xt >= v0 && xt < v1 && (int)threadIdx.x == (xt - v0) % kAccThreads) {
+    const int kk = (xt - v0) / kAccThreads;
+    float xv = x[0];
+#pragma unroll
+    for (int k = 1; k < kPer; ++k)
+      if (k == kk) xv = x[k];
+    xlog[(size_t)b * nrows + r] = xv;
   }
 }
 
@@ -248,7 +267,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_slice_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
     const double* __restrict__ uniforms, int32_t gamma, int32_t V, float temperature, int32_t probs,
     const SliceStat* __restrict__ stats, int32_t nslices, int32_t ndraw, SliceSum* __restrict__ sums,
-    int32_t* __restrict__ js) {
+    int32_t* __restrict__ js, double* __restrict__ weights) {
   __shared__ int s_j;
   __shared__ double s_d[kAccThreads / 64];
   __shared__ int s_i[kAccThreads / 64];
@@ -264,6 +283,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_slice_kernel(
   const float* tr = trow0 + (size_t)j * V;
   const float* dr = drow0 + (size_t)(residual ? j : 0) * V;
   const int v0 = slice * kDraw, v1 = min(V, v0 + kDraw);
+  double* wr = weights + (size_t)b * 2 * V;  // the draw's weights, then p_j's
+  double* wp = wr + V;
   float xp[kDrawPer], xq[kDrawPer];
 #pragma unroll
   for (int k = 0; k < kDrawPer; ++k) {
@@ -282,6 +303,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_slice_kernel(
     if (v >= v1) continue;
     const double p = dist_of(dp, xp[k], v, t);
     const double r = residual ? fmax(0.0, p - dist_of(dq, xq[k], v, t)) : p;
+    wr[v] = r;
+    wp[v] = p;
     sr += r;
     sp += p;
     if (r > 0.0) lr = v;
@@ -309,9 +332,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_slice_kernel(
 // entries, so a prefix sum in thread order is one in index order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kAccThreads) void accept_final_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, const double* __restrict__ uniforms,
-    int32_t gamma, int32_t V, float temperature, int32_t probs, const SliceStat* __restrict__ stats, int32_t nslices,
-    int32_t ndraw, const SliceSum* __restrict__ sums, const int32_t* __restrict__ js, int32_t* __restrict__ n_acc,
+    const double* __restrict__ uniforms, int32_t gamma, int32_t V, int32_t ndraw, const SliceSum* __restrict__ sums,
+    const int32_t* __restrict__ js, const double* __restrict__ weights, int32_t* __restrict__ n_acc,
     int32_t* __restrict__ next) {
   __shared__ int s_slice, s_use_r, s_found, s_last;
   __shared__ double s_before, s_tgt;
@@ -365,36 +387,18 @@ __global__ __launch_bounds__(kAccThreads) void accept_final_kernel(
     }
     return;
   }
-  const bool residual = j < gamma && s_use_r;
-  const int nrows = 2 * gamma + 1;
-  const SliceStat* st = stats + (size_t)b * nrows * nslices;
-  const float* tr = target + ((size_t)b * (gamma + 1) + j) * V;
-  const float* dr = draft + ((size_t)b * gamma + (residual ? j : 0)) * V;
+  const double* wsrc = weights + (size_t)b * 2 * V + (s_use_r ? 0 : V);
   const int e0 = slice * kDraw + (int)threadIdx.x * kDrawPer;
-  float xp[kDrawPer], xq[kDrawPer];
-#pragma unroll
-  for (int k = 0; k < kDrawPer; ++k) {
-    const int v = min(e0 + k, V - 1);
-    xp[k] = tr[v];
-    xq[k] = residual ? dr[v] : 0.f;
-  }
-  const RowDist dp = merge_row(st + (size_t)j * nslices, nslices, temperature, probs);
-  const RowDist dq = residual ? merge_row(st + (size_t)(gamma + 1 + j) * nslices, nslices, temperature, probs) : dp;
-  const double t = (double)temperature;
   double wv[kDrawPer];
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) wv[k] = wsrc[min(e0 + k, V - 1)];
   double local = 0.0;
   int last_pos = -1;
 #pragma unroll
   for (int k = 0; k < kDrawPer; ++k) {
-    const int v = e0 + k;
-    double r = 0.0;
-    if (v < V) {
-      const double p = dist_of(dp, xp[k], v, t);
-      r = residual ? fmax(0.0, p - dist_of(dq, xq[k], v, t)) : p;
-    }
-    wv[k] = r;
-    local += r;
-    if (r > 0.0) last_pos = v;
+    if (e0 + k >= V) wv[k] = 0.0;
+    local += wv[k];
+    if (wv[k] > 0.0) last_pos = e0 + k;
   }
   // exclusive prefix of the per-thread sums, in thread order
   double incl = local;
@@ -425,6 +429,175 @@ __global__ __launch_bounds__(kAccThreads) void accept_final_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 2, chains of 1 .. kFastGamma drafts: the same decision and draw
+// slice with the memory round trips overlapped.  Every load is issued at the
+// start: this thread's kDrawPer draw entries of every candidate row (target
+// rows 0 .. gamma, draft rows 0 .. gamma-1: whichever the decision picks is
+// already in registers), the slice statistics of every row, the drafted
+// tokens with their logits (recorded by the statistics kernel) and the
+// uniforms.  The rows' distributions are merged 16 lanes per row (lane s
+// takes slice s: one exponential each, then the serial sum in slice order,
+// so each equals the one merge_row gives).
+// ---------------------------------------------------------------------------
+constexpr int kFastGamma = 7;
+
+__global__ __launch_bounds__(kAccThreads) void accept_slice_small_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
+    const double* __restrict__ uniforms, int32_t gamma, int32_t V, float temperature, int32_t probs,
+    const SliceStat* __restrict__ stats, const float* __restrict__ xlog, int32_t nslices, int32_t ndraw,
+    SliceSum* __restrict__ sums, int32_t* __restrict__ js, double* __restrict__ weights) {
+  __shared__ RowDist s_rd[2 * kFastGamma + 1];
+  __shared__ int s_j;
+  __shared__ double s_d[kAccThreads / 64];
+  __shared__ int s_i[kAccThreads / 64];
+  const int tid = threadIdx.x;
+  const int slice = (int)(blockIdx.x % (unsigned)ndraw);
+  const int b = (int)(blockIdx.x / (unsigned)ndraw);
+  const int nrows = 2 * gamma + 1;
+  const float* trow0 = target + (size_t)b * (gamma + 1) * V;
+  const float* drow0 = draft + (size_t)b * gamma * V;
+  const int v0 = slice * kDraw, v1 = min(V, v0 + kDraw);
+
+  float cp[kFastGamma + 1][kDrawPer], cq[kFastGamma][kDrawPer];
+#pragma unroll
+  for (int jj = 0; jj <= kFastGamma; ++jj) {
+    const float* tr = trow0 + (size_t)min(jj, gamma) * V;
+#pragma unroll
+    for (int k = 0; k < kDrawPer; ++k) cp[jj][k] = tr[min(v0 + tid + kAccThreads * k, V - 1)];
+  }
+#pragma unroll
+  for (int jj = 0; jj < kFastGamma; ++jj) {
+    const float* dr = drow0 + (size_t)min(jj, gamma - 1) * V;
+#pragma unroll
+    for (int k = 0; k < kDrawPer; ++k) cq[jj][k] = dr[min(v0 + tid + kAccThreads * k, V - 1)];
+  }
+  int xtok = -1;
+  float lt = 0.f, ld = 0.f;
+  double ui = 0.0;
+  if (tid < gamma) {
+    xtok = tokens[(size_t)b * gamma + tid];
+    ui = uniforms[(size_t)b * (gamma + 1) + tid];
+    if (!probs) {
+      lt = xlog[(size_t)b * nrows + tid];
+      ld = xlog[(size_t)b * nrows + gamma + 1 + tid];
+    }
+  }
+  if (tid == 0) s_j = gamma;
+
+  // row distributions, 16 lanes per row
+  {
+    const int l16 = tid & 15, r = tid >> 4;
+    const bool live = r < nrows && l16 < nslices;
+    SliceStat x;
+    x.mx = -__builtin_huge_valf();
+    x.amax = 0x7fffffff;
+    x.z = 0.0;
+    if (live && !probs) x = stats[((size_t)b * nrows + r) * nslices + l16];
+    float bv = x.mx;
+    int bi = x.amax;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 16);
+      const int oi = __shfl_xor(bi, off, 16);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    RowDist d;
+    d.zmax = 0.0;
+    d.Z = 1.0;
+    d.invZ = 1.0;
+    d.amax = bi;
+    d.mode = probs ? 2 : (temperature == 0.f ? 1 : 0);
+    if (d.mode == 0) {
+      const double t = (double)temperature;
+      d.zmax = (double)bv / t;
+      const double e = (live && x.z > 0.0) ? x.z * exp((double)x.mx / t - d.zmax) : 0.0;
+      double Z = 0.0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) Z += __shfl(e, q, 16);
+      d.Z = Z;
+      d.invZ = 1.0 / Z;
+    }
+    if (r < nrows && l16 == 0) s_rd[r] = d;
+  }
+  __syncthreads();
+
+  // the chain decision: threads i < gamma test draft i
+  const double t = (double)temperature;
+  if (tid < gamma) {
+    bool keep = false;
+    if (xtok >= 0 && xtok < V) {  // a token outside [0, V) is never kept
+      if (probs) {
+        lt = trow0[(size_t)tid * V + xtok];
+        ld = drow0[(size_t)tid * V + xtok];
+      }
+      const double px = dist_of(s_rd[tid], lt, xtok, t);
+      const double qx = dist_of(s_rd[gamma + 1 + tid], ld, xtok, t);
+      if (px > 0.0) {
+        const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
+        keep = alpha >= ui;
+      }
+    }
+    if (!keep) atomicMin(&s_j, tid);
+  }
+  __syncthreads();
+  const int j = s_j;
+  const bool residual = j < gamma;
+  float xp[kDrawPer], xq[kDrawPer];
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    xp[k] = cp[0][k];
+    xq[k] = cq[0][k];
+  }
+#pragma unroll
+  for (int jj = 1; jj <= kFastGamma; ++jj)
+    if (jj == j) {
+#pragma unroll
+      for (int k = 0; k < kDrawPer; ++k) xp[k] = cp[jj][k];
+    }
+#pragma unroll
+  for (int jj = 1; jj < kFastGamma; ++jj)
+    if (jj == j) {
+#pragma unroll
+      for (int k = 0; k < kDrawPer; ++k) xq[k] = cq[jj][k];
+    }
+  const RowDist dp = s_rd[j];
+  const RowDist dq = residual ? s_rd[gamma + 1 + j] : dp;
+  double* wr = weights + (size_t)b * 2 * V;  // the draw's weights, then p_j's
+  double* wp = wr + V;
+  double sr = 0.0, sp = 0.0;
+  int lr = -1, lp = -1;
+#pragma unroll
+  for (int k = 0; k < kDrawPer; ++k) {
+    const int v = v0 + tid + kAccThreads * k;
+    if (v >= v1) continue;
+    const double p = dist_of(dp, xp[k], v, t);
+    const double r = residual ? fmax(0.0, p - dist_of(dq, xq[k], v, t)) : p;
+    wr[v] = r;
+    wp[v] = p;
+    sr += r;
+    sp += p;
+    if (r > 0.0) lr = v;
+    if (p > 0.0) lp = v;
+  }
+  sr = block_sum(sr, s_d);
+  sp = block_sum(sp, s_d);
+  lr = block_max(lr, s_i);
+  lp = block_max(lp, s_i);
+  if (tid == 0) {
+    SliceSum o;
+    o.r = sr;
+    o.p = sp;
+    o.last_r = lr;
+    o.last_p = lp;
+    sums[(size_t)b * ndraw + slice] = o;
+    if (slice == 0) js[b] = j;
+  }
+}
+
 size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 0 || V < 1) return 0;
   const size_t nslices = (size_t)(V + kSlice - 1) / kSlice;
@@ -432,7 +605,8 @@ size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V) {
   const size_t a = ((size_t)B * (2 * gamma + 1) * nslices * sizeof(SliceStat) + 255) & ~(size_t)255;
   const size_t b = ((size_t)B * ndraw * sizeof(SliceSum) + 255) & ~(size_t)255;
   const size_t c = ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
-  return a + b + c;
+  const size_t x = ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
+  return a + b + c + x + (size_t)B * 2 * V * sizeof(double);
 }
 
 int32_t accept_max_vocab() { return kSlice * kMaxSlices; }
@@ -450,19 +624,29 @@ hipError_t launch_accept(const float* target, const float* draft, const int32_t*
   SliceSum* sums = (SliceSum*)(w + a);
   const size_t bsz = ((size_t)B * ndraw * sizeof(SliceSum) + 255) & ~(size_t)255;
   int32_t* js = (int32_t*)(w + a + bsz);
+  const size_t csz = ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
+  float* xlog = (float*)(w + a + bsz + csz);
+  const size_t xsz = ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
+  double* weights = (double*)(w + a + bsz + csz + xsz);
   if (!probs) {
     const unsigned blocks = (unsigned)nslices * (unsigned)(2 * gamma + 1) * (unsigned)B;
-    hipLaunchKernelGGL(accept_stats_kernel, dim3(blocks), dim3(kAccThreads), 0, stream, target, draft, gamma, V,
-                       temperature, nslices, stats);
+    hipLaunchKernelGGL(accept_stats_kernel, dim3(blocks), dim3(kAccThreads), 0, stream, target, draft, tokens, gamma,
+                       V, temperature, nslices, stats, xlog);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(accept_slice_kernel, dim3((unsigned)ndraw * (unsigned)B), dim3(kAccThreads), 0, stream, target,
-                     draft, tokens, uniforms, gamma, V, temperature, probs, stats, nslices, ndraw, sums, js);
+  if (gamma >= 1 && gamma <= kFastGamma)
+    hipLaunchKernelGGL(accept_slice_small_kernel, dim3((unsigned)ndraw * (unsigned)B), dim3(kAccThreads), 0, stream,
+                       target, draft, tokens, uniforms, gamma, V, temperature, probs, stats, xlog, nslices, ndraw, sums,
+                       js, weights);
+  else
+    hipLaunchKernelGGL(accept_slice_kernel, dim3((unsigned)ndraw * (unsigned)B), dim3(kAccThreads), 0, stream,
+                       target, draft, tokens, uniforms, gamma, V, temperature, probs, stats, nslices, ndraw, sums, js,
+                       weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_final_kernel, dim3(B), dim3(kAccThreads), 0, stream, target, draft, uniforms, gamma, V,
-                     temperature, probs, stats, nslices, ndraw, sums, js, n_acc, next);
+  hipLaunchKernelGGL(accept_final_kernel, dim3(B), dim3(kAccThreads), 0, stream, uniforms, gamma, V, ndraw, sums, js,
+                     weights, n_acc, next);
   return hipGetLastError();
 }
 

@@ -243,7 +243,8 @@ int tf_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* tree_ma
  *   target: device fp32 [B][gamma+1][V]; draft: device fp32 [B][gamma][V];
  *   draft_tokens: device int32 [B][gamma] (each in [0, V)); uniforms: device
  *   fp64 [B][gamma+1] in (0, 1).  Outputs: device int32 [B].
- *   ws: tf_accept_workspace_size(B, gamma, V) bytes (per-row statistics).
+ *   ws: tf_accept_workspace_size(B, gamma, V) bytes (per-row statistics and
+ *       the draw's fp64 weights, 16 V bytes per sequence).
  *   Limits: V <= 65536, gamma <= 1024, B * (2 gamma + 1) * ceil(V / 4096) < 2^31.
  */
 #define TF_ACCEPT_PROBS 1

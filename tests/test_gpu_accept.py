@@ -135,3 +135,28 @@ def test_vocabulary_slicing_bit_exact(V, T):
         rn, rnext, margin = oracle.accept(a.target[b], a.draft[b], tokens[b], a.uniforms[b], T)
         if margin >= 1e-12:
             assert (n[b], nxt[b]) == (rn, rnext), b
+
+
+@pytest.mark.parametrize("gamma", [1, 7, 8, 20])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_chain_lengths_bit_exact(gamma, T):
+    """Chains at and around the length where the kernel switches from keeping
+    every candidate row in registers (1 .. 7 drafts) to loading the chosen row
+    after the decision: bit-exact against the oracle."""
+    B, V = 16, 32000
+    a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=True, seed=26 + gamma)
+    rng = np.random.default_rng(27)
+    tokens = a.tokens.copy()
+    for b in range(B):
+        for i in range(gamma):
+            q = oracle.distribution(a.draft[b, i], T if T > 0 else 1.0)
+            tokens[b, i] = rng.choice(V, p=q / q.sum())
+    n, nxt = run(a.target, a.draft, tokens, a.uniforms, T)
+    guarded = 0
+    for b in range(B):
+        rn, rnext, margin = oracle.accept(a.target[b], a.draft[b], tokens[b], a.uniforms[b], T)
+        if margin < 1e-12:
+            guarded += 1
+            continue
+        assert (n[b], nxt[b]) == (rn, rnext), b
+    assert guarded <= 1
