@@ -148,6 +148,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
     for (int j = 0; j < 8; ++j) qs[j] += f[j];
   }
   const uint16_t* keys = ck + (size_t)cbase[b] + (size_t)g * cap * kHeadDim;
+  // raw buffer (stride 0, size in bytes); 0x00020000 is the descriptor's last
+  // word on this target: 32-bit data format, no swizzle, no index
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)keys, (short)0, C * (int)(kHeadDim * sizeof(uint16_t)), 0x00020000);
   float* out = scores + ((size_t)b * H + g) * c_max;
