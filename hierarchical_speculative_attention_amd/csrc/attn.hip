@@ -980,7 +980,11 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
   const long per_head = target_wgs / heads;  // splits per (sequence, KV head) that keep the grid within target
   long tpw = max_tpw;
   if (per_head >= 1) {
-    long fit = ((long)max_virtual + per_head - 1) / per_head;
+    // whole rounds of per_head splits: one when the splits fit max_tpw, else
+    // as few as do (a last round of a few long splits would run on its own)
+    const long rounds = ((long)max_virtual + per_head * max_tpw - 1) / (per_head * max_tpw);
+    const long n = per_head * max(1L, rounds);
+    long fit = ((long)max_virtual + n - 1) / n;
     fit = max(128L, (fit + kTile - 1) / kTile * kTile);
     if (fit < tpw) tpw = fit;
   }

@@ -55,10 +55,11 @@ struct SplitPlan {
 };
 
 // Virtual tokens per workgroup: the fewest (a multiple of the tile, at least
-// 128, at most max_tpw) that keep the grid within target_wgs workgroups, the
-// number resident at once.  A grid a little past that would leave its last
+// 128, at most max_tpw) that give the grid a whole number of rounds of
+// target_wgs workgroups, the number resident at once -- one round when
+// max_tpw allows.  A grid a little past a whole round would leave its last
 // workgroups to start only when the first ones finish.
-constexpr int32_t kVerifyMaxTpw = 4096;
+constexpr int32_t kVerifyMaxTpw = 8192;
 constexpr int32_t kSparseMaxTpw = 1024;
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
                       int32_t max_tpw);
