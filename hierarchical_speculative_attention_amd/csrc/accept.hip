@@ -27,6 +27,7 @@
 // exponentials per entry after the slice was found); reading the stored
 // weights instead took it from 10.5 to 5.3 us, and the small-chain form of
 // kernel 2 (below) the call from 34.6 to 19.7 us (gamma = 6, V = 32000).
+// (kFastGamma = 15 keeps 31 rows x 4 entries in registers per thread.)
 #include "tf_internal.h"
 
 namespace tfk {
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_final_kernel(
 // takes slice s: one exponential each, then the serial sum in slice order,
 // so each equals the one merge_row gives).
 // ---------------------------------------------------------------------------
-constexpr int kFastGamma = 7;
+constexpr int kFastGamma = 15;
 
 __global__ __launch_bounds__(kAccThreads) void accept_slice_small_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
@@ -486,8 +487,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_slice_small_kernel(
   if (tid == 0) s_j = gamma;
 
   // row distributions, 16 lanes per row
-  {
-    const int l16 = tid & 15, r = tid >> 4;
+  for (int r0 = 0; r0 < nrows; r0 += kAccThreads / 16) {
+    const int l16 = tid & 15, r = r0 + (tid >> 4);
     const bool live = r < nrows && l16 < nslices;
     SliceStat x;
     x.mx = -__builtin_huge_valf();

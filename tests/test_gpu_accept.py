@@ -137,11 +137,11 @@ def test_vocabulary_slicing_bit_exact(V, T):
             assert (n[b], nxt[b]) == (rn, rnext), b
 
 
-@pytest.mark.parametrize("gamma", [1, 7, 8, 20])
+@pytest.mark.parametrize("gamma", [1, 8, 15, 16, 20])
 @pytest.mark.parametrize("T", [1.0, 0.0])
 def test_chain_lengths_bit_exact(gamma, T):
     """Chains at and around the length where the kernel switches from keeping
-    every candidate row in registers (1 .. 7 drafts) to loading the chosen row
+    every candidate row in registers (1 .. 15 drafts) to loading the chosen row
     after the decision: bit-exact against the oracle."""
     B, V = 16, 32000
     a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=True, seed=26 + gamma)
