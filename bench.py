@@ -38,6 +38,7 @@ SMALL_REPS = 8        # calls per graph for the once-per-step calls (accept), so
 CSRC = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "csrc")
 VERIFY_SRCS = [os.path.join(CSRC, f) for f in ("attn.hip", "api.hip", "tf_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_traffic.txt")
+DEFAULT_WORKLOAD = "llama2-7b-128k-32layers"  # the shape the committed traffic counters were taken on
 
 
 def parse():
@@ -45,7 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama2-7b-128k-32layers")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--budget", type=int, default=None, help="override the workload's token budget (retrieval)")
+    ap.add_argument("--gamma", type=int, default=None, help="override the workload's draft count (verify rows - 1)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers the CPU oracle baseline times")
@@ -108,6 +111,12 @@ def main():
     lens = W["lens"]
     layers = args.layers or W["layers"]
     cs, budget, gamma, vocab = W["chunk_size"], W["budget"], W["gamma"], W["vocab"]
+    if args.budget is not None:
+        budget = args.budget
+    if args.gamma is not None:
+        gamma = args.gamma
+    if budget < cs or gamma < 0:
+        raise SystemExit(f"budget {budget} must be at least one chunk ({cs}) and gamma >= 0")
     S, Wn = W["n_sink"], W["window"]
     Q = gamma + 1
     k = budget // cs
@@ -312,7 +321,8 @@ def main():
     step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
     verify_bytes = by["verify"]
     achieved = verify_bytes / verify_avg_s / 1e9
-    traffic = read_traffic()
+    # (the counters are of the verify launch at the default workload's shape)
+    traffic = read_traffic() if args.workload == DEFAULT_WORKLOAD and gamma == W["gamma"] else None
     ms_per_step = elapsed / args.steps * 1e3
 
     result = {

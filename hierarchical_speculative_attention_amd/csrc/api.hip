@@ -4,6 +4,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "tf_internal.h"
 
@@ -13,11 +15,34 @@ namespace {
 
 thread_local char g_detail[512] = "";
 
+// TF_LOG set (and not "0") in the environment: every rejected call prints its
+// status and detail, and every attention call its launch shape, to stderr.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("TF_LOG");
+    return e && e[0] && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void log_line(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[tf] %s\n", buf);
+}
+
+const char* status_name(int status);
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
   va_end(ap);
+  log_line("%s: %s", status_name(status), g_detail);
   return status;
 }
 
@@ -115,9 +140,7 @@ void fill_plan(tfk::AttnArgs& a, const tfk::SplitPlan& p, void* ws) {
   }
 }
 
-}  // namespace
-
-TF_EXPORT const char* tf_status_string(int status) {
+const char* status_name(int status) {
   switch (status) {
     case TF_OK: return "TF_OK";
     case TF_ERR_INVALID_ARG: return "TF_ERR_INVALID_ARG";
@@ -127,6 +150,17 @@ TF_EXPORT const char* tf_status_string(int status) {
   }
   return "TF_ERR_UNKNOWN";
 }
+
+// Launch of an attention call (after its checks passed), logged when TF_LOG is set.
+int attn_call(const char* fn, int dtype, int mode, const tfk::AttnArgs& a, hipStream_t stream) {
+  log_line("%s: B=%d Hq=%d H=%d rows/head=%d max_len=%d tokens/workgroup=%d splits=%d%s", fn, a.B, a.Hq, a.Hkv,
+           a.rows, a.max_len, a.tpw, a.nsplit, a.nsplit > 1 ? " (+ split merge)" : "");
+  return check_hip(tfk::launch_attn(dtype, mode, a, stream), fn);
+}
+
+}  // namespace
+
+TF_EXPORT const char* tf_status_string(int status) { return status_name(status); }
 
 TF_EXPORT const char* tf_last_error_detail(void) { return g_detail; }
 
@@ -231,7 +265,7 @@ TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const voi
   a.k = k;
   a.cs = chunk_size;
   fill_plan(a, plan, ws);
-  return check_hip(tfk::launch_attn(kv->dtype, tfk::kSparse, a, (hipStream_t)stream), "tf_sparse_attn");
+  return attn_call("tf_sparse_attn", kv->dtype, tfk::kSparse, a, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -275,7 +309,7 @@ TF_EXPORT int tf_sparse_verify_attn(const void* q, int32_t Hq, int32_t Q, const 
   a.cs = chunk_size;
   a.tail = tail;
   fill_plan(a, plan, ws);
-  return check_hip(tfk::launch_attn(kv->dtype, tfk::kSparseTail, a, (hipStream_t)stream), "tf_sparse_verify_attn");
+  return attn_call("tf_sparse_verify_attn", kv->dtype, tfk::kSparseTail, a, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -306,7 +340,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
   plan.rows_pad = ((a.rows + 15) / 16) * 16;
   plan.part_o_bytes = plan.part_ml_bytes = plan.total_bytes = 0;
   fill_plan(a, plan, nullptr);
-  return check_hip(tfk::launch_attn(sd->dtype, tfk::kStream, a, (hipStream_t)stream), "tf_stream_attn");
+  return attn_call("tf_stream_attn", sd->dtype, tfk::kStream, a, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -338,7 +372,7 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
   fill_plan(a, plan, ws);
-  return check_hip(tfk::launch_attn(kv->dtype, tfk::kVerify, a, (hipStream_t)stream), "tf_verify_attn");
+  return attn_call("tf_verify_attn", kv->dtype, tfk::kVerify, a, (hipStream_t)stream);
 }
 
 TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
@@ -364,7 +398,7 @@ TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const vo
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
   fill_plan(a, plan, ws);
   a.tmask = tree_mask;
-  return check_hip(tfk::launch_attn(kv->dtype, tfk::kVerifyTree, a, (hipStream_t)stream), "tf_verify_tree_attn");
+  return attn_call("tf_verify_tree_attn", kv->dtype, tfk::kVerifyTree, a, (hipStream_t)stream);
 }
 
 TF_EXPORT int tf_tree_masks(const int32_t* parent, int32_t B, int32_t Q, uint64_t* tree_mask, tf_stream_t stream) {

@@ -36,6 +36,9 @@
  *    explicitly ordered).  A workspace needs no initialisation: it only holds
  *    per-split partial results that each call writes before reading.
  *  - Caches must hold finite values.
+ *  - With TF_LOG set to anything but "0" in the environment, every rejected
+ *    call prints its status and detail, and every attention call its launch
+ *    shape (tokens per workgroup, split count), to stderr as "[tf] ..." lines.
  */
 #ifndef TF_ATTN_H
 #define TF_ATTN_H

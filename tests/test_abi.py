@@ -185,3 +185,30 @@ def test_tree_accept_validates():
     assert call(ws=None, ws_bytes=0) == T.TF_ERR_WORKSPACE
     assert L.tf_tree_accept_workspace_size(2, 100) >= 2 * 100 * 8
     assert call(B=0) == T.TF_OK
+
+
+LOG_PROBE = r"""
+import ctypes
+from hierarchical_speculative_attention_amd import _lib as T
+FAKE = ctypes.c_void_p(0x10000)
+kv = T.TfKvDesc(1, 4, 64, T.TF_DTYPE_BF16, FAKE.value, FAKE.value, FAKE.value, 100)
+st = T.lib().tf_verify_attn(FAKE, 4, 5, FAKE, FAKE, ctypes.byref(kv), FAKE, None, FAKE, 1 << 30, None)
+assert st == T.TF_ERR_UNSUPPORTED, st
+"""
+
+
+@pytest.mark.parametrize("value,logged", [("1", True), ("0", False), (None, False)])
+def test_tf_log_prints_rejected_calls(value, logged):
+    import subprocess
+    import sys
+    env = {k: v for k, v in os.environ.items() if k != "TF_LOG"}
+    if value is not None:
+        env["TF_LOG"] = value
+    r = subprocess.run([sys.executable, "-c", LOG_PROBE], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[tf] ")]
+    if logged:
+        assert lines == ["[tf] TF_ERR_UNSUPPORTED: kv: head dim 64 (only 128)"], r.stderr
+    else:
+        assert lines == [], r.stderr
