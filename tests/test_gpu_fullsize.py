@@ -172,3 +172,26 @@ def test_llama2_7b_128k_sparse_verify_with_tail():
         o, l = oracle.sparse_verify_attn(oracle.widen(qv_b[0, g], "bf16"), Kh, Vh, Kh.shape[0], ix[0, g],
                                          W["chunk_size"], tail)
         assert np.abs(o_h[0, g] - o).max() <= ATOL and np.abs(l_h[0, g] - l).max() <= ATOL
+
+
+def test_llama2_7b_128k_verify_in_a_larger_allocation():
+    # 512 rows allocated past the sequence (the three-tier loop's cache): the
+    # split plan takes two whole rounds of workgroups (32 splits of 4128 rows)
+    # instead of 16 splits of 8192 plus a second round of one; parity on heads
+    # of the first and last XCD groups
+    Q = 7
+    W = synth.WORKLOADS["llama2-7b-128k-1layer"]
+    K, V, qv, qd, lay, _ = synth.make_layer_torch(
+        lens=W["lens"], Hq=W["Hq"], Hkv=W["Hkv"], d=128, dtype="bf16", Q=Q, chunk_size=W["chunk_size"],
+        plant=None, seed=3, layer=0, device=DEV, extra_rows=512)
+    n = int(lay.seq_len[0])
+    kv = KVDesc.from_layout(lay, torch.bfloat16, DEV, max_len=n + 512)
+    o_v, l_v = tf.verify_attn(qv, K, V, kv)
+    torch.cuda.synchronize()
+    qv_b = host_bits(qv)
+    ov, lv = o_v.cpu().double().numpy(), l_v.cpu().double().numpy()
+    for g in (0, 13, 31):
+        Kh = oracle.widen(head_bits_gpu(K, lay, 0, g).reshape(-1, 128), "bf16")
+        Vh = oracle.widen(head_bits_gpu(V, lay, 0, g).reshape(-1, 128), "bf16")
+        o, l = oracle.verify_attn(oracle.widen(qv_b[0, g], "bf16"), Kh, Vh, n)
+        assert np.abs(ov[0, g] - o).max() <= ATOL and np.abs(lv[0, g] - l).max() <= ATOL
