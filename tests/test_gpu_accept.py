@@ -86,11 +86,11 @@ def test_gamma_zero_and_out_of_vocab_tokens():
 
 
 def test_losslessness_on_gpu():
-    """200k independent one-trial sequences in one call: the first emitted
+    """10^6 independent one-trial sequences in one call: the first emitted
     token follows p_0 and, when the first draft was kept, the second follows
     p_1 (chi-square at alpha = 1e-3)."""
     rng = np.random.default_rng(23)
-    V, gamma, B = 8, 3, 200000
+    V, gamma, B = 8, 3, 1000000
     p = rng.dirichlet(np.ones(V) * 0.7, gamma + 1)
     q = rng.dirichlet(np.ones(V) * 0.7, gamma)
     p[0, 5] = 0.0
