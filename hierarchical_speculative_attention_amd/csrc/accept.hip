@@ -8,15 +8,15 @@
 // precision as the fp64 reference.  The vocabulary is cut into slices of
 // kSlice entries and the work spread over (slice, row, sequence):
 //  1. accept_stats_kernel, per (slice, row, sequence): the slice's largest
-//     logit (lowest index on ties) and sum of exp(x / T - slice max / T);
+//     logit (lowest index on ties) and sum of exp(x / T - slice max / T),
+//     and the row's logit at its drafted token when that falls in the slice;
 //  2. accept_slice_kernel (accept_slice_small_kernel for 1 .. kFastGamma
 //     drafts), per (draw slice of kDraw entries, sequence): every
 //     workgroup takes the chain decision itself (one thread per draft, from
-//     the row statistics), then sums its slice of the draw's weights --
-//     max(0, p_j - q_j) after a rejection at j, p_gamma when all drafts are
-//     kept -- and of p_j (the fallback when the residual vanishes through
-//     rounding);
-//     and stores the slice's weights of both kinds;
+//     the row statistics), then stores and sums its slice of the draw's
+//     weights -- max(0, p_j - q_j) after a rejection at j, p_gamma when all
+//     drafts are kept -- and of p_j (the fallback when the residual vanishes
+//     through rounding);
 //  3. accept_final_kernel, per sequence: the draw slice whose running sum
 //     first passes u * total, then one block prefix sum over that slice's
 //     stored weights for the entry (inverse CDF, strict '>').
