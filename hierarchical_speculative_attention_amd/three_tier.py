@@ -170,20 +170,31 @@ class ThreeTierStep:
         for L in self.dr:
             tf.stream_attn(self.syn.draft_q, L.Ks, L.Vs, L.sd, self.S, self.W, out=self.o_d, stream=self.s)
 
-    def _run(self, key, body):
-        """body() now, eagerly, or as the replay of its graph (captured on first use)."""
-        if not self.graphs:
-            body()
-            return
-        g = self._g.get(key)
-        if g is None:
-            s = self.s
-            s.synchronize()
+    def _capture(self):
+        """Capture every graph a step can need before the first step: the
+        retrieval, a round for each count of unseen tokens (0-2) and parity
+        of the chain count, the one-row extension and Force 3.  Capturing
+        records the launches without running them, so no state changes."""
+        s = self.s
+        s.synchronize()
+        bodies = {"retrieval": self._retrieval, "extend": self._extend_one, "force3": self._force3}
+        for pend in range(3):
+            for cin in range(2):
+                bodies[("round", pend, cin)] = (lambda p=pend, c=cin: self._round(p, c))
+        for key, body in bodies.items():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 body()
             self._g[key] = g
-        g.replay()
+
+    def _run(self, key, body):
+        """body() now, eagerly, or as the replay of its graph."""
+        if not self.graphs:
+            body()
+            return
+        if not self._g:
+            self._capture()
+        self._g[key].replay()
 
     # -- the bodies --------------------------------------------------------------
     def _retrieval(self):
