@@ -323,9 +323,10 @@ int tf_commit_length(int32_t* seq_len, int32_t B, int32_t add, int32_t gamma, co
  *   [B][Q] (tokens[b][0] not read); uniforms: device fp64 [B][Q] in (0, 1).
  *   Outputs: n_accepted[b] = kept nodes; path[b][0 .. Q-2] = the kept nodes
  *   in order, then -1 (NULL allowed when Q = 1); next_token[b].
- *   ws: tf_tree_accept_workspace_size(B, V) bytes (per sequence two fp64 rows
- *     of V -- the residual and the current node's draft distribution -- and
- *     the per-slice statistics of up to 64 target and 64 draft rows).
+ *   ws: tf_tree_accept_workspace_size(B, V) bytes (per sequence three fp64
+ *     rows of V -- a stored residual, the current node's draft distribution
+ *     and the draw's weights -- the per-slice statistics of up to 64 target
+ *     and 64 draft rows, and the residuals' partial normalisers).
  *   Limits: Q <= 64, V <= 65536.
  */
 int tf_tree_accept(const float* target, const float* draft, const int32_t* tokens, const int32_t* parent,

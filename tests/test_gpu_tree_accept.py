@@ -139,3 +139,30 @@ def test_tree_accept_edge_shapes(V, T):
             assert int(n[b]) == len(rp) and int(nxt[b]) == rx, (Q, b)
             if Q > 1:
                 assert list(path[b, :n[b]]) == rp and np.all(path[b, n[b]:] == -1), (Q, b)
+
+
+@pytest.mark.parametrize("Q", [2, 3, 4, 9])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tree_accept_many_siblings(Q, T):
+    """A root with Q - 1 children drafted independently of the target: most
+    are rejected, so the walk uses the precomputed normalisers for the first
+    two rejections at a node, and the in-walk passes (and its own draw) from
+    the third on; bit-exact against the oracle."""
+    rng = np.random.default_rng(126 + Q + int(T))
+    B, V = 32, 32000
+    target = rng.normal(0, 2, (B, Q, V)).astype(np.float32)
+    draft = rng.normal(0, 2, (B, Q, V)).astype(np.float32)
+    parents = [[-1] + [0] * (Q - 1) for _ in range(B)]
+    tokens = np.array([draft_tokens(rng, draft[b], parents[b], T, V) for b in range(B)], np.int32)
+    u = synth.open_uniforms(rng, (B, Q))
+    n, path, nxt = tf.tree_accept(d(target), d(draft), d(tokens), d(np.array(parents, np.int32)), d(u), T)
+    torch.cuda.synchronize()
+    n, path, nxt = n.cpu().numpy(), path.cpu().numpy(), nxt.cpu().numpy()
+    checked = 0
+    for b in range(B):
+        rp, rx, margin = oracle.tree_accept(target[b], draft[b], tokens[b], parents[b], u[b], T)
+        if margin < 1e-12:
+            continue
+        checked += 1
+        assert int(n[b]) == len(rp) and list(path[b, :n[b]]) == rp and int(nxt[b]) == rx, b
+    assert checked >= B - 2
