@@ -224,6 +224,9 @@ class ThreeTierStep:
         tf.collect_candidates(self.drafts_row, self.n1, self.y, self.syn.q_rows, self.cnt[cin], self.cnt[1 - cin],
                               self.cand, self.cand_q, stream=s)
         tf.commit_length(self.seq_len, 0, g1, self.n1, stream=s)   # rejected drafts leave the full cache
+        # the drafter consumed the current token and drafts 1 .. g1 - 1: the
+        # g1 - 1 - min(n1, g1 - 1) of those after the first rejection leave its ring
+        tf.commit_length(self.d_len, 0, g1 - 1, self.n1, stream=s)
 
     def _extend_one(self):
         for L in self.t:
@@ -244,9 +247,14 @@ class ThreeTierStep:
                                 max_chunks=(g2 + 1) // self.cs + 2, stream=s)
 
     def _stage_uniforms(self, dst, counts):
-        """Copy the next uniforms (taken as _u(c) for each c in counts, in order) into dst."""
+        """Copy the next uniforms (taken as _u(c) for each c in counts, in order)
+        into dst: one copy when they are consecutive (no wrap in between)."""
+        start = self.u_pos
         parts = [self._u(c) for c in counts]
-        dst.copy_(torch.cat(parts, 1) if len(parts) > 1 else parts[0])
+        if self.u_pos - start == dst.shape[1]:
+            dst.copy_(self.syn.uniforms[start:self.u_pos].view(1, -1))
+        else:
+            dst.copy_(torch.cat(parts, 1))
 
     # -- one step --------------------------------------------------------------
     def step(self) -> int:
@@ -279,9 +287,8 @@ class ThreeTierStep:
                                      self.u_round.cpu().numpy()[0, g1:]))
                 self.n = n_round + 1 + n1
                 # the drafter consumed the current token and drafts 1 .. g1 - 1
-                drop = (g1 - 1) - min(n1, g1 - 1)
-                self._drop(self.d_len, drop)
-                d_len -= drop
+                # (the device length was cut inside the round)
+                d_len -= (g1 - 1) - min(n1, g1 - 1)
                 self.pending = self.n - d_len
             # the full cache holds the current token and the first total - 1
             # emitted tokens: keep the current token and exactly gamma2 candidates
