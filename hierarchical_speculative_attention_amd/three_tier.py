@@ -11,7 +11,9 @@ sequences the calls and keeps the host-side counts.  It drives one sequence
 (B = 1): how many Force 2 rounds a step needs depends on how many drafts each
 round keeps, so after each round the kept count is read back (8 bytes) and
 the host decides whether another round is needed and how many rows each cache
-gains or loses.
+gains or loses.  With graphs=True the call sequences between those reads (the
+retrieval, a round, Force 3) are HIP graphs captured before the first step
+and replayed.
 
 The models' outputs -- new K/V rows, queries and logits -- are synthetic
 device tensors given by the caller (there are no weights here); the control
