@@ -659,8 +659,9 @@ def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_i
     to_bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     dt = "bf16" if tdt == torch.bfloat16 else "fp16"
     G = Hq // Hkv
-    t_layers = 0.0
-    for x in sample_layers:
+
+    def heads_of(x, pairs):
+        """Oracle time of the step's per-head work for the given (sequence, KV head) pairs of layer x."""
         Kb, Vb = to_bits(x.K), to_bits(x.V)
         qv, qd = to_bits(x.qv), to_bits(x.qd)
         Ksb, Vsb = to_bits(x.Ks), to_bits(x.Vs)
@@ -668,40 +669,62 @@ def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_i
         cap = x.kv.seq_cap.cpu().numpy()
         scap = int(x.sd.seq_cap[0].item())
         sbase = x.sd.seq_base.cpu().numpy()
-        for b, n in enumerate(lens):
-            for g in range(Hkv):
-                off = int(base[b]) + g * int(cap[b]) * d
-                K = oracle.widen(Kb[off:off + n * d].reshape(n, d), dt)
-                V = oracle.widen(Vb[off:off + n * d].reshape(n, d), dt)
-                ck = oracle.chunk_keys(K, n, cs)            # prefill: not timed
-                soff = int(sbase[b]) + g * scap * d
-                Ks = oracle.widen(Ksb[soff:soff + scap * d].reshape(scap, d), dt)
-                Vs = oracle.widen(Vsb[soff:soff + scap * d].reshape(scap, d), dt)
-                t0 = time.perf_counter()
-                c0 = max(0, (n - Q) // cs)
-                ck[c0:] = oracle.chunk_keys(K[c0 * cs:n], n - c0 * cs, cs)   # tail refresh
-                qg = np.stack([oracle.widen(qd[b, g * G + j], dt) for j in range(G)])
-                sel = oracle.select_topk(oracle.chunk_scores(qg, ck), k)
-                for j in range(G):
-                    h = g * G + j
-                    oracle.sparse_attn(qg[j], K, V, n, sel, cs)
-                    # streaming positions in ring order; every slot of the ring is resident here
-                    pos = oracle.stream_positions(n, S, Wn)
-                    slots = [p if p < S else S + (p - S) % (scap - S) for p in pos]
-                    oracle.attention(qg[j], Ks[slots], Vs[slots])
-                    oracle.verify_attn(oracle.widen(qv[b, h], dt), K, V, n)
-                t_layers += time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for b in range(acc_in.target.shape[0]):
-        oracle.accept(acc_in.target[b], acc_in.draft[b], acc_in.tokens[b], acc_in.uniforms[b], 1.0)
-    t_acc = time.perf_counter() - t0
+        t = 0.0
+        for b, g in pairs:
+            n = lens[b]
+            off = int(base[b]) + g * int(cap[b]) * d
+            K = oracle.widen(Kb[off:off + n * d].reshape(n, d), dt)
+            V = oracle.widen(Vb[off:off + n * d].reshape(n, d), dt)
+            ck = oracle.chunk_keys(K, n, cs)            # prefill: not timed
+            soff = int(sbase[b]) + g * scap * d
+            Ks = oracle.widen(Ksb[soff:soff + scap * d].reshape(scap, d), dt)
+            Vs = oracle.widen(Vsb[soff:soff + scap * d].reshape(scap, d), dt)
+            t0 = time.perf_counter()
+            c0 = max(0, (n - Q) // cs)
+            ck[c0:] = oracle.chunk_keys(K[c0 * cs:n], n - c0 * cs, cs)   # tail refresh
+            qg = np.stack([oracle.widen(qd[b, g * G + j], dt) for j in range(G)])
+            sel = oracle.select_topk(oracle.chunk_scores(qg, ck), k)
+            for j in range(G):
+                h = g * G + j
+                oracle.sparse_attn(qg[j], K, V, n, sel, cs)
+                # streaming positions in ring order; every slot of the ring is resident here
+                pos = oracle.stream_positions(n, S, Wn)
+                slots = [p if p < S else S + (p - S) % (scap - S) for p in pos]
+                oracle.attention(qg[j], Ks[slots], Vs[slots])
+                oracle.verify_attn(oracle.widen(qv[b, h], dt), K, V, n)
+            t += time.perf_counter() - t0
+        return t
+
+    def accepts():
+        t0 = time.perf_counter()
+        for b in range(acc_in.target.shape[0]):
+            oracle.accept(acc_in.target[b], acc_in.draft[b], acc_in.tokens[b], acc_in.uniforms[b], 1.0)
+        return time.perf_counter() - t0
+
+    every = [(b, g) for b in range(len(lens)) for g in range(Hkv)]
+    t_layers = sum(heads_of(x, every) for x in sample_layers)
+    t_acc = accepts()
     nl = len(sample_layers)
     t_step = t_layers / nl * layers + t_acc
-    return {"value": round(1.0 / t_step, 6), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
-            "sample": f"fp64 numpy oracle on {nl} of the {layers} layers (all {Hkv} KV heads x {Hq} query heads, "
-                      f"{len(lens)} sequence(s)) + 1 accept, {t_layers + t_acc:.1f} s timed, scaled to "
-                      f"{layers} layers ({t_layers / nl:.2f} s per layer); chunk-key prefill untimed"}
+    out = {"value": round(1.0 / t_step, 6), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+           "sample": f"fp64 numpy oracle on {nl} of the {layers} layers (all {Hkv} KV heads x {Hq} query heads, "
+                     f"{len(lens)} sequence(s)) + 1 accept, {t_layers + t_acc:.1f} s timed, scaled to "
+                     f"{layers} layers ({t_layers / nl:.2f} s per layer); chunk-key prefill untimed"}
+    # the same oracle on one thread, over a few heads of one layer
+    try:
+        from threadpoolctl import threadpool_limits
+        few = every[:4]
+        with threadpool_limits(limits=1):
+            t1 = heads_of(sample_layers[0], few)
+            t1a = accepts()
+        t1_step = t1 / len(few) * len(every) * layers + t1a
+        out["single_thread"] = {"value": round(1.0 / t1_step, 6), "unit": "steps/s", "cores": 1,
+                                "sample": f"{len(few)} (sequence, KV head) pairs of one layer + 1 accept on one "
+                                          f"thread, {t1 + t1a:.1f} s timed, scaled to the step"}
+    except ImportError:
+        pass
+    return out
 
 
 if __name__ == "__main__":
