@@ -52,6 +52,15 @@ def test_verify_query_tiles(Hq, Hkv, Q, n):
     compare_attn(out, lse, *oracle_verify(inp, Q))
 
 
+@pytest.mark.parametrize("n,Q", [(24000, 7), (40003, 3)])
+def test_verify_splits_of_uneven_size(n, Q):
+    # 32 KV heads: 16 splits of a multiple of 32 rows that is no power of two
+    # (1504 and 2528 rows), the last split partial
+    inp = synth.make_attn_inputs(lens=[n], Hq=32, Hkv=32, dtype="bf16", Q=Q, seed=5, cap_extra=7)
+    out, lse = run_verify(inp, Q)
+    compare_attn(out, lse, *oracle_verify(inp, Q))
+
+
 def test_verify_empty_and_max_len_clamp():
     inp = synth.make_attn_inputs(lens=[0, 3, 200], Hq=2, Hkv=2, dtype="bf16", Q=2, seed=3, cap_extra=8)
     out, lse = run_verify(inp, 2)
