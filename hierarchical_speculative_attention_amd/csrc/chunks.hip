@@ -187,22 +187,33 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
       if (c < c_max) out[c] = (c < C) ? v : -__builtin_huge_valf();
     }
   };
+  // Blocks holding keys first (out-of-range loads still occupy the wave --
+  // 0.4-1 us per launch when a wave with one block issued a second batch --
+  // so none is issued for a block wholly past C), then the -inf of the blocks
+  // wholly past C, with no loads.
+  const int nkey = min(nblk, (C + kScoreBlock - 1) / kScoreBlock);
   int blk = blockIdx.x * kScoreWaves + w;
-  u32x4 xa[kScoreLoads], xb[kScoreLoads];
-  fetch(blk, xa);
-  // (a wave with one block issues no second batch: out-of-range loads still
-  // occupy the wave, measured 0.4-1 us slower per launch at one block per wave)
-  if (blk + stride < nblk) fetch(blk + stride, xb);
-  while (true) {
-    if (blk >= nblk) break;
-    score(blk, xa);
-    fetch(blk + 2 * stride, xa);
-    blk += stride;
-    if (blk >= nblk) break;
-    score(blk, xb);
-    fetch(blk + 2 * stride, xb);
-    blk += stride;
+  {
+    u32x4 xa[kScoreLoads], xb[kScoreLoads];
+    fetch(blk, xa);
+    if (blk + stride < nkey) fetch(blk + stride, xb);
+    while (true) {
+      if (blk >= nkey) break;
+      score(blk, xa);
+      fetch(blk + 2 * stride, xa);
+      blk += stride;
+      if (blk >= nkey) break;
+      score(blk, xb);
+      fetch(blk + 2 * stride, xb);
+      blk += stride;
+    }
   }
+  // (blk is now the wave's first block at or past nkey)
+  if (part < kScoreLoads)
+    for (; blk < nblk; blk += stride) {
+      const int c = blk * kScoreBlock + 4 * part + grp;
+      if (c < c_max) out[c] = -__builtin_huge_valf();
+    }
 }
 
 // a2, fp32 chunk keys: grid (ceil(c_max / 64), H, B), 256 threads; each wave
