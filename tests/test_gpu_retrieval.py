@@ -187,13 +187,13 @@ def test_topk_large_rows(C, k):
             assert np.array_equal(idx[b, g], oracle.select_topk(s[b, g, :n].astype(np.float64), k))
 
 
-@pytest.mark.parametrize("C", [5003, 16384, 40000, 50001])
+@pytest.mark.parametrize("C", [1500, 3001, 4096, 5003, 16384, 40000, 50001])
 def test_topk_value_spreads(C):
     """Rows whose k-th key sits in bins of every size: exponents spread so the
     first 8-bit digit already isolates a small bin, quantised values whose
     16-bit bins hold exact duplicates, a narrow band that needs all four
-    digits, and 64 keys per thread (C > 32768) with row lengths that are and
-    are not a multiple of 4."""
+    digits.  Row lengths cover every keys-per-thread instantiation (2 to 64
+    keys per thread) with lengths that are and are not a multiple of 4."""
     rng = np.random.default_rng(C + 1)
     rows = [
         np.sign(rng.standard_normal(C)) * np.exp2(rng.uniform(-60, 60, C)),     # spread exponents
