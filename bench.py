@@ -163,6 +163,7 @@ def main():
         l_v = torch.empty((B, Hq, Q), dtype=torch.float32, device=dev)
         ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Q, n_max), dev)
         ws_s = tf.workspace(tf.sparse_attn_workspace_size(B, Hq, Hkv, k, cs), dev)
+        ws_t = tf.workspace(tf.select_topk_workspace_size(B, Hkv, c_max, k), dev)
         ws_a = tf.workspace(tf.accept_workspace_size(B, gamma, vocab), dev)
         acc_in = synth.make_accept_inputs(B=B, gamma=gamma, vocab=vocab, seed=0)
         tgt = torch.from_numpy(acc_in.target).to(dev)
@@ -191,7 +192,7 @@ def main():
             ("chunk_refresh", lambda: tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk,
                                                           max_chunks=tail_count, stream=stream)),
             ("score", lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream)),
-            ("topk", lambda: tf.select_topk(scores, n_chunks, k, idx=idx, stream=stream)),
+            ("topk", lambda: tf.select_topk(scores, n_chunks, k, idx=idx, ws=ws_t, stream=stream)),
             ("sparse", lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s,
                                               stream=stream)),
             ("stream", lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream)),

@@ -6,7 +6,7 @@ ctypes binding and the seeded input generators.  Importing the package does
 not load the library; the first call does, and raises if it is not built.
 """
 from ._lib import (  # noqa: F401
-    KVDesc, TfError, accept, build_chunk_keys, score_chunks, select_topk, sparse_attn,
+    KVDesc, TfError, accept, build_chunk_keys, score_chunks, select_topk, select_topk_workspace_size, sparse_attn,
     sparse_verify_attn, sparse_verify_attn_workspace_size,
     stream_attn, verify_attn, workspace, verify_attn_workspace_size,
     sparse_attn_workspace_size, accept_workspace_size, tree_accept_workspace_size, lib, append_kv, commit_length,

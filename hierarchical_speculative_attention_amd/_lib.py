@@ -205,15 +205,23 @@ def score_chunks(q: torch.Tensor, Hq: int, ck: torch.Tensor, ckd: KVDesc, c_max:
     return scores
 
 
+def select_topk_workspace_size(B: int, rows: int, c_max: int, k: int) -> int:
+    return int(lib().tf_select_topk_workspace_size(B, rows, c_max, k))
+
+
 def select_topk(scores: torch.Tensor, n_chunks: torch.Tensor, k: int, idx: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
+                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     _need(scores, "scores", torch.float32)
     _need(n_chunks, "n_chunks", torch.int32)
     B, rows, c_max = scores.shape
     if idx is None:
         idx = torch.empty((B, rows, k), dtype=torch.int32, device=scores.device)
     _need(idx, "idx", torch.int32)
-    _check(lib().tf_select_topk(_ptr(scores), B, rows, c_max, _ptr(n_chunks), int(k), _ptr(idx), None, 0,
+    need = select_topk_workspace_size(B, rows, c_max, k)
+    if ws is None and need:
+        ws = workspace(need, scores.device)
+    wp, wn = (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+    _check(lib().tf_select_topk(_ptr(scores), B, rows, c_max, _ptr(n_chunks), int(k), _ptr(idx), wp, wn,
                                 _stream(stream, scores.device)), "tf_select_topk")
     return idx
 

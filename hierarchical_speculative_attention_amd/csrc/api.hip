@@ -212,13 +212,14 @@ TF_EXPORT int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq, const 
 // ---------------------------------------------------------------------------
 // a3
 // ---------------------------------------------------------------------------
-TF_EXPORT size_t tf_select_topk_workspace_size(int32_t, int32_t, int32_t, int32_t) { return 0; }
+TF_EXPORT size_t tf_select_topk_workspace_size(int32_t B, int32_t rows_per_seq, int32_t c_max, int32_t k) {
+  if (B < 1 || rows_per_seq < 1 || c_max < 1 || k < 1 || c_max > (1 << 20) || B > 65535) return 0;
+  return tfk::topk_workspace_bytes(B, rows_per_seq, c_max, k);
+}
 
 TF_EXPORT int tf_select_topk(const float* scores, int32_t B, int32_t rows_per_seq, int32_t c_max,
                              const int32_t* n_chunks, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
                              tf_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (B < 0 || rows_per_seq < 1 || c_max < 1 || k < 1)
     return fail(TF_ERR_INVALID_ARG, "B=%d rows=%d c_max=%d k=%d out of range", B, rows_per_seq, c_max, k);
   if (c_max > (1 << 20)) return fail(TF_ERR_UNSUPPORTED, "c_max %d above 1<<20", c_max);
@@ -227,7 +228,11 @@ TF_EXPORT int tf_select_topk(const float* scores, int32_t B, int32_t rows_per_se
   TRY(check_ptr(scores, "scores", 4));
   TRY(check_ptr(n_chunks, "n_chunks", 4));
   TRY(check_ptr(idx, "idx", 4));
-  return check_hip(tfk::launch_topk(scores, B, rows_per_seq, c_max, n_chunks, k, idx, (hipStream_t)stream),
+  TRY(check_ws(ws, ws_bytes, tfk::topk_workspace_bytes(B, rows_per_seq, c_max, k)));
+  const tfk::TopkSplit p = tfk::plan_topk(B, rows_per_seq, c_max, k);
+  log_line("tf_select_topk: B=%d rows=%d c_max=%d k=%d slices=%d%s", B, rows_per_seq, c_max, k, p.S,
+           p.S > 1 ? " (+ merge)" : "");
+  return check_hip(tfk::launch_topk(scores, B, rows_per_seq, c_max, n_chunks, k, idx, ws, (hipStream_t)stream),
                    "tf_select_topk");
 }
 

@@ -73,8 +73,18 @@ hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs
 hipError_t launch_scores(const uint16_t* q, int32_t q_dtype, int32_t Hq, const void* ck,
                          const tf_kv_desc& ckd, float* scores, int32_t c_max, hipStream_t stream);
 // top-k
-hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_max,
-                       const int32_t* n_chunks, int32_t k, int32_t* idx, hipStream_t stream);
+// Top-k: rows of more than 16384 chunks, at most kTopkSplitMaxRows of them
+// per call, are selected in kTopkSlices slices per row and then merged.
+constexpr int kTopkSlices = 8;
+constexpr int kTopkSplitMaxRows = 16;
+struct TopkSplit {
+  int S;  // slices per row (1: one workgroup per row)
+  int L;  // chunks per slice
+};
+TopkSplit plan_topk(int32_t B, int32_t rows, int32_t c_max, int32_t k);
+size_t topk_workspace_bytes(int32_t B, int32_t rows, int32_t c_max, int32_t k);
+hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_max, const int32_t* n_chunks,
+                       int32_t k, int32_t* idx, void* ws, hipStream_t stream);
 // accept
 size_t accept_ws_bytes(int32_t B, int32_t gamma, int32_t V);
 int32_t accept_max_vocab();

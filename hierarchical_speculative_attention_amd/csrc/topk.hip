@@ -23,6 +23,14 @@
 //  * both output counts share one prefix sum.
 // A direct rank of the keys left in the k-th key's bin (in place of the last
 // passes) measured slower than the passes it replaced and is not used.
+//
+// Few long rows (at most 16 rows of more than 16384 chunks) would leave the
+// chip idle while one workgroup per row loads 32-64 keys per thread (at 32768
+// chunks: 4.8 us loading, 4.6 us in pass 0, ~2.2 us per later pass).  They are
+// selected in two launches instead: the same selection over 8 slices of each
+// row, each writing its k best as (key, chunk index) candidates in chunk
+// order, then over the row's 8 k candidates (8 rows of 32768 chunks, k = 512:
+// 22.0 -> 14.1 us per call; 4 or 16 slices: 15.3 and 15.0 us).
 #include "tf_internal.h"
 
 namespace tfk {
@@ -104,58 +112,111 @@ __device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int krem
   }
 }
 
-template <int IPT>
+// What one workgroup selects from:
+//  kRowScores  the whole row of scores -> idx (one workgroup per row);
+//  kRowSlice   slice blockIdx.z (chunks [z L, (z + 1) L)) of a row of scores ->
+//              the slice's k best as (key, chunk index) candidates, ascending;
+//  kRowMerge   the S k candidates of a row (slices in order, so ascending
+//              chunk index; key 0 = padding) -> idx.
+// An item of the row's k best (key descending, index ascending) has fewer
+// than k items before it in its slice too, so it is among its slice's
+// candidates; the merge's ties go to the lower candidate position, which is
+// the lower chunk index.
+enum : int { kRowScores = 0, kRowSlice = 1, kRowMerge = 2 };
+
+template <int IPT, int SRC>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int32_t rows,
                                                              int32_t c_max, const int32_t* __restrict__ n_chunks,
-                                                             int32_t k, int32_t* __restrict__ idx) {
+                                                             int32_t k, int32_t* __restrict__ idx,
+                                                             uint2* __restrict__ cand, int32_t L) {
   __shared__ int s_hist[2][kHistWords];
   __shared__ unsigned s_warp[2 * kTopkWaves];
   __shared__ unsigned s_prefix;
   __shared__ int s_krem;
   const int row = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
-  const float* src = scores + ((size_t)b * rows + row) * c_max;
-  int32_t* dst = idx + ((size_t)b * rows + row) * k;
+  const size_t row_id = (size_t)b * rows + row;
   const int i0 = tid * IPT;
 
-  // Scores first: every load is in bounds (index clamped into the row) and
+  // Items first: every load is in bounds (index clamped into the row) and
   // none waits for another or for the chunk count.
   // (32-bit byte offsets from the row base: one address register per load)
-  const char* srcb = (const char*)src;
   float v[IPT];
-  if (IPT >= 4 && (c_max & 3) == 0) {
-    const int last4 = c_max / 4 - 1;
+  uint2 cv[SRC == kRowMerge ? IPT : 1];
+  int lo = 0, n_load = c_max;  // slice: chunks [lo, lo + n_load) of the row
+  if (SRC == kRowSlice) {
+    lo = blockIdx.z * L;
+    n_load = min(L, c_max - lo);
+  }
+  if (SRC == kRowMerge) {
+    const int nc = L;  // candidates per row (S k)
+    const char* cb = (const char*)(cand + row_id * nc);
+    if ((IPT & 1) == 0) {
 #pragma unroll
-    for (int q = 0; q < IPT / 4; ++q) {
-      const float4 x = *(const float4*)(srcb + (unsigned)min(i0 / 4 + q, last4) * 16u);
-      v[4 * q + 0] = x.x;
-      v[4 * q + 1] = x.y;
-      v[4 * q + 2] = x.z;
-      v[4 * q + 3] = x.w;
+      for (int q = 0; q < IPT / 2; ++q) {
+        const uint4 x = *(const uint4*)(cb + (unsigned)min(i0 / 2 + q, nc / 2 - 1) * 16u);
+        cv[2 * q] = make_uint2(x.x, x.y);
+        cv[2 * q + 1] = make_uint2(x.z, x.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) cv[j] = *(const uint2*)(cb + (unsigned)min(i0 + j, nc - 1) * 8u);
     }
-  } else if (IPT <= 32) {
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, c_max - 1) * 4u);
   } else {
-    // (64 keys per thread: one address register per load would not fit beside
-    // the values; load in groups of 16)
+    const char* srcb = (const char*)(scores + row_id * c_max + lo);
+    // (16-byte loads need a 16-byte aligned row start; the scores pointer
+    // itself is only required to be 4-byte aligned)
+    if (IPT >= 4 && (c_max & 3) == 0 && (SRC == kRowScores || (L & 3) == 0) && ((uintptr_t)scores & 15) == 0) {
+      const int last4 = n_load / 4 - 1;
 #pragma unroll
-    for (int g = 0; g < IPT; g += 16) {
+      for (int q = 0; q < IPT / 4; ++q) {
+        const float4 x = *(const float4*)(srcb + (unsigned)min(i0 / 4 + q, last4) * 16u);
+        v[4 * q + 0] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else if (IPT <= 32) {
 #pragma unroll
-      for (int j = g; j < g + 16; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, c_max - 1) * 4u);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < IPT; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, n_load - 1) * 4u);
+    } else {
+      // (64 keys per thread: one address register per load would not fit beside
+      // the values; load in groups of 16)
+#pragma unroll
+      for (int g = 0; g < IPT; g += 16) {
+#pragma unroll
+        for (int j = g; j < g + 16; ++j) v[j] = *(const float*)(srcb + (unsigned)min(i0 + j, n_load - 1) * 4u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;
   const int C = min(max(n_chunks[b], 0), c_max);
 
   if (C <= k) {
-    for (int j = tid; j < k; j += kTopkThreads) dst[j] = j < C ? j : -1;
-    return;
+    if (SRC != kRowSlice) {
+      int32_t* dst = idx + row_id * k;
+      for (int j = tid; j < k; j += kTopkThreads) dst[j] = j < C ? j : -1;
+    }
+    return;  // (a slice leaves the row to the merge)
   }
+  // items of this workgroup that exist: the row's C chunks, the slice's part
+  // of them, or the candidates (padding has key 0)
+  const int n_items = SRC == kRowScores ? C : SRC == kRowSlice ? min(max(C - lo, 0), L) : L;
   unsigned key[IPT];
 #pragma unroll
-  for (int j = 0; j < IPT; ++j) key[j] = (i0 + j < C) ? order_key(v[j]) : 0u;
+  for (int j = 0; j < IPT; ++j)
+    key[j] = (i0 + j < n_items) ? (SRC == kRowMerge ? cv[j].x : order_key(v[j])) : 0u;
+
+  if (SRC == kRowSlice && n_items <= k) {
+    // the whole slice is its own selection: candidates in order, then padding
+    uint2* out = cand + (row_id * gridDim.z + blockIdx.z) * k;  // (slice kernel only)
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if (i0 + j < n_items) out[i0 + j] = make_uint2(key[j], (unsigned)(lo + i0 + j));
+    for (int j = n_items + tid; j < k; j += kTopkThreads) out[j] = make_uint2(0u, 0xFFFFFFFFu);
+    return;
+  }
   __syncthreads();
 
   unsigned prefix = 0;
@@ -193,6 +254,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int eq_before = (int)(pre >> 16), gt_before = (int)(pre & 0xFFFFu);
   int eq_left = min(max(krem - eq_before, 0), (int)n_eq);
   int pos = gt_before + min(eq_before, krem);
+  int32_t* dst = SRC == kRowSlice ? nullptr : idx + row_id * k;
+  uint2* out = SRC == kRowSlice ? cand + (row_id * gridDim.z + blockIdx.z) * k : nullptr;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     bool keep = key[j] > T;
@@ -200,7 +263,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       keep = true;
       --eq_left;
     }
-    if (keep && pos < k) dst[pos++] = i0 + j;
+    if (keep && pos < k) {
+      if (SRC == kRowScores) dst[pos] = i0 + j;
+      if (SRC == kRowSlice) out[pos] = make_uint2(key[j], (unsigned)(lo + i0 + j));
+      if (SRC == kRowMerge) dst[pos] = (int32_t)cv[j].y;
+      ++pos;
+    }
   }
 }
 
@@ -292,13 +360,61 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel_long(const float* __
   }
 }
 
-hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_max,
-                       const int32_t* n_chunks, int32_t k, int32_t* idx, hipStream_t stream) {
-  const dim3 grid(rows, B), block(kTopkThreads);
+TopkSplit plan_topk(int32_t B, int32_t rows, int32_t c_max, int32_t k) {
+  TopkSplit p;
+  p.S = 1;
+  p.L = c_max;
+  // Few long rows: one workgroup per row would leave the chip idle and spend
+  // most of its time loading 32+ keys per thread.  Eight slices per row, each
+  // cutting its chunks to k candidates at least by half.
+  if ((long)B * rows <= kTopkSplitMaxRows && c_max > 16384 && c_max <= 65536) {
+    const int S = kTopkSlices;
+    const int L = ((c_max + S - 1) / S + 3) / 4 * 4;
+    if (2L * k <= L && (long)S * k <= 16384) {
+      p.S = S;
+      p.L = L;
+    }
+  }
+  return p;
+}
+
+size_t topk_workspace_bytes(int32_t B, int32_t rows, int32_t c_max, int32_t k) {
+  const TopkSplit p = plan_topk(B, rows, c_max, k);
+  return p.S > 1 ? (size_t)B * rows * p.S * k * sizeof(uint2) : 0;
+}
+
+hipError_t launch_topk(const float* scores, int32_t B, int32_t rows, int32_t c_max, const int32_t* n_chunks,
+                       int32_t k, int32_t* idx, void* ws, hipStream_t stream) {
   const int ipt = (c_max + kTopkThreads - 1) / kTopkThreads;
+  const dim3 block(kTopkThreads);
+  const TopkSplit p = plan_topk(B, rows, c_max, k);
+  if (p.S > 1) {
+    uint2* cand = (uint2*)ws;
+    const int ipt1 = (p.L + kTopkThreads - 1) / kTopkThreads;
+    const int nc = p.S * k;
+    const int ipt2 = (nc + kTopkThreads - 1) / kTopkThreads;
+#define TF_TOPK_SLICE(N)                                                                                  \
+  if (ipt1 <= N) {                                                                                        \
+    hipLaunchKernelGGL((topk_kernel<N, kRowSlice>), dim3(rows, B, p.S), block, 0, stream, scores, rows, c_max, \
+                       n_chunks, k, idx, cand, p.L);                                                      \
+  } else
+    TF_TOPK_SLICE(1) TF_TOPK_SLICE(2) TF_TOPK_SLICE(4) TF_TOPK_SLICE(8) TF_TOPK_SLICE(16) return hipErrorInvalidValue;
+#undef TF_TOPK_SLICE
+#define TF_TOPK_MERGE(N)                                                                                  \
+  if (ipt2 <= N) {                                                                                        \
+    hipLaunchKernelGGL((topk_kernel<N, kRowMerge>), dim3(rows, B), block, 0, stream, scores, rows, c_max,   \
+                       n_chunks, k, idx, cand, nc);                                                       \
+    return hipGetLastError();                                                                             \
+  }
+    TF_TOPK_MERGE(1) TF_TOPK_MERGE(2) TF_TOPK_MERGE(4) TF_TOPK_MERGE(8) TF_TOPK_MERGE(16)
+#undef TF_TOPK_MERGE
+    return hipErrorInvalidValue;
+  }
+  const dim3 grid(rows, B);
 #define TF_TOPK_CASE(N) \
   if (ipt <= N) {       \
-    hipLaunchKernelGGL(topk_kernel<N>, grid, block, 0, stream, scores, rows, c_max, n_chunks, k, idx); \
+    hipLaunchKernelGGL((topk_kernel<N, kRowScores>), grid, block, 0, stream, scores, rows, c_max, n_chunks, k, idx, \
+                       (uint2*)nullptr, c_max); \
     return hipGetLastError(); \
   }
   TF_TOPK_CASE(1)

@@ -135,6 +135,7 @@ class ThreeTierStep:
                                 dev)
         self.ws3 = tf.workspace(tf.verify_attn_workspace_size(1, Hq, kv0.H, gamma2 + 1, kv0.max_len), dev)
         self.wsa = tf.workspace(tf.accept_workspace_size(1, max(gamma1, gamma2), V), dev)
+        self.wst = tf.workspace(tf.select_topk_workspace_size(1, kv0.H, self.c_max, k), dev)
         # uniforms of a round (gamma1 drafter draws, then gamma1 + 1 for level 1) and of
         # Force 3 (gamma2 + 1), staged in fixed buffers so that graphs can replay them
         self.u_round = torch.empty((1, 2 * gamma1 + 1), dtype=torch.float64, device=dev)
@@ -202,7 +203,7 @@ class ThreeTierStep:
     def _retrieval(self):
         for L, idx in zip(self.t, self.idx):
             tf.score_chunks(self.syn.draft_q, self.Hq, L.ck, L.ckd, self.c_max, scores=self.scores, stream=self.s)
-            tf.select_topk(self.scores, self.ck_len, self.k, idx=idx, stream=self.s)
+            tf.select_topk(self.scores, self.ck_len, self.k, idx=idx, ws=self.wst, stream=self.s)
 
     def _round(self, pend, cin):
         """Force 1 drafts gamma1 tokens (after consuming 1 + pend tokens), Force 2

@@ -127,7 +127,15 @@ int tf_score_chunks(const void* q, int32_t q_dtype, int32_t Hq,
  *   scores  : device fp32 [B][rows_per_seq][c_max].
  *   n_chunks: device int32 [B] (clamped into [0, c_max]).
  *   idx     : device int32 [B][rows_per_seq][k].
- *   Needs no workspace (ws may be NULL).  c_max <= 1 << 20.
+ *   ws      : tf_select_topk_workspace_size(B, rows_per_seq, c_max, k) bytes
+ *             (256-byte aligned; no initialisation).  It is nonzero only for
+ *             at most 16 rows (B * rows_per_seq) of 16385 to 65536 chunks
+ *             with k <= 2048 and 2 k <= the slice length (c_max / 8 rounded
+ *             up to a multiple of 4): these are selected in 8 slices per row
+ *             (each slice's k best as 8-byte candidates) and then merged.
+ *             Otherwise ws may be NULL.  Too small a workspace returns
+ *             TF_ERR_WORKSPACE.
+ *   c_max <= 1 << 20.
  */
 int tf_select_topk(const float* scores, int32_t B, int32_t rows_per_seq, int32_t c_max,
                    const int32_t* n_chunks, int32_t k, int32_t* idx,

@@ -97,6 +97,17 @@ def test_other_entry_points_validate():
     assert L.tf_select_topk(FAKE, 1, 4, 100, FAKE, 0, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
     assert L.tf_select_topk(FAKE, 1, 4, (1 << 20) + 1, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_UNSUPPORTED
     assert L.tf_select_topk(None, 1, 4, 100, FAKE, 5, FAKE, None, 0, None) == T.TF_ERR_INVALID_ARG
+    # few rows of more than 16384 chunks are selected in 8 slices per row and
+    # merged: 8 (key, index) candidates of 8 bytes per slice, row and k
+    assert L.tf_select_topk_workspace_size(1, 8, 32768, 512) == 8 * 8 * 512 * 8
+    assert L.tf_select_topk_workspace_size(2, 8, 40000, 1023) == 2 * 8 * 8 * 1023 * 8
+    assert L.tf_select_topk_workspace_size(1, 32, 16384, 512) == 0     # one workgroup per row
+    assert L.tf_select_topk_workspace_size(1, 8, 16384, 512) == 0
+    assert L.tf_select_topk_workspace_size(1, 17, 32768, 512) == 0     # enough rows to fill the chip
+    assert L.tf_select_topk_workspace_size(1, 8, 32768, 4096) == 0     # slices would not halve the items
+    assert L.tf_select_topk_workspace_size(1, 8, 70000, 512) == 0      # rows re-read from memory
+    assert L.tf_select_topk(FAKE, 1, 8, 32768, FAKE, 512, FAKE, None, 0, None) == T.TF_ERR_WORKSPACE
+    assert L.tf_select_topk(FAKE, 1, 8, 32768, FAKE, 512, FAKE, FAKE, 1000, None) == T.TF_ERR_WORKSPACE
     assert L.tf_sparse_attn(FAKE, 4, FAKE, FAKE, ctypes.byref(kv), FAKE, 0, 8, FAKE, None, None, 0, None) == T.TF_ERR_INVALID_ARG
     need = L.tf_sparse_attn_workspace_size(1, 4, 4, 512, 8)
     assert need > 0

@@ -208,3 +208,30 @@ def test_topk_value_spreads(C):
             for g in range(s.shape[1]):
                 ref = oracle.select_topk(s[0, g, :n].astype(np.float64), k)
                 assert np.array_equal(idx[0, g], ref), (k, n, g)
+
+
+@pytest.mark.parametrize("B,rows,C,ks", [(1, 8, 32768, [1, 512, 2048]), (2, 3, 40001, [7, 1000]),
+                                         (1, 16, 65536, [1024]), (1, 1, 20000, [64, 1250])])
+def test_topk_split_rows(B, rows, C, ks):
+    """Few long rows take the slice-and-merge path (a workspace is needed):
+    rows whose length leaves slices full, partial (fewer keys than k, all of
+    them candidates) or empty, rows with every key tied, NaN rows, row
+    lengths that are not a multiple of 4, and the largest slice and merge
+    sizes (65536 chunks, 8 x 1024 candidates)."""
+    assert all(tf.select_topk_workspace_size(B, rows, C, k) > 0 for k in ks)
+    rng = np.random.default_rng(C + rows)
+    s = (rng.standard_normal((B, rows, C)) * 3).astype(np.float32)
+    s[:, :, rng.choice(C, 200)] = 6.25                   # ties near the top
+    s[0, 0, :] = 0.0                                     # every key tied
+    if rows > 1:
+        s[0, 1, rng.choice(C, C // 3, replace=False)] = np.nan
+    if rows > 2:
+        s[0, 2, :] = np.round(s[0, 2, :])                # heavy ties in every slice
+    for n in [C, C - 3, C // 2 + 1, 4100, 700, ks[-1] + 1, ks[-1], 100, 0]:
+        n_b = [n] + [max(0, C - 5 - n)] * (B - 1)
+        for k in ks:
+            idx = run_topk(s, n_b, k)
+            for b in range(B):
+                for g in range(rows):
+                    ref = oracle.select_topk(s[b, g, :n_b[b]].astype(np.float64), k)
+                    assert np.array_equal(idx[b, g], ref), (n_b[b], k, b, g)
