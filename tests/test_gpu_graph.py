@@ -76,3 +76,42 @@ def test_step_graph_replays_match_eager():
         s.synchronize()
         for n, t in outs.items():
             assert torch.equal(t, ref[n]), (rep, n)
+
+
+def test_sliced_topk_graph_replays():
+    """Few long rows (8 rows of 32768 chunks) take the slice-and-merge top-k;
+    a graph of it replays to the eager result and to the oracle for new
+    scores written into the captured buffer between replays, with eager
+    calls on other scores overwriting the shared workspace in between."""
+    import oracle
+    B, rows, C, k = 1, 8, 32768, 512
+    ws = tf.workspace(tf.select_topk_workspace_size(B, rows, C, k), "cuda")
+    assert ws is not None
+    n = torch.tensor([C - 7], dtype=torch.int32, device="cuda")
+    scores = torch.empty((B, rows, C), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, rows, k), dtype=torch.int32, device="cuda")
+    other = torch.randn((B, rows, C), device="cuda")
+    other_idx = torch.empty_like(idx)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        scores.normal_()
+        tf.select_topk(scores, n, k, idx=idx, ws=ws, stream=s)  # warm-up before capture
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        tf.select_topk(scores, n, k, idx=idx, ws=ws, stream=s)
+    rng = np.random.default_rng(31)
+    for rep in range(3):
+        host = (rng.standard_normal((B, rows, C)) * 2).astype(np.float32)
+        host[:, :, rng.choice(C, 300)] = 4.5           # ties near the threshold
+        with torch.cuda.stream(s):
+            scores.copy_(torch.from_numpy(host).to("cuda"))
+            tf.select_topk(other, n, k, idx=other_idx, ws=ws, stream=s)
+            idx.fill_(-2)
+        g.replay()
+        s.synchronize()
+        got = idx.cpu().numpy()
+        eager = tf.select_topk(scores, n, k).cpu().numpy()
+        assert np.array_equal(got, eager), rep
+        for r in range(rows):
+            assert np.array_equal(got[0, r], oracle.select_topk(host[0, r, :C - 7].astype(np.float64), k)), (rep, r)
