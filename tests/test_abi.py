@@ -223,3 +223,18 @@ def test_tf_log_prints_rejected_calls(value, logged):
         assert lines == ["[tf] TF_ERR_UNSUPPORTED: kv: head dim 64 (only 128)"], r.stderr
     else:
         assert lines == [], r.stderr
+
+
+def test_topk_workspace_follows_documented_rule():
+    """tf_select_topk needs a workspace exactly when the header says so: at
+    most 16 rows of 16385..65536 chunks, k <= 2048 and 2k <= the slice length
+    (c_max / 8 rounded up to a multiple of 4); then 8 candidates of 8 bytes per
+    row and k."""
+    L = T.lib()
+    for B, rows in [(1, 1), (1, 8), (2, 8), (1, 16), (4, 4), (1, 17), (3, 6), (1, 32)]:
+        for c_max in [16384, 16385, 20001, 32768, 40001, 65536, 65537, 100000]:
+            for k in [1, 512, 1250, 2048, 2049, 4096, 5000]:
+                sl = ((c_max + 7) // 8 + 3) // 4 * 4
+                split = B * rows <= 16 and 16384 < c_max <= 65536 and 2 * k <= sl and k <= 2048
+                want = B * rows * 8 * k * 8 if split else 0
+                assert L.tf_select_topk_workspace_size(B, rows, c_max, k) == want, (B, rows, c_max, k)
