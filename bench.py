@@ -322,6 +322,8 @@ def main():
                       "GB_s": round(gbs, 1), "bytes": int(by[n]), "bound": bound[n]}
         if bound[n] == "hbm":
             kernels[n]["frac"] = round(gbs / HBM_PEAK_GBPS, 4)
+    # few long rows are selected in slices, then merged (two launches)
+    kernels["topk"]["launches"] = 2 if ws_t is not None else 1
     step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
     verify_bytes = by["verify"]
     achieved = verify_bytes / verify_avg_s / 1e9
