@@ -88,6 +88,26 @@ def drafter_reserve(gamma1: int, gamma2: int) -> int:
     return gamma1 + gamma2 + 3
 
 
+def check_ring(slots_after_sinks: int, window: int, gamma1: int, gamma2: int, layer: int = 0) -> None:
+    """Raise unless a drafter ring can take a step's appends: an append to a
+    ring with fewer than window + reserve slots after the sinks writes nothing
+    (it only sets its status), so the drafter would attend stale rows."""
+    need = window + drafter_reserve(gamma1, gamma2)
+    if slots_after_sinks < need:
+        raise ValueError(f"drafter layer {layer}: ring has {slots_after_sinks} slots after the sinks, needs "
+                         f"window + reserve = {need} (gamma1 = {gamma1}, gamma2 = {gamma2})")
+
+
+def check_room(n: int, gamma1: int, gamma2: int, cap: int) -> None:
+    """Raise unless the full cache has room for every row a step starting
+    from n committed rows may write.  A round starts at a length below
+    n + gamma2 and appends gamma1 + 1 rows, so the deepest row is
+    n + gamma1 + gamma2 - 1; an append without room writes nothing."""
+    if n + gamma1 + gamma2 > cap:
+        raise ValueError(f"full cache: a step from {n} committed rows may write up to row "
+                         f"{n + gamma1 + gamma2 - 1}, but only {cap} rows are allocated")
+
+
 class ThreeTierStep:
     def __init__(self, target: List[TargetLayer], drafter: List[DrafterLayer], syn: Synthetic, *, Hq: int,
                  chunk_size: int, k: int, tail: int, gamma1: int, gamma2: int, n_sink: int, window: int,
@@ -128,7 +148,9 @@ class ThreeTierStep:
         self.cand = torch.empty((1, gamma2), **i32)
         self.cand_q = torch.empty((1, gamma2, V), dtype=torch.float32, device=dev)
         self.zero = torch.zeros(1, **i32)
-        self.status = torch.empty(1, **i32)             # append status, never read (lengths are host-checked)
+        # append status: never read; step() checks on the host, before it
+        # enqueues anything, that every append of the step has room
+        self.status = torch.empty(1, **i32)
         self.chunk_begin = torch.empty(1, **i32)
         self.host = torch.empty(4, dtype=torch.int32).pin_memory()
         self.ws2 = tf.workspace(tf.sparse_verify_attn_workspace_size(1, Hq, kv0.H, gamma1 + 1, k, chunk_size, tail),
@@ -141,6 +163,11 @@ class ThreeTierStep:
         self.u_round = torch.empty((1, 2 * gamma1 + 1), dtype=torch.float64, device=dev)
         self.u_f3 = torch.empty((1, gamma2 + 1), dtype=torch.float64, device=dev)
         self.u_pos = 0
+        # capacities, read once: an append without room only sets its status and
+        # writes nothing, so a step that would overrun must be refused up front
+        self.cap = min(int(L.kv.seq_cap[0].item()) for L in target)
+        for i, L in enumerate(drafter):
+            check_ring(int(L.sd.seq_cap[0].item()) - n_sink, window, gamma1, gamma2, i)
         self.n = int(kv0.seq_len[0].item())            # committed rows before the current token
         self.pending = self.n - int(drafter[0].sd.seq_len[0].item())  # committed tokens the drafter has not consumed
         assert 0 <= self.pending <= 2
@@ -264,6 +291,7 @@ class ThreeTierStep:
         """One three-tier step; returns the number of tokens it emits."""
         g1, g2 = self.g1, self.g2
         n_start = self.n
+        check_room(n_start, g1, g2, self.cap)
         d_start = self.n - self.pending       # drafter's consumed length
         with torch.cuda.stream(self.s) if self.s is not None else _nullcontext():
             # retrieval for this step, from the committed rows

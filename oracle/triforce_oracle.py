@@ -357,6 +357,9 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
     alpha = min(1, p(x) / q(x)) >= u, u ~ U(0, 1); at the first rejection the
     next token is drawn from max(0, p - q) / sum_v max(0, p(v) - q(v)).
     Readings: p(x) = 0 always rejects (and q(x) = 0 < p(x) accepts, alpha = 1);
+    a drafted token outside the vocabulary [0, V) has no probability under p
+    and is rejected the same way (the residual draw then proceeds as for any
+    rejection at that position);
     if every draft is kept a bonus token is drawn from the target row gamma;
     the draw is by inverse CDF with the extra uniform u[gamma]; a residual
     that sums to 0 (only through rounding) falls back to p.
@@ -372,6 +375,9 @@ def accept(target: np.ndarray, draft: np.ndarray, tokens: Sequence[int], uniform
         p = distribution(target[i], temperature, probs)
         q = distribution(draft[i], temperature, probs)
         x = int(tokens[i])
+        if not 0 <= x < p.shape[0]:
+            j = i
+            break
         px, qx = float(p[x]), float(q[x])
         if px > 0.0:
             alpha = 1.0 if qx == 0.0 else min(1.0, px / qx)

@@ -66,14 +66,34 @@ def test_random_logits_bit_exact(T, correlated):
         assert n.max() >= 2
 
 
-def test_gamma_zero_and_out_of_vocab_tokens():
-    a = synth.make_accept_inputs(B=8, gamma=3, vocab=1000, seed=22)
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_gamma_zero_and_out_of_vocab_tokens(T):
+    """Drafted tokens outside [0, V) (-1, V, V + 2, 5000, INT32_MIN) at the
+    first, a middle and the last position, after correlated drafts that
+    are mostly kept: (n_accepted, next_token) bit-exact against the
+    oracle, which rejects such a token like one with p(x) = 0."""
+    B, gamma, V = 24, 3, 1000
+    a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=True, seed=22)
+    rng = np.random.default_rng(22)
     toks = a.tokens.copy()
-    toks[:, 0] = -1
-    toks[1, 0] = 5000
-    n, nxt = run(a.target, a.draft, toks, a.uniforms, 1.0)
-    assert np.all(n == 0)                      # a token outside [0, V) is never kept
-    assert np.all((nxt >= 0) & (nxt < 1000))
+    for b in range(B):
+        for i in range(gamma):
+            q = oracle.distribution(a.draft[b, i], T if T > 0 else 1.0)
+            toks[b, i] = rng.choice(V, p=q / q.sum()) if T > 0 else int(np.argmax(a.draft[b, i]))
+    bad = [-1, V, V + 2, 5000, np.iinfo(np.int32).min]
+    for b in range(B):
+        toks[b, b % gamma] = bad[b % len(bad)]
+    n, nxt = run(a.target, a.draft, toks, a.uniforms, T)
+    checked = 0
+    for b in range(B):
+        rn, rnext, margin = oracle.accept(a.target[b], a.draft[b], toks[b], a.uniforms[b], T)
+        assert rn <= b % gamma                 # the out-of-vocabulary token is never kept
+        if margin < 1e-12:
+            continue
+        checked += 1
+        assert (n[b], nxt[b]) == (rn, rnext), b
+    assert checked >= B - 1
+    assert n.max() >= 1                        # some drafts ahead of the bad one were kept
     # gamma = 0: a plain sample from the target row
     t = torch.from_numpy(a.target[:, :1].copy()).cuda()
     u = torch.from_numpy(a.uniforms[:, :1].copy()).cuda()

@@ -132,13 +132,16 @@ def test_tree_accept_edge_shapes(V, T):
         n, path, nxt = tf.tree_accept(d(target), d(draft), d(tokens), d(np.array(parents, np.int32)), d(u), T)
         torch.cuda.synchronize()
         n, path, nxt = n.cpu().numpy(), path.cpu().numpy(), nxt.cpu().numpy()
+        checked = 0
         for b in range(B):
             rp, rx, margin = oracle.tree_accept(target[b], draft[b], tokens[b], parents[b], u[b], T)
             if margin < 1e-12:
                 continue
+            checked += 1
             assert int(n[b]) == len(rp) and int(nxt[b]) == rx, (Q, b)
             if Q > 1:
                 assert list(path[b, :n[b]]) == rp and np.all(path[b, n[b]:] == -1), (Q, b)
+        assert checked >= B - 2, (Q, checked)
 
 
 @pytest.mark.parametrize("Q", [2, 3, 4, 9])

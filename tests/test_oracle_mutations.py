@@ -89,6 +89,47 @@ def accept_no_bonus(target, draft, tokens, uniforms, temperature, probs=False):
 ORIG_ACCEPT = T.accept
 
 
+def accept_token_index_wraps(target, draft, tokens, uniforms, temperature, probs=False):
+    gamma = len(tokens)
+    j = gamma
+    for i in range(gamma):
+        p = T.distribution(target[i], temperature, probs)
+        q = T.distribution(draft[i], temperature, probs)
+        x = int(tokens[i])
+        px, qx = float(p[x]), float(q[x])      # mistake: no range check, -1 reads the last entry
+        if px > 0.0 and (qx == 0.0 or min(1.0, px / qx) >= float(uniforms[i])):
+            continue
+        j = i
+        break
+    r = (np.maximum(0.0, T.distribution(target[j], temperature, probs) - T.distribution(draft[j], temperature, probs))
+         if j < gamma else T.distribution(target[gamma], temperature, probs))
+    return j, T.inverse_cdf(r, float(uniforms[gamma])), 1.0
+
+
+def accept_token_clamped(target, draft, tokens, uniforms, temperature, probs=False):
+    V = np.asarray(target).shape[1]
+    toks = [min(max(int(x), 0), V - 1) for x in tokens]  # mistake: out-of-vocabulary tokens clamped
+    return ORIG_ACCEPT(target, draft, toks, uniforms, temperature, probs)
+
+
+def round_fp16_via_fp32(x, dtype):
+    if dtype == "fp16":
+        return np.asarray(x, np.float64).astype(np.float32).astype(np.float16).view(np.uint16)  # mistake: rounds twice
+    return ORIG_ROUND(x, dtype)
+
+
+def round_fp16_truncates(x, dtype):
+    if dtype == "fp16":
+        x = np.asarray(x, np.float64)
+        m, e = np.frexp(x)
+        r = np.ldexp(np.trunc(np.ldexp(m, 11)), e - 11)   # mistake: truncation, not nearest even
+        return r.astype(np.float16).view(np.uint16)
+    return ORIG_ROUND(x, dtype)
+
+
+ORIG_ROUND = T.round_f64_to_bits
+
+
 def append_ring_short_reserve(slots, n, n_sink, window, new, reserve=None):
     reserve = new.shape[0] if reserve is None else reserve
     return ORIG_APPEND_RING(slots, n, n_sink, window, new, reserve - 1)   # mistake: one slot of slack short
@@ -201,6 +242,10 @@ CASES = [
     ("stream_positions", stream_positions_short, lambda: pins.test_stream_ring_equals_mask_and_library(1000, 4, 252)),
     ("accept", accept_flipped_residual, pins.test_accept_hand_examples),
     ("accept", accept_no_bonus, pins.test_accept_hand_examples),
+    ("accept", accept_token_index_wraps, pins.test_accept_hand_examples),
+    ("accept", accept_token_clamped, pins.test_accept_hand_examples),
+    ("round_f64_to_bits", round_fp16_via_fp32, pins.test_round_to_fp16_ties_subnormals_and_library),
+    ("round_f64_to_bits", round_fp16_truncates, pins.test_round_to_fp16_ties_subnormals_and_library),
     ("append_ring", append_ring_short_reserve, pins.test_ring_without_slack_refuses_and_would_corrupt),
     ("commit_length", commit_drops_one_more, pins.test_commit_length_closed_forms),
     ("commit_length", commit_drops_one_more, pins.test_full_cache_decode_loop_matches_list_model),

@@ -57,6 +57,30 @@ def test_round_to_bf16_ties_and_library():
     assert np.array_equal(ref, got)
 
 
+def test_round_to_fp16_ties_subnormals_and_library():
+    one = 1.0
+    cases = {one: 0x3C00,
+             one + 2.0 ** -11: 0x3C00,            # tie -> even (mantissa 0)
+             one + 3 * 2.0 ** -11: 0x3C02,        # tie -> even (mantissa 2)
+             one + 2.0 ** -11 + 2.0 ** -30: 0x3C01,  # just above the tie: one rounding, not two via fp32
+             -2.5: 0xC100,
+             2.0 ** -24: 0x0001,                  # smallest subnormal
+             3 * 2.0 ** -25: 0x0002,              # subnormal tie -> even
+             2.0 ** -26: 0x0000,                  # below half the smallest subnormal
+             65504.0: 0x7BFF,                     # largest finite
+             65520.0: 0x7C00}                     # tie between 65504 and 2^16 -> even -> overflow to inf
+    with np.errstate(over="ignore"):        # 65520 overflows to inf by design
+        for x, bits in cases.items():
+            assert int(oracle.round_f64_to_bits(np.array([x]), "fp16")[0]) == bits, x
+    # float32-representable inputs across the normal and subnormal fp16 range:
+    # torch's fp32 -> fp16 cast rounds to nearest even
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-26, 15, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_f64_to_bits(x.astype(np.float64), "fp16")
+    assert np.array_equal(ref, got)
+
+
 # ---------------------------------------------------------------------------
 # a1 chunk keys: closed forms
 # ---------------------------------------------------------------------------
