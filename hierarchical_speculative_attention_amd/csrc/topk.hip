@@ -5,24 +5,33 @@
 // order-preserving unsigned key (NaN -> key of -inf, -0.0 -> +0.0).  Thread t
 // owns the contiguous index range [t * IPT, (t + 1) * IPT) and keeps its keys
 // in registers for the whole kernel.  A most-significant-digit-first radix
-// select (four 8-bit passes over LDS histograms) finds the exact k-th largest
-// key T and how many keys equal to T must be taken.  One block-wide prefix sum
-// in thread order then gives each kept item's output slot (all keys > T, then
-// the lowest-index keys == T), so the output is ascending and bit-exact for a
+// select over LDS histograms finds the exact k-th largest key T and how many
+// keys equal to T must be taken: the first digit is 11 bits wide, the later
+// ones 8, 8 and 5; as soon as the bin holding the k-th largest key has at most
+// 64 keys, those keys are copied to LDS and one wave ranks them directly
+// instead of running the remaining passes.  One block-wide prefix sum in
+// thread order then gives each kept item's output slot (all keys > T, then the
+// lowest-index keys == T), so the output is ascending and bit-exact for a
 // given score array.
 //
-// Costs that shaped it (measured on the chip, 16384 chunks per row):
+// Costs that shaped it (measured on the chip, 32 rows of 16384 chunks,
+// k = 512; kernel time 12.1 -> 10.8 us with the last four changes):
 //  * the score loads are issued unconditionally (index clamped into the row)
-//    and all at once, before the chunk count arrives: one memory round trip
-//    instead of one per key;
+//    and all at once, with the chunk count, before anything waits for them;
+//    the first histogram is cleared meanwhile and the only barrier before the
+//    first pass follows, so each thread counts as soon as its keys arrive;
 //  * real score rows crowd a few top-byte bins and same-address LDS atomics
 //    within one instruction serialise, so each histogram is kept in kSub
-//    copies indexed by lane % kSub, 257 words apart (8 copies beat 4, 16, 32);
+//    copies indexed by lane % kSub, one bin of different copies in different
+//    banks (8 copies beat 4, 16, 32), and the first digit has 2048 bins, its
+//    bin picked by all sixteen waves;
+//  * after 19 bits the k-th key's bin holds a few keys: copying them to LDS
+//    and ranking them in one wave (broadcast LDS reads, no lane shuffles)
+//    replaces the last two passes; ranking a bin of up to 256 keys with the
+//    whole block instead of the second pass measured slower;
 //  * histograms are double-buffered (the next pass's copy is cleared while
-//    this one fills), so a pass needs two barriers;
-//  * both output counts share one prefix sum.
-// A direct rank of the keys left in the k-th key's bin (in place of the last
-// passes) measured slower than the passes it replaced and is not used.
+//    this one fills), so a pass needs two barriers; the output prefix sum
+//    needs one; both output counts share it.
 //
 // Few long rows (at most 16 rows of more than 16384 chunks) would leave the
 // chip idle while one workgroup per row loads 32-64 keys per thread (at 32768
@@ -40,6 +49,19 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kSub = 8;            // histogram copies, one per lane % kSub
 constexpr int kHistStride = 257;   // words between copies (different LDS banks for one bin)
 constexpr int kHistWords = kSub * kHistStride;
+// The first digit is 11 bits wide (sign, exponent, two mantissa bits): real
+// score rows crowd a handful of 8-bit top digits, and same-address LDS
+// atomics serialise; 2048 bins spread them.  Later digits: 8, 8 and 5 bits.
+constexpr int kWide = 11;
+constexpr int kWideBins = 1 << kWide;
+constexpr int kWideStride = kWideBins + 1;  // one bin of different copies in different banks
+constexpr int kWideWords = kSub * kWideStride;
+static_assert(kWideWords % 4 == 0, "the wide histogram is cleared in 16-byte stores");
+// lowest bit of the digit of pass p (0 .. 3)
+__device__ __forceinline__ constexpr int digit_shift(int p) { return p == 0 ? 32 - kWide : p == 3 ? 0 : 32 - kWide - 8 * p; }
+#ifndef TF_TOPK_SMALL
+#define TF_TOPK_SMALL kSmall
+#endif
 
 // Keys of real scores are >= 0x007FFFFF (the key of -inf), so 0 marks
 // "no item".
@@ -51,6 +73,9 @@ __device__ __forceinline__ unsigned order_key(float f) {
 }
 
 // Exclusive prefix sum over the 1024 threads in thread order (modulo 2^32).
+// One barrier: each wave publishes its total, then every wave reads all
+// sixteen totals (broadcast reads) and adds those of the waves before it.
+// s_warp is written once per call, so a second call needs its own array.
 __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* s_warp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   unsigned incl = x;
@@ -61,25 +86,21 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* s_warp
   }
   if (lane == 63) s_warp[w] = incl;
   __syncthreads();
-  if (w == 0) {
-    const unsigned t = lane < kTopkWaves ? s_warp[lane] : 0u;
-    unsigned ti = t;
+  unsigned before = 0u;
 #pragma unroll
-    for (int off = 1; off < kTopkWaves; off <<= 1) {
-      const unsigned y = __shfl_up(ti, off);
-      if (lane >= off) ti += y;
-    }
-    if (lane < kTopkWaves) s_warp[kTopkWaves + lane] = ti - t;  // exclusive wave offsets
+  for (int q = 0; q < kTopkWaves / 4; ++q) {
+    const uint4 t = ((const uint4*)s_warp)[q];
+    before += (4 * q + 0 < w ? t.x : 0u) + (4 * q + 1 < w ? t.y : 0u) + (4 * q + 2 < w ? t.z : 0u) +
+              (4 * q + 3 < w ? t.w : 0u);
   }
-  __syncthreads();
-  const unsigned r = s_warp[kTopkWaves + w] + incl - x;
-  __syncthreads();
-  return r;
+  return before + incl - x;
 }
 
 // Chooses, in descending digit order, the bin of histogram h (kSub copies)
-// that holds the krem-th largest key; run by the 64 threads of wave 0.
-__device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int krem, unsigned* s_prefix, int* s_krem) {
+// that holds the krem-th largest key, and the number of keys in it; run by
+// the 64 threads of wave 0.
+__device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int width, int krem, unsigned* s_prefix,
+                                         int* s_krem, int* s_cnt) {
   const int lane = threadIdx.x;
   // lane l owns bins 255-4l .. 252-4l
   int c[4];
@@ -104,11 +125,76 @@ __device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int krem
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (above < krem && krem <= above + c[j]) {
-        *s_prefix = (prefix << 8) | (unsigned)(255 - 4 * lane - j);
+        *s_prefix = (prefix << width) | (unsigned)(255 - 4 * lane - j);
         *s_krem = krem - above;
+        *s_cnt = c[j];
       }
       above += c[j];
     }
+  }
+}
+
+// The same choice over the 2048 bins of the first digit, by all sixteen
+// waves: wave w sums bins 2047 - 128 w down to 1920 - 128 w (two per lane,
+// kSub copies each) and scans them, the wave totals meet in LDS, and the one
+// lane whose bins hold the krem-th largest key writes the result.  Every
+// thread of the block calls it; it ends with a barrier.
+__device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_tot, unsigned* s_prefix, int* s_krem,
+                                          int* s_cnt) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b0 = kWideBins - 1 - 128 * w - 2 * lane;  // this lane's bins: b0, then b0 - 1
+  int c0 = 0, c1 = 0;
+#pragma unroll
+  for (int x = 0; x < kSub; ++x) {
+    c0 += h[x * kWideStride + b0];
+    c1 += h[x * kWideStride + b0 - 1];
+  }
+  const int sum = c0 + c1;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_tot[w] = (unsigned)incl;
+  __syncthreads();
+  int above = incl - sum;  // keys in higher bins of this wave, then of the waves before it
+#pragma unroll
+  for (int q = 0; q < kTopkWaves / 4; ++q) {
+    const uint4 t = ((const uint4*)s_tot)[q];
+    above += (int)((4 * q + 0 < w ? t.x : 0u) + (4 * q + 1 < w ? t.y : 0u) + (4 * q + 2 < w ? t.z : 0u) +
+                   (4 * q + 3 < w ? t.w : 0u));
+  }
+  if (above < krem && krem <= above + sum) {
+    const bool first = krem <= above + c0;
+    *s_prefix = (unsigned)(first ? b0 : b0 - 1);
+    *s_krem = first ? krem - above : krem - above - c0;
+    *s_cnt = first ? c0 : c1;
+  }
+  __syncthreads();
+}
+
+// The krem-th largest of the n <= kSmall keys in s_key[0, n) (s_key[n,
+// kSmall) hold 0, which no key equals or falls below), and how many keys equal
+// to it are still to be taken; run by wave 0.  Lane l reads all the slots
+// with broadcast LDS reads and counts the keys above its own and equal to it;
+// the lanes holding the krem-th largest value write the same pair.  (Ranking
+// up to 256 keys with four threads each over the whole block measured slower
+// than the 8-bit pass it would replace.)
+constexpr int kSmall = 64;
+__device__ __forceinline__ void rank_small(const unsigned* s_key, int n, int krem, unsigned* s_T, int* s_krem) {
+  const int lane = threadIdx.x;
+  const unsigned mine = lane < n ? s_key[lane] : 0u;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int q = 0; q < kSmall / 4; ++q) {
+    const uint4 o = ((const uint4*)s_key)[q];  // one address for every lane: a broadcast
+    gt += (int)(o.x > mine) + (int)(o.y > mine) + (int)(o.z > mine) + (int)(o.w > mine);
+    eq += (int)(o.x == mine) + (int)(o.y == mine) + (int)(o.z == mine) + (int)(o.w == mine);
+  }
+  if (lane < n && gt < krem && krem <= gt + eq) {
+    *s_T = mine;
+    *s_krem = krem - gt;
   }
 }
 
@@ -129,14 +215,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                              int32_t c_max, const int32_t* __restrict__ n_chunks,
                                                              int32_t k, int32_t* __restrict__ idx,
                                                              uint2* __restrict__ cand, int32_t L) {
+  __shared__ __attribute__((aligned(16))) int s_wide[kWideWords];
   __shared__ int s_hist[2][kHistWords];
-  __shared__ unsigned s_warp[2 * kTopkWaves];
+  __shared__ __attribute__((aligned(16))) unsigned s_warp[2 * kTopkWaves];
+  __shared__ __attribute__((aligned(16))) unsigned s_tot[kTopkWaves];
   __shared__ unsigned s_prefix;
-  __shared__ int s_krem;
+  __shared__ int s_krem, s_cnt, s_n;
+  __shared__ __attribute__((aligned(16))) unsigned s_small[kSmall];
   const int row = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const size_t row_id = (size_t)b * rows + row;
   const int i0 = tid * IPT;
+  if (tid == 0) s_n = 0;
+  if (tid < kSmall) s_small[tid] = 0u;
+  // the row's chunk count is read now, so its round trip overlaps the loads
+  const int n_chunks_b = n_chunks[b];
+  asm volatile("" : : "s"(n_chunks_b));
 
   // Items first: every load is in bounds (index clamped into the row) and
   // none waits for another or for the chunk count.
@@ -190,8 +284,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       }
     }
   }
-  for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;
-  const int C = min(max(n_chunks[b], 0), c_max);
+  // The first histogram is cleared while the loads are in flight; the
+  // barrier after it is the last one before the first pass, so each thread
+  // starts counting as soon as its own keys arrive.
+  for (int j = tid; j < kWideWords / 4; j += kTopkThreads) ((uint4*)s_wide)[j] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  const int C = min(max(n_chunks_b, 0), c_max);
 
   if (C <= k) {
     if (SRC != kRowSlice) {
@@ -217,27 +315,68 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     for (int j = n_items + tid; j < k; j += kTopkThreads) out[j] = make_uint2(0u, 0xFFFFFFFFu);
     return;
   }
-  __syncthreads();
 
   unsigned prefix = 0;
   int krem = k;
-  for (int pass = 0; pass < 4; ++pass) {  // (left to the compiler to unroll: 0.7 us faster than a rolled loop)
-    const int shift = 24 - 8 * pass;
-    int* h = s_hist[pass & 1];
-    int* hn = s_hist[(pass & 1) ^ 1];
-    for (int j = tid; j < kHistWords; j += kTopkThreads) hn[j] = 0;  // next pass's histogram
+  // First pass: the 11-bit top digit of every key.
+  {
+    const int sub = (lane & (kSub - 1)) * kWideStride;
+    for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;  // the next pass's histogram
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if (key[j] != 0u) atomicAdd(&s_wide[sub + (key[j] >> digit_shift(0))], 1);
+    __syncthreads();
+    pick_wide(s_wide, krem, s_tot, &s_prefix, &s_krem, &s_cnt);
+    prefix = s_prefix;
+    krem = s_krem;
+  }
+  // Later passes: the next 8 (last: 5) bits of the keys still in the running,
+  // then the bin holding the krem-th largest.
+  auto radix_pass = [&](const int pass) {
+    const int shift = digit_shift(pass), width = digit_shift(pass - 1) - digit_shift(pass);
+    int* h = s_hist[(pass - 1) & 1];
+    int* hn = s_hist[pass & 1];
+    if (pass < 3)
+      for (int j = tid; j < kHistWords; j += kTopkThreads) hn[j] = 0;  // the next pass's histogram
     const int sub = (lane & (kSub - 1)) * kHistStride;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const unsigned kk = key[j];
-      const bool match = kk != 0u && (pass == 0 || (kk >> (shift + 8)) == prefix);
-      if (match) atomicAdd(&h[sub + ((kk >> shift) & 255u)], 1);
+      if (kk != 0u && (kk >> digit_shift(pass - 1)) == prefix) atomicAdd(&h[sub + ((kk >> shift) & ((1u << width) - 1u))], 1);
     }
     __syncthreads();
-    if (tid < 64) pick_bin(h, prefix, krem, &s_prefix, &s_krem);
+    if (tid < 64) pick_bin(h, prefix, width, krem, &s_prefix, &s_krem, &s_cnt);
     __syncthreads();
     prefix = s_prefix;
     krem = s_krem;
+  };
+  // A bin of at most kSmall keys (after 19 bits, real score rows leave one
+  // or a few there): its keys are copied to LDS and ranked by one wave in
+  // place of the remaining passes (each pass costs two block barriers and a
+  // bin pick).
+  auto finish_small = [&](const int pass) {
+    const int shift = digit_shift(pass);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const unsigned kk = key[j];
+      if (kk != 0u && (kk >> shift) == prefix) s_small[atomicAdd(&s_n, 1)] = kk;
+    }
+    __syncthreads();
+    if (tid < 64) rank_small(s_small, s_n, krem, &s_prefix, &s_krem);
+    __syncthreads();
+    prefix = s_prefix;
+    krem = s_krem;
+  };
+  if (s_cnt <= TF_TOPK_SMALL) {
+    finish_small(0);
+  } else {
+    radix_pass(1);
+    if (s_cnt <= TF_TOPK_SMALL) {
+      finish_small(1);
+    } else {
+      radix_pass(2);
+      if (s_cnt <= TF_TOPK_SMALL) finish_small(2); else radix_pass(3);
+    }
   }
   const unsigned T = prefix;
 
@@ -279,7 +418,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel_long(const float* __
                                                                   int32_t c_max, const int32_t* __restrict__ n_chunks,
                                                                   int32_t k, int32_t* __restrict__ idx) {
   __shared__ int s_hist[kTopkWaves][256];
-  __shared__ unsigned s_warp[2 * kTopkWaves];
+  __shared__ __attribute__((aligned(16))) unsigned s_warp[2 * kTopkWaves];
   __shared__ unsigned s_prefix;
   __shared__ int s_krem;
   const int row = blockIdx.x, b = blockIdx.y;
@@ -347,7 +486,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel_long(const float* __
   const int eq_before = (int)block_excl_scan((unsigned)n_eq, s_warp);
   const int take_eq = min(max(krem - eq_before, 0), n_eq);
   const int mine = n_gt + take_eq;
-  int pos = (int)block_excl_scan((unsigned)mine, s_warp);
+  int pos = (int)block_excl_scan((unsigned)mine, s_warp + kTopkWaves);
   int eq_left = take_eq;
   for (int i = i0; i < i1; ++i) {
     const unsigned kk = order_key(src[i]);

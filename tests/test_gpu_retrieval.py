@@ -235,3 +235,54 @@ def test_topk_split_rows(B, rows, C, ks):
                 for g in range(rows):
                     ref = oracle.select_topk(s[b, g, :n_b[b]].astype(np.float64), k)
                     assert np.array_equal(idx[b, g], ref), (n_b[b], k, b, g)
+
+
+def _cluster_row(rng, C, k, m, shared_bits, above, ties=False):
+    """A row whose k-th largest score lies in a cluster of m keys that share
+    their top `shared_bits` key bits: `above` large scores, the cluster, the
+    rest small.  With ties, the cluster holds few distinct values."""
+    row = rng.standard_normal(C).astype(np.float32)          # small: |x| < 8 almost surely
+    row = np.clip(row, -7.5, 7.5)
+    pos = rng.permutation(C)
+    row[pos[:above]] = (100.0 + rng.random(above) * 50).astype(np.float32)
+    base = np.float32(8.0).view(np.uint32)                   # key bits of positive floats: float bits | 2^31
+    span = 1 << (32 - shared_bits)                           # values sharing the top shared_bits key bits
+    steps = rng.integers(0, 4 if ties else span, m) if span > 1 else np.zeros(m, np.int64)
+    row[pos[above:above + m]] = (base + steps.astype(np.uint32)).view(np.float32)
+    return row
+
+
+def test_topk_headline_shape_adversarial():
+    """The benchmark's top-k shape exactly: 32 rows of 16384 chunks, k = 512,
+    bit-exact against the oracle, on rows that steer every path of the radix
+    selection: GPU-like scores, the k-th key inside a cluster of 63 / 64 / 65 /
+    200 keys sharing their top 16, 19 or 24 key bits (with and without ties),
+    all equal, NaN-heavy, all NaN, +-0, +-inf at the boundary, heavy ties,
+    subnormal-range values."""
+    rng = np.random.default_rng(140)
+    C, k = 16384, 512
+    rows = []
+    q = rng.standard_normal(128)
+    kb = rng.standard_normal((C, 128)) / np.sqrt(8)
+    kb[rng.choice(C, 164, replace=False)] += 0.5 * q
+    rows.append((kb @ q).astype(np.float32))                 # scores shaped like the workload's
+    for m in (63, 64, 65, 200):
+        for bits in (16, 19, 24):
+            rows.append(_cluster_row(rng, C, k, m, bits, above=k - min(m, 40)))
+    rows.append(_cluster_row(rng, C, k, 64, 16, above=k - 30, ties=True))
+    rows.append(_cluster_row(rng, C, k, 300, 24, above=k - 150, ties=True))
+    rows.append(np.zeros(C, np.float32))                                        # all equal
+    r = np.zeros(C, np.float32); r[::2] = -0.0; rows.append(r)                  # +-0
+    r = rng.standard_normal(C).astype(np.float32); r[rng.choice(C, 6000, replace=False)] = np.nan; rows.append(r)
+    rows.append(np.full(C, np.nan, np.float32))
+    r = rng.standard_normal(C).astype(np.float32); r[rng.choice(C, 511, replace=False)] = np.inf
+    r[rng.choice(C, 3000, replace=False)] = -np.inf; rows.append(r)            # +inf just short of k
+    rows.append((np.round(rng.standard_normal(C) * 2) / 4).astype(np.float32))  # heavy ties
+    rows.append((rng.standard_normal(C) * 1e-38).astype(np.float32))           # subnormal range
+    while len(rows) < 32:
+        rows.append((rng.standard_normal(C) * rng.uniform(0.1, 50)).astype(np.float32))
+    scores = np.stack(rows[:32])[None]
+    idx = run_topk(scores, [C], k)
+    for g in range(32):
+        ref = oracle.select_topk(scores[0, g].astype(np.float64), k)
+        assert np.array_equal(idx[0, g], ref), g
