@@ -30,6 +30,7 @@ EXPORTS = [
     "tf_verify_attn", "tf_verify_attn_workspace_size", "tf_accept", "tf_accept_workspace_size",
     "tf_append_kv", "tf_commit_length", "tf_collect_candidates", "tf_verify_tree_attn", "tf_tree_masks",
     "tf_tree_accept", "tf_tree_accept_workspace_size",
+    "tf_verify_attn_noalloc", "tf_verify_attn_noalloc_max_bytes",
 ]
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         "tf_tree_masks": (ctypes.c_int, [vp, i32, i32, vp, vp]),
         "tf_tree_accept": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]),
         "tf_tree_accept_workspace_size": (sz, [i32, i32]),
+        "tf_verify_attn_noalloc": (ctypes.c_int, [vp, i32, i32, vp, vp, dp, vp, vp, vp]),
+        "tf_verify_attn_noalloc_max_bytes": (sz, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -312,6 +315,28 @@ def verify_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc,
                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, q.device)),
            "tf_verify_attn")
     return out, lse
+
+
+def verify_attn_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv: KVDesc, out: torch.Tensor,
+                        lse: Optional[torch.Tensor] = None, stream=None):
+    """tf_verify_attn_noalloc: verify attention with the library's built-in
+    scratch instead of a workspace.  Nothing is allocated, here either: out
+    (fp32 [B][Hq][Q][d]) is the caller's, lse ([B][Hq][Q]) is optional."""
+    _need(q, "q", kv.dtype)
+    _need(K, "K", kv.dtype)
+    _need(V, "V", kv.dtype)
+    _need(out, "out", torch.float32)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    Hq, Q = q.shape[1], q.shape[2]
+    kd = kv.c()
+    _check(lib().tf_verify_attn_noalloc(_ptr(q), Hq, Q, _ptr(K), _ptr(V), ctypes.byref(kd), _ptr(out), _ptr(lse),
+                                        _stream(stream, q.device)), "tf_verify_attn_noalloc")
+    return out, lse
+
+
+def verify_attn_noalloc_max_bytes() -> int:
+    return int(lib().tf_verify_attn_noalloc_max_bytes())
 
 
 def accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor, uniforms: torch.Tensor,

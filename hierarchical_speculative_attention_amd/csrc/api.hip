@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "tf_internal.h"
 
@@ -378,6 +379,79 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
   fill_plan(a, plan, ws);
   return attn_call("tf_verify_attn", kv->dtype, tfk::kVerify, a, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// a6 without a caller workspace, for callers that cannot allocate (code under
+// graph capture, serving loops that forbid allocation).  The split partials
+// live in `scratch`, a file-scope device array of kNoAllocScratchBytes that
+// every GPU the library runs on holds until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it names a
+// host-side stand-in): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and that address is what the
+// kernels get.  Every call on a GPU shares that GPU's copy, so calls that
+// overlap on one GPU (different streams, or different host threads) race.
+// The partials need no clearing: each split writes every value it is later
+// read for.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's copy of `scratch` (looked up on the
+// first call made with the device current); TF_ERR_* on failure.
+int scratch_on_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  TRY(check_hip(hipGetDevice(&dev), "hipGetDevice"));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    TRY(check_hip(hipStreamGetDevice(stream, &sdev), "hipStreamGetDevice"));
+    if (sdev != dev) return fail(TF_ERR_INVALID_ARG, "stream is on device %d but device %d is current", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(TF_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    TRY(check_hip(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!ptr || !aligned(ptr, 256)) return fail(TF_ERR_HIP, "scratch address %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+TF_EXPORT size_t tf_verify_attn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+TF_EXPORT int tf_verify_attn_noalloc(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                                     const tf_kv_desc* kv, float* out, float* lse, tf_stream_t stream) {
+  TRY(check_desc(kv, "kv", false));
+  if (Hq < 1 || Hq % kv->H != 0) return fail(TF_ERR_INVALID_ARG, "Hq=%d is not a multiple of H=%d", Hq, kv->H);
+  if (Q < 1) return fail(TF_ERR_INVALID_ARG, "Q must be >= 1");
+  if ((long)(Hq / kv->H) * Q > tfk::kMaxRows)
+    return fail(TF_ERR_UNSUPPORTED, "G*Q = %ld query rows per KV head (at most %d)", (long)(Hq / kv->H) * Q,
+                tfk::kMaxRows);
+  if (kv->B == 0) return ok();
+  TRY(check_ptr(q, "q", 16));
+  TRY(check_ptr(K, "K", 16));
+  TRY(check_ptr(V, "V", 16));
+  TRY(check_ptr(out, "out", 16));
+  if (lse) TRY(check_ptr(lse, "lse", 4));
+  const tfk::SplitPlan plan =
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
+  if (plan.total_bytes > kNoAllocScratchBytes)
+    return fail(TF_ERR_WORKSPACE, "this call needs %zu bytes of split partials; the built-in scratch holds %zu "
+                "(use tf_verify_attn with a workspace)", plan.total_bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (plan.total_bytes) TRY(scratch_on_current_device((hipStream_t)stream, &ws));
+  tfk::AttnArgs a;
+  fill_common(a, q, K, V, kv, Hq, Q, out, lse);
+  fill_plan(a, plan, ws);
+  return attn_call("tf_verify_attn_noalloc", kv->dtype, tfk::kVerify, a, (hipStream_t)stream);
 }
 
 TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,

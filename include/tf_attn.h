@@ -212,6 +212,26 @@ int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const vo
 size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len);
 
 /*
+ * a6 without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops or harnesses that forbid
+ * allocation).  Same arguments, semantics and results as tf_verify_attn
+ * (bitwise: the same kernels and split plan) except that the split partials
+ * go to a scratch array built into the library: every GPU the library runs
+ * on holds tf_verify_attn_noalloc_max_bytes() = 48 MiB of it until the process
+ * ends, and a call whose partials need more (tf_verify_attn_workspace_size
+ * above that; e.g. 8 sequences of 128K rows and G * Q = 36) is refused with
+ * TF_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing.
+ * The scratch is shared by every call on that GPU: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  stream must belong to the current device (TF_ERR_INVALID_ARG
+ * otherwise); the scratch's device address is looked up on the first call on
+ * each device.
+ */
+int tf_verify_attn_noalloc(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
+                           const tf_kv_desc* kv, float* out, float* lse, tf_stream_t stream);
+size_t tf_verify_attn_noalloc_max_bytes(void);
+
+/*
  * a6 over a candidate tree.  [blog] Force 3 evaluates the candidate tree that
  * Force 2 assembles in one parallel pass with tree attention.  The last Q
  * cache rows hold the tree's nodes in order: node m is row n_b - Q + m.

@@ -238,3 +238,24 @@ def test_topk_workspace_follows_documented_rule():
                 split = B * rows <= 16 and 16384 < c_max <= 65536 and 2 * k <= sl and k <= 2048
                 want = B * rows * 8 * k * 8 if split else 0
                 assert L.tf_select_topk_workspace_size(B, rows, c_max, k) == want, (B, rows, c_max, k)
+
+
+def test_verify_noalloc_validates_before_any_device_call():
+    """The entry point that allocates nothing refuses, on the host and before
+    any HIP call, arguments tf_verify_attn refuses and a call whose split
+    partials exceed its built-in scratch (no GPU is touched here)."""
+    L = T.lib()
+    cap = L.tf_verify_attn_noalloc_max_bytes()
+    assert cap == 48 << 20
+    big = desc(B=8, H=32, max_len=1 << 20)
+    assert T.lib().tf_verify_attn_workspace_size(8, 32, 32, 7, 1 << 20) > cap
+    st = L.tf_verify_attn_noalloc(FAKE, 32, 7, FAKE, FAKE, ctypes.byref(big), FAKE, None, None)
+    assert st == T.TF_ERR_WORKSPACE
+    assert b"scratch" in L.tf_last_error_detail()
+    kv = desc(B=1, H=4, max_len=100)
+    assert L.tf_verify_attn_noalloc(FAKE, 6, 5, FAKE, FAKE, ctypes.byref(kv), FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_verify_attn_noalloc(FAKE, 4, 0, FAKE, FAKE, ctypes.byref(kv), FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_verify_attn_noalloc(None, 4, 5, FAKE, FAKE, ctypes.byref(kv), FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    assert L.tf_verify_attn_noalloc(FAKE, 4, 5, FAKE, FAKE, None, FAKE, None, None) == T.TF_ERR_INVALID_ARG
+    empty = desc(B=0, H=4, max_len=0)
+    assert L.tf_verify_attn_noalloc(None, 4, 5, None, None, ctypes.byref(empty), None, None, None) == T.TF_OK
