@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-three-tier", action="store_true", help="skip the three-tier step loop")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the per-call timing of sparse verification, tree verification / accept and appends")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-kernel figures of the GQA 512K and ragged 8-sequence workloads")
     return ap.parse_args()
 
 
@@ -86,8 +88,221 @@ def read_traffic():
         return None
 
 
+TRACE_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_kernel_trace.txt")
+
+
+def read_kernel_trace(verify_bytes):
+    """Each verify kernel's own average duration from the committed rocprofv3
+    kernel-trace summary (if it was taken on the current kernel source), and
+    the fractions of the HBM peak they give: the attention kernel alone, and
+    the attention kernel plus the split merge."""
+    if not os.path.exists(TRACE_FILE):
+        return None
+    kv = {}
+    for line in open(TRACE_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attn_hip_sha256") != sources_sha(VERIFY_SRCS):
+        return None
+    try:
+        a, m = float(kv["attention_kernel_avg_us"]), float(kv["split_merge_kernel_avg_us"])
+    except (KeyError, ValueError):
+        return None
+    return {"attention_kernel_us": a, "split_merge_kernel_us": m,
+            "frac_attention_kernel": round(verify_bytes / (a * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac_both_kernels": round(verify_bytes / ((a + m) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "source": os.path.relpath(TRACE_FILE, ROOT)}
+
+
 class Layer:
     pass
+
+
+def build_layers(W, layers, Q, ck_dt, tdt, dev, stream):
+    """The workload's layers, generated on the device (synth.make_layer_torch):
+    full K/V with EXTRA_ROWS of room per sequence, the queries, the chunk-key
+    buffer and a sink + window ring per layer."""
+    import torch
+    import hierarchical_speculative_attention_amd as tf
+    from hierarchical_speculative_attention_amd import synth
+    B, Hq, Hkv, d, lens, cs = W["B"], W["Hq"], W["Hkv"], W["d"], W["lens"], W["chunk_size"]
+    S, Wn = W["n_sink"], W["window"]
+    C = [-(-n // cs) for n in lens]
+    L = []
+    with torch.cuda.stream(stream):
+        for l in range(layers):
+            K, V, qv, qd, lay, planted = synth.make_layer_torch(
+                lens=lens, Hq=Hq, Hkv=Hkv, d=d, dtype=W["dtype"], Q=Q, chunk_size=cs, plant=W["plant"],
+                seed=0, layer=l, device=dev, plant_fraction=W.get("plant_fraction", 0.01),
+                plant_count=W.get("plant_count", 0), zipf_s=W.get("zipf_s", 1.1), extra_rows=EXTRA_ROWS)
+            x = Layer()
+            x.K, x.V, x.qv, x.qd = K, V, qv, qd.view(B, Hq, d)
+            x.kv = tf.KVDesc.from_layout(lay, tdt, dev)
+            ck_lay = synth.KVLayout.build(C, Hkv, d, caps=C)
+            x.ckd = tf.KVDesc.from_layout(ck_lay, ck_dt, dev)
+            x.ck = torch.empty(ck_lay.total_elems, dtype=ck_dt, device=dev)
+            g = torch.Generator(device=dev).manual_seed(synth.torch_seed(0, l, "ring"))
+            scap = S + Wn + synth.STREAM_SLACK
+            s_lay = synth.KVLayout.build(lens, Hkv, d, caps=[scap] * B)
+            x.Ks = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
+            x.Vs = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
+            x.sd = tf.KVDesc.from_layout(s_lay, tdt, dev)
+            x.planted = planted
+            L.append(x)
+    stream.synchronize()
+    return L
+
+
+def step_context(W, budget, gamma, ck_dt, tdt, dev, stream):
+    """Buffers one decode step of the workload shares across its layers, and
+    the per-layer calls of the step."""
+    import torch
+    import hierarchical_speculative_attention_amd as tf
+    from hierarchical_speculative_attention_amd import synth
+    c = Layer()
+    c.B, c.Hq, c.Hkv, c.d, c.lens = W["B"], W["Hq"], W["Hkv"], W["d"], W["lens"]
+    c.cs, c.budget, c.gamma, c.vocab = W["chunk_size"], budget, gamma, W["vocab"]
+    c.S, c.Wn = W["n_sink"], W["window"]
+    c.Q, c.k = gamma + 1, budget // c.cs
+    c.C = [-(-n // c.cs) for n in c.lens]
+    c.c_max = max(c.C)
+    B, Hq, Hkv, d, Q, k = c.B, c.Hq, c.Hkv, c.d, c.Q, c.k
+    with torch.cuda.stream(stream):
+        c.n_chunks = torch.tensor(c.C, dtype=torch.int32, device=dev)
+        c.tail_chunk = torch.tensor([max(0, (n - Q) // c.cs) for n in c.lens], dtype=torch.int32, device=dev)
+        c.tail_count = (Q + c.cs - 1) // c.cs + 1
+        c.scores = torch.empty((B, Hkv, c.c_max), dtype=torch.float32, device=dev)
+        c.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        c.o_sp = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        c.l_sp = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        c.o_st = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        c.l_st = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        c.o_v = torch.empty((B, Hq, Q, d), dtype=torch.float32, device=dev)
+        c.l_v = torch.empty((B, Hq, Q), dtype=torch.float32, device=dev)
+        c.ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Q, max(c.lens)), dev)
+        c.ws_s = tf.workspace(tf.sparse_attn_workspace_size(B, Hq, Hkv, k, c.cs), dev)
+        c.ws_t = tf.workspace(tf.select_topk_workspace_size(B, Hkv, c.c_max, k), dev)
+        c.ws_a = tf.workspace(tf.accept_workspace_size(B, gamma, c.vocab), dev)
+        c.acc_in = synth.make_accept_inputs(B=B, gamma=gamma, vocab=c.vocab, seed=0)
+        c.tgt = torch.from_numpy(c.acc_in.target).to(dev)
+        c.drf = torch.from_numpy(c.acc_in.draft).to(dev)
+        c.tok = torch.from_numpy(c.acc_in.tokens).to(dev)
+        c.uni = torch.from_numpy(c.acc_in.uniforms).to(dev)
+        c.n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+        c.nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        c.host_out = torch.empty(2 * B, dtype=torch.int32).pin_memory()
+    stream.synchronize()
+
+    def layer_calls(x):
+        return [
+            ("chunk_refresh", lambda: tf.build_chunk_keys(x.K, x.kv, c.cs, x.ck, x.ckd, chunk_begin=c.tail_chunk,
+                                                          max_chunks=c.tail_count, stream=stream)),
+            ("score", lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c.c_max, scores=c.scores, stream=stream)),
+            ("topk", lambda: tf.select_topk(c.scores, c.n_chunks, k, idx=c.idx, ws=c.ws_t, stream=stream)),
+            ("sparse", lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, c.idx, c.cs, out=c.o_sp, lse=c.l_sp, ws=c.ws_s,
+                                              stream=stream)),
+            ("stream", lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, c.S, c.Wn, out=c.o_st, lse=c.l_st,
+                                              stream=stream)),
+            ("verify", lambda: tf.verify_attn(x.qv, x.K, x.V, x.kv, out=c.o_v, lse=c.l_v, ws=c.ws_v, stream=stream)),
+        ]
+
+    def accept_call():
+        tf.accept(c.tgt, c.drf, c.tok, c.uni, 1.0, n_accepted=c.n_acc, next_token=c.nxt, ws=c.ws_a, stream=stream)
+
+    def readback():
+        c.host_out[:B].copy_(c.n_acc, non_blocking=True)
+        c.host_out[B:].copy_(c.nxt, non_blocking=True)
+        stream.synchronize()  # the step ends with n_accepted / next_token on the host
+
+    c.layer_calls, c.accept_call, c.readback = layer_calls, accept_call, readback
+    return c
+
+
+def prefill_chunk_keys(L, c, stream):
+    """Chunk-mean keys of every layer over the whole cache (a prefill cost,
+    timed on its own); returns milliseconds."""
+    import torch
+    import hierarchical_speculative_attention_amd as tf
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for x in L:
+        tf.build_chunk_keys(x.K, x.kv, c.cs, x.ck, x.ckd, stream=stream)
+    e1.record(stream)
+    stream.synchronize()
+    return e0.elapsed_time(e1)
+
+
+KINDS = ["chunk_refresh", "score", "topk", "sparse", "stream", "verify", "accept"]
+BOUND = {"chunk_refresh": "latency", "score": "hbm", "topk": "latency", "sparse": "hbm", "stream": "latency",
+         "verify": "hbm", "accept": "latency"}
+
+
+def time_kinds(L, c, names, stream):
+    """One HIP graph per kernel kind with one launch per layer (the layers
+    cycled to at least MIN_LAUNCHES launches; SMALL_REPS calls for the accept),
+    WARM_REPLAYS untimed replays, then KERNEL_REPS replays between HIP events
+    on the launch stream.  Returns (mean us per call, {median, p10, p90})."""
+    import torch
+    us, dist = {}, {}
+    cyc = -(-MIN_LAUNCHES // len(L))  # a graph of fewer launches would be timed with its launch overhead
+    Lc = L * cyc
+    with torch.cuda.stream(stream):
+        for n in names:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                if n == "accept":
+                    for _ in range(SMALL_REPS):
+                        c.accept_call()
+                else:
+                    for x in Lc:
+                        dict(c.layer_calls(x))[n]()
+            for _ in range(WARM_REPLAYS):
+                g.replay()
+            stream.synchronize()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(KERNEL_REPS + 1)]
+            evs[0].record(stream)
+            for r in range(KERNEL_REPS):
+                g.replay()
+                evs[r + 1].record(stream)
+            stream.synchronize()
+            per = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 for r in range(KERNEL_REPS)])
+            per /= SMALL_REPS if n == "accept" else len(Lc)    # us per call, one value per replay
+            us[n] = float(per.mean())
+            dist[n] = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+                       "p90": float(np.percentile(per, 90))}
+    return us, dist, cyc
+
+
+def algorithmic_bytes(c, ckb):
+    """Bytes each call must move (no re-read, no avoided work counted)."""
+    kvb = 2  # bytes per stored K/V element
+    d, Hq, Hkv, B, k, cs, Q = c.d, c.Hq, c.Hkv, c.B, c.k, c.cs, c.Q
+    row = d * kvb
+    lens = c.lens
+    sel_tokens = sum(min(k * cs, n) for n in lens)
+    vis_stream = sum(min(c.S, n) + max(0, n - max(c.S, n - c.Wn)) for n in lens)
+    return {
+        "chunk_refresh": Hkv * B * c.tail_count * (cs * row + d * ckb),
+        "score": Hkv * sum(c.C) * d * ckb + B * Hq * row + B * Hkv * c.c_max * 4,
+        "topk": B * Hkv * (sum(c.C) // B if B else 0) * 4 + B * Hkv * k * 4,
+        "sparse": Hkv * sel_tokens * 2 * row + B * Hkv * k * 4 + B * Hq * (row + d * 4 + 4),
+        "stream": Hkv * vis_stream * 2 * row + B * Hq * (row + d * 4 + 4),
+        "verify": Hkv * sum(lens) * 2 * row + B * Hq * Q * (row + d * 4 + 4),
+        "accept": B * (2 * c.gamma + 1) * c.vocab * 4,
+    }
+
+
+def kernel_table(us, dist, by, names):
+    out = {}
+    for n in names:
+        gbs = by[n] / (us[n] * 1e-6) / 1e9
+        out[n] = {"us": round(us[n], 2), "us_median": round(dist[n]["median"], 2),
+                  "us_p10": round(dist[n]["p10"], 2), "us_p90": round(dist[n]["p90"], 2),
+                  "GB_s": round(gbs, 1), "bytes": int(by[n]), "bound": BOUND[n]}
+        if BOUND[n] == "hbm":
+            out[n]["frac"] = round(gbs / HBM_PEAK_GBPS, 4)
+    return out
 
 
 def main():
@@ -102,7 +317,6 @@ def main():
 
     import torch
     from hierarchical_speculative_attention_amd import synth
-    import hierarchical_speculative_attention_amd as tf
 
     W = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -125,83 +339,19 @@ def main():
     ck_dt = torch.float32 if args.ck_dtype == "fp32" else tdt
     n_max = max(lens)
     C = [-(-n // cs) for n in lens]
-    c_max = max(C)
     t_setup = time.perf_counter()
 
     # ---- inputs, resident in HBM ------------------------------------------
-    L = []
-    with torch.cuda.stream(stream):
-        for l in range(layers):
-            K, V, qv, qd, lay, planted = synth.make_layer_torch(
-                lens=lens, Hq=Hq, Hkv=Hkv, d=d, dtype=W["dtype"], Q=Q, chunk_size=cs, plant=W["plant"],
-                seed=0, layer=l, device=dev, plant_fraction=W.get("plant_fraction", 0.01),
-                plant_count=W.get("plant_count", 0), zipf_s=W.get("zipf_s", 1.1), extra_rows=EXTRA_ROWS)
-            x = Layer()
-            x.K, x.V, x.qv, x.qd = K, V, qv, qd.view(B, Hq, d)
-            x.kv = tf.KVDesc.from_layout(lay, tdt, dev)
-            ck_lay = synth.KVLayout.build(C, Hkv, d, caps=C)
-            x.ckd = tf.KVDesc.from_layout(ck_lay, ck_dt, dev)
-            x.ck = torch.empty(ck_lay.total_elems, dtype=ck_dt, device=dev)
-            g = torch.Generator(device=dev).manual_seed(synth.torch_seed(0, l, "ring"))
-            scap = S + Wn + synth.STREAM_SLACK
-            s_lay = synth.KVLayout.build(lens, Hkv, d, caps=[scap] * B)
-            x.Ks = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
-            x.Vs = torch.randn(s_lay.total_elems, generator=g, device=dev).to(tdt)
-            x.sd = tf.KVDesc.from_layout(s_lay, tdt, dev)
-            x.planted = planted
-            L.append(x)
-        n_chunks = torch.tensor(C, dtype=torch.int32, device=dev)
-        tail_chunk = torch.tensor([max(0, (n - Q) // cs) for n in lens], dtype=torch.int32, device=dev)
-        tail_count = (Q + cs - 1) // cs + 1
-        scores = torch.empty((B, Hkv, c_max), dtype=torch.float32, device=dev)
-        idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
-        o_sp = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-        l_sp = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        o_st = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-        l_st = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        o_v = torch.empty((B, Hq, Q, d), dtype=torch.float32, device=dev)
-        l_v = torch.empty((B, Hq, Q), dtype=torch.float32, device=dev)
-        ws_v = tf.workspace(tf.verify_attn_workspace_size(B, Hq, Hkv, Q, n_max), dev)
-        ws_s = tf.workspace(tf.sparse_attn_workspace_size(B, Hq, Hkv, k, cs), dev)
-        ws_t = tf.workspace(tf.select_topk_workspace_size(B, Hkv, c_max, k), dev)
-        ws_a = tf.workspace(tf.accept_workspace_size(B, gamma, vocab), dev)
-        acc_in = synth.make_accept_inputs(B=B, gamma=gamma, vocab=vocab, seed=0)
-        tgt = torch.from_numpy(acc_in.target).to(dev)
-        drf = torch.from_numpy(acc_in.draft).to(dev)
-        tok = torch.from_numpy(acc_in.tokens).to(dev)
-        uni = torch.from_numpy(acc_in.uniforms).to(dev)
-        n_acc = torch.empty(B, dtype=torch.int32, device=dev)
-        nxt = torch.empty(B, dtype=torch.int32, device=dev)
-        host_out = torch.empty(2 * B, dtype=torch.int32).pin_memory()
-    stream.synchronize()
+    L = build_layers(W, layers, Q, ck_dt, tdt, dev, stream)
+    c = step_context(W, budget, gamma, ck_dt, tdt, dev, stream)
+    layer_calls, accept_call, readback = c.layer_calls, c.accept_call, c.readback
 
     # ---- prefill: chunk-mean keys of every layer (timed on its own) --------
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for x in L:
-        tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, stream=stream)
-    e1.record(stream)
-    stream.synchronize()
-    prefill_ms = e0.elapsed_time(e1)
+    prefill_ms = prefill_chunk_keys(L, c, stream)
     tokens_total = sum(lens)
     prefill_bytes = layers * Hkv * (tokens_total * d * 2 + sum(C) * d * L[0].ck.element_size())
 
     # ---- one decode step ----------------------------------------------------
-    def layer_calls(x):
-        return [
-            ("chunk_refresh", lambda: tf.build_chunk_keys(x.K, x.kv, cs, x.ck, x.ckd, chunk_begin=tail_chunk,
-                                                          max_chunks=tail_count, stream=stream)),
-            ("score", lambda: tf.score_chunks(x.qd, Hq, x.ck, x.ckd, c_max, scores=scores, stream=stream)),
-            ("topk", lambda: tf.select_topk(scores, n_chunks, k, idx=idx, ws=ws_t, stream=stream)),
-            ("sparse", lambda: tf.sparse_attn(x.qd, x.K, x.V, x.kv, idx, cs, out=o_sp, lse=l_sp, ws=ws_s,
-                                              stream=stream)),
-            ("stream", lambda: tf.stream_attn(x.qd, x.Ks, x.Vs, x.sd, S, Wn, out=o_st, lse=l_st, stream=stream)),
-            ("verify", lambda: tf.verify_attn(x.qv, x.K, x.V, x.kv, out=o_v, lse=l_v, ws=ws_v, stream=stream)),
-        ]
-
-    def accept_call():
-        tf.accept(tgt, drf, tok, uni, 1.0, n_accepted=n_acc, next_token=nxt, ws=ws_a, stream=stream)
-
     def step_gpu(verify_events=None):
         for x in L:
             for name, fn in layer_calls(x):
@@ -214,11 +364,6 @@ def main():
                 else:
                     fn()
         accept_call()
-
-    def readback():
-        host_out[:B].copy_(n_acc, non_blocking=True)
-        host_out[B:].copy_(nxt, non_blocking=True)
-        stream.synchronize()  # the step ends with n_accepted / next_token on the host
 
     with torch.cuda.stream(stream):
         # eager warm-up, then the step captured once as a HIP graph
@@ -252,36 +397,12 @@ def main():
         torch.cuda.synchronize()
         elapsed_eager = time.perf_counter() - t0
     verify_eager_avg_s = float(np.mean([a_.elapsed_time(b_) for a_, b_ in vev])) / 1e3
+    del graph
 
     # ---- per-kernel breakdown: one graph per kernel kind, one launch per layer
-    names = ["chunk_refresh", "score", "topk", "sparse", "stream", "verify", "accept"]
-    us, dist = {}, {}
-    cyc = -(-MIN_LAUNCHES // layers)  # a graph of fewer launches would be timed with its launch overhead
-    Lc = L * cyc
+    names = KINDS
+    us, dist, cyc = time_kinds(L, c, names, stream)
     with torch.cuda.stream(stream):
-        for n in names:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                if n == "accept":
-                    for _ in range(SMALL_REPS):
-                        accept_call()
-                else:
-                    for x in Lc:
-                        dict(layer_calls(x))[n]()
-            for _ in range(WARM_REPLAYS):
-                g.replay()
-            stream.synchronize()
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(KERNEL_REPS + 1)]
-            evs[0].record(stream)
-            for r in range(KERNEL_REPS):
-                g.replay()
-                evs[r + 1].record(stream)
-            stream.synchronize()
-            per = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 for r in range(KERNEL_REPS)])
-            per /= SMALL_REPS if n == "accept" else len(Lc)    # us per call, one value per replay
-            us[n] = float(per.mean())
-            dist[n] = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
-                       "p90": float(np.percentile(per, 90))}
         # secondary peak: a 1 GiB device-to-device copy (1 GiB read + 1 GiB written)
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -298,37 +419,17 @@ def main():
     verify_avg_s = us["verify"] * 1e-6
 
     # ---- algorithmic bytes --------------------------------------------------
-    kvb = 2  # bytes per stored K/V element
-    ckb = L[0].ck.element_size()
-    row = d * kvb
-    sel_tokens = sum(min(k * cs, n) for n in lens)
-    vis_stream = sum(min(S, n) + max(0, n - max(S, n - Wn)) for n in lens)
-    by = {
-        "chunk_refresh": Hkv * B * tail_count * (cs * row + d * ckb),
-        "score": Hkv * sum(C) * d * ckb + B * Hq * row + B * Hkv * c_max * 4,
-        "topk": B * Hkv * (sum(C) // B if B else 0) * 4 + B * Hkv * k * 4,
-        "sparse": Hkv * sel_tokens * 2 * row + B * Hkv * k * 4 + B * Hq * (row + d * 4 + 4),
-        "stream": Hkv * vis_stream * 2 * row + B * Hq * (row + d * 4 + 4),
-        "verify": Hkv * tokens_total * 2 * row + B * Hq * Q * (row + d * 4 + 4),
-        "accept": B * (2 * gamma + 1) * vocab * 4,
-    }
-    bound = {"chunk_refresh": "latency", "score": "hbm", "topk": "latency", "sparse": "hbm", "stream": "latency",
-             "verify": "hbm", "accept": "latency"}
-    kernels = {}
-    for n in names:
-        gbs = by[n] / (us[n] * 1e-6) / 1e9
-        kernels[n] = {"us": round(us[n], 2), "us_median": round(dist[n]["median"], 2),
-                      "us_p10": round(dist[n]["p10"], 2), "us_p90": round(dist[n]["p90"], 2),
-                      "GB_s": round(gbs, 1), "bytes": int(by[n]), "bound": bound[n]}
-        if bound[n] == "hbm":
-            kernels[n]["frac"] = round(gbs / HBM_PEAK_GBPS, 4)
+    by = algorithmic_bytes(c, L[0].ck.element_size())
+    kernels = kernel_table(us, dist, by, names)
     # few long rows are selected in slices, then merged (two launches)
-    kernels["topk"]["launches"] = 2 if ws_t is not None else 1
+    kernels["topk"]["launches"] = 2 if c.ws_t is not None else 1
     step_bytes = layers * sum(by[n] for n in names if n != "accept") + by["accept"]
     verify_bytes = by["verify"]
     achieved = verify_bytes / verify_avg_s / 1e9
-    # (the counters are of the verify launch at the default workload's shape)
-    traffic = read_traffic() if args.workload == DEFAULT_WORKLOAD and gamma == W["gamma"] else None
+    default_shape = args.workload == DEFAULT_WORKLOAD and gamma == W["gamma"] and budget == W["budget"]
+    # (the counters and the kernel trace are of the verify launch at the default workload's shape)
+    traffic = read_traffic() if default_shape else None
+    trace = read_kernel_trace(verify_bytes) if default_shape else None
     ms_per_step = elapsed / args.steps * 1e3
 
     result = {
@@ -361,12 +462,17 @@ def main():
                          "are then partly read from the Infinity Cache"),
         "roofline": {"kernel": "verify_attn (attn_kernel + combine_kernel, verify mode)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "frac_basis": "call level: one tf_verify_attn call = the attention kernel, then the split "
+                                   "merge kernel, timed together (see avg_launch_us); kernel_trace gives each "
+                                   "kernel's own rocprofv3 duration",
+                     "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(verify_bytes),
                      "avg_launch_us": round(verify_avg_s * 1e6, 2),
                      "timing": f"HIP events on the launch stream around each of {KERNEL_REPS} replays of a graph "
                                "of the step's verify launches (one per layer, back to back); mean over replays",
                      "eager_avg_launch_us": round(verify_eager_avg_s * 1e6, 2),
+                     "kernel_trace": trace,
                      "copy_GB_s": round(copy_gbps, 1),
                      "frac_of_copy": round(achieved / copy_gbps, 4)},
         "kernels": kernels,
@@ -379,6 +485,7 @@ def main():
                                "GB_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},
         "setup_s": round(time.perf_counter() - t_setup, 1),
     }
+    idx, acc_in = c.idx, c.acc_in
     if not args.no_next_rows:
         result["next_rows"] = next_rows_leg(L, lens, Hq, Hkv, d, cs, k, S, Wn, gamma, idx, acc_in, dev, stream)
         result["next_rows_timing"] = (f"per call: a HIP graph of one call per layer ({SMALL_REPS} in all for the "
@@ -394,7 +501,84 @@ def main():
             # the same oracle, on the calls the three-tier loop adds (reported beside next_rows)
             result["cpu_baseline"]["next_rows"] = next_rows_cpu_baseline(L[0], lens[0], Hq, Hkv, d, cs, idx, gamma,
                                                                          acc_in, tdt)
+        result["cpu_baseline"]["small_layer"] = cpu_baseline_small()
+    if not args.no_other_workloads and args.workload == DEFAULT_WORKLOAD:
+        # the step's layers leave the GPU before the other workloads are generated
+        del L, c, idx
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        others = {}
+        for name, b_, g_, cpu in OTHER_WORKLOADS:
+            others[f"{name}/budget{b_}/gamma{g_}"] = other_workload(name, b_, g_, args.steps, args.warmup, ck_dt,
+                                                                    dev, stream, cpu and not args.no_cpu_baseline)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        result["other_workloads"] = others
+        result["other_workloads_timing"] = ("the same per-kernel graphs as kernels (layers cycled to at least "
+                                            f"{MIN_LAUNCHES} launches), and for the multi-layer workload the whole "
+                                            "step replayed as a HIP graph (steps_per_s)")
     print(json.dumps(result), flush=True)
+
+
+# The other workloads measured beside the default one: (name, budget, gamma).
+OTHER_WORKLOADS = [("gqa-hq32-hkv8-512k-16layers", 8192, 8, False), ("ragged-b8-16k-128k", 4096, 6, True),
+                   ("ragged-b8-16k-128k", 2048, 4, False)]   # (name, budget, gamma, time the oracle too)
+
+
+def other_workload(name, budget, gamma, steps, warmup, ck_dt, dev, stream, cpu=False):
+    """Per-kernel figures of another workload at its own shape (and, with
+    several layers, the step rate): the same calls and timing as the default
+    workload's kernels."""
+    import torch
+    from hierarchical_speculative_attention_amd import synth
+    W = synth.WORKLOADS[name]
+    tdt = torch.bfloat16 if W["dtype"] == "bf16" else torch.float16
+    layers = W["layers"]
+    L = build_layers(W, layers, gamma + 1, ck_dt, tdt, dev, stream)
+    c = step_context(W, budget, gamma, ck_dt, tdt, dev, stream)
+    prefill_chunk_keys(L, c, stream)
+    out = {"batch": W["B"], "q_heads": W["Hq"], "kv_heads": W["Hkv"], "context": W["lens"] if W["B"] > 1 else
+           W["lens"][0], "layers": layers, "chunk_size": c.cs, "budget": budget, "gamma": gamma,
+           "verify_queries": c.Q, "kv_gib_per_layer": round(c.Hkv * sum(W["lens"]) * c.d * 2 * 2 / 2 ** 30, 2)}
+    if layers > 1:
+        with torch.cuda.stream(stream):
+            def step_gpu():
+                for x in L:
+                    for _, fn in c.layer_calls(x):
+                        fn()
+                c.accept_call()
+            step_gpu()
+            c.readback()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step_gpu()
+            for _ in range(warmup):
+                graph.replay()
+                c.readback()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                graph.replay()
+                c.readback()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            del graph
+        out["steps_per_s"] = round(steps / el, 3)
+        out["ms_per_step"] = round(el / steps * 1e3, 3)
+    names = KINDS
+    us, dist, cyc = time_kinds(L, c, names, stream)
+    by = algorithmic_bytes(c, L[0].ck.element_size())
+    out["kernels"] = kernel_table(us, dist, by, names)
+    out["kernels"]["topk"]["launches"] = 2 if c.ws_t is not None else 1
+    out["sparse_draft_pass_us"] = round(us["score"] + us["topk"] + us["sparse"], 2)
+    if cyc > 1:
+        out["kernels_note"] = (f"{layers} layer(s) cycled {cyc} times per graph; every call here moves more than "
+                               "the ~256 MB Infinity Cache except the latency-bound ones")
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(L[:1], W["lens"], c.Hq, c.Hkv, c.d, c.cs, c.k, c.S, c.Wn, c.Q, layers,
+                                           c.acc_in, tdt)
+    del L, c
+    return out
 
 
 def time_graph(fn, stream, per_replay):
@@ -634,6 +818,58 @@ def next_rows_cpu_baseline(x, n, Hq, Hkv, d, cs, idx, gamma, acc, tdt):
     oracle.tree_accept(acc.target[0], drf, tok, parent, acc.uniforms[0, :Qt], 1.0)
     out["tree_accept"] = {"us": round((time.perf_counter() - t0) * 1e6, 1), "sample": "one call"}
     return {"calls": out, "kind": "oracle", "cores": int(threads), "unit": "us per call"}
+
+
+def cpu_baseline_small():
+    """The oracle over the whole small single layer (8 heads, n = 4096, fp16,
+    chunk 8, budget 512, 4 sinks + 252 window, gamma = 4, vocabulary 32000):
+    one step (tail refresh, scores, top-k, sparse, streaming and verify
+    attention for every head, then one accept) on all cores and on one
+    thread.  Inputs come from the same seeded generators, on the host."""
+    import oracle
+    from hierarchical_speculative_attention_amd import synth
+    W = synth.WORKLOADS["tiny-h8-n4k-fp16"]
+    n, H, cs, dt = W["lens"][0], W["Hq"], W["chunk_size"], W["dtype"]
+    k, Q, S, Wn = W["budget"] // cs, W["gamma"] + 1, W["n_sink"], W["window"]
+    inp = synth.make_attn_inputs(lens=[n], Hq=H, Hkv=H, dtype=dt, Q=Q, seed=0, chunk_size=cs,
+                                 plant=W["plant"], plant_count=W["plant_count"])
+    st = synth.make_stream_inputs(lens=[n], Hq=H, Hkv=H, dtype=dt, n_sink=S, window=Wn, seed=0)
+    acc = synth.make_accept_inputs(B=1, gamma=W["gamma"], vocab=W["vocab"], seed=0)
+    lay = inp.layout
+    heads = []
+    for g in range(H):
+        K = oracle.widen(lay.head(inp.K, 0, g), dt)
+        V = oracle.widen(lay.head(inp.V, 0, g), dt)
+        heads.append((K, V, oracle.chunk_keys(K, n, cs),     # prefill: not timed
+                      oracle.widen(inp.q_draft[0, g, 0], dt), oracle.widen(inp.q_verify[0, g], dt),
+                      oracle.widen(st.K_logical[0][g], dt), oracle.widen(st.V_logical[0][g], dt),
+                      oracle.widen(st.q[0, g, 0], dt)))
+
+    def step():
+        t0 = time.perf_counter()
+        for K, V, ck, qd, qv, Kl, Vl, qs in heads:
+            c0 = max(0, (n - Q) // cs)
+            ck[c0:] = oracle.chunk_keys(K[c0 * cs:n], n - c0 * cs, cs)
+            sel = oracle.select_topk(oracle.chunk_scores(qd[None], ck), k)
+            oracle.sparse_attn(qd, K, V, n, sel, cs)
+            oracle.stream_attn_masked(qs, Kl, Vl, n, S, Wn)
+            oracle.verify_attn(qv, K, V, n)
+        oracle.accept(acc.target[0], acc.draft[0], acc.tokens[0], acc.uniforms[0], 1.0)
+        return time.perf_counter() - t0
+
+    out = {"workload": "tiny-h8-n4k-fp16 (8 heads, n 4096, fp16, budget 512, gamma 4)", "unit": "steps/s",
+           "kind": "oracle", "sample": "the whole step, every head"}
+    t = min(step() for _ in range(3))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        out["all_cores"] = {"value": round(1.0 / t, 3), "cores": int(threads), "s_per_step": round(t, 4)}
+        with threadpool_limits(limits=1):
+            t1 = min(step() for _ in range(3))
+        out["single_thread"] = {"value": round(1.0 / t1, 3), "cores": 1, "s_per_step": round(t1, 4)}
+    except ImportError:
+        out["all_cores"] = {"value": round(1.0 / t, 3), "cores": None, "s_per_step": round(t, 4)}
+    return out
 
 
 def cpu_model():
