@@ -293,6 +293,46 @@ def algorithmic_bytes(c, ckb):
     }
 
 
+BENCH_LIB = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "libtfbench.so")
+CEILING_GRIDS = (256, 512, 1024)
+
+
+def read_ceiling(L, stream):
+    """How fast HBM serves the verification pass's bytes when nothing else is
+    done with them: a kernel that only reads each layer's K and V (the
+    measurement aid libtfbench.so, verify's access shape), timed like the
+    per-kernel graphs (one launch per layer), for a few grid sizes."""
+    import ctypes
+    import torch
+    if not os.path.exists(BENCH_LIB):
+        return None
+    lib = ctypes.CDLL(BENCH_LIB)
+    lib.tfb_read_kv.restype = ctypes.c_int
+    lib.tfb_read_kv.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    cyc = -(-MIN_LAUNCHES // len(L))
+    Lc = L * cyc
+    nbytes = L[0].K.numel() * L[0].K.element_size()
+    sink = torch.empty(max(CEILING_GRIDS) * 4, dtype=torch.int32, device=L[0].K.device)
+    out = {}
+    with torch.cuda.stream(stream):
+        for grid in CEILING_GRIDS:
+            def launches():
+                for x in Lc:
+                    st = lib.tfb_read_kv(ctypes.c_void_p(x.K.data_ptr()), ctypes.c_void_p(x.V.data_ptr()), nbytes,
+                                         grid, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                    if st != 0:
+                        raise RuntimeError(f"tfb_read_kv: hip error {st}")
+            r = time_graph(launches, stream, len(Lc))
+            out[grid] = 2 * nbytes / (r["us"] * 1e-6) / 1e9
+    best = max(out, key=out.get)
+    return {"GB_s": round(out[best], 1), "grid": best, "bytes_per_launch": 2 * nbytes,
+            "GB_s_by_grid": {str(g): round(v, 1) for g, v in out.items()},
+            "what": "a kernel that only reads each layer's K and V (verify's access shape: 1 KB per wave "
+                    "instruction, nontemporal 16-byte loads, 4 per tensor in flight per lane), one launch per layer "
+                    "in a HIP graph; the best grid"}
+
+
 def kernel_table(us, dist, by, names):
     out = {}
     for n in names:
@@ -417,6 +457,7 @@ def main():
         copy_gbps = 2 * src.numel() * src.element_size() * COPY_REPS / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
     verify_avg_s = us["verify"] * 1e-6
+    ceiling = read_ceiling(L, stream)
 
     # ---- algorithmic bytes --------------------------------------------------
     by = algorithmic_bytes(c, L[0].ck.element_size())
@@ -473,6 +514,8 @@ def main():
                                "of the step's verify launches (one per layer, back to back); mean over replays",
                      "eager_avg_launch_us": round(verify_eager_avg_s * 1e6, 2),
                      "kernel_trace": trace,
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": (round(achieved / ceiling["GB_s"], 4) if ceiling else None),
                      "copy_GB_s": round(copy_gbps, 1),
                      "frac_of_copy": round(achieved / copy_gbps, 4)},
         "kernels": kernels,
