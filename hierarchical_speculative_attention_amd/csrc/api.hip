@@ -134,6 +134,7 @@ void fill_plan(tfk::AttnArgs& a, const tfk::SplitPlan& p, void* ws) {
   a.tpw = p.tpw;
   a.nsplit = p.nsplit;
   a.rows_pad = p.rows_pad;
+  a.tail_last = p.tail_last;
   if (p.total_bytes) {
     char* w = (char*)ws;
     a.part_ml = (float*)w;
@@ -344,6 +345,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
   if (plan.tpw < 128) plan.tpw = 128;
   plan.nsplit = 1;
   plan.rows_pad = ((a.rows + 15) / 16) * 16;
+  plan.tail_last = 0;
   plan.part_o_bytes = plan.part_ml_bytes = plan.total_bytes = 0;
   fill_plan(a, plan, nullptr);
   return attn_call("tf_stream_attn", sd->dtype, tfk::kStream, a, (hipStream_t)stream);

@@ -879,7 +879,21 @@ void attn_kernel(const AttnArgs a) {
       attn_item<DT, MODE, NQT>(a, lo, r / per, r % per, s_idx, s_stage, s_m, s_l);
     }
   } else {
-    attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, s_idx, s_stage, s_m, s_l);
+    // One item per workgroup: grid (splits, KV heads, sequences), or, when
+    // the plan ends in a short split per (sequence, KV head), a 1-D grid that
+    // puts those splits after all the others.  Workgroups are dispatched in
+    // index order, so the grid's second round is then made of the short
+    // items, not of full splits of the last heads.
+    if (a.tail_last) {
+      const int heads = a.B * a.Hkv;
+      const int full = a.nsplit - 1;
+      const int L = blockIdx.x;
+      const int split = L < full * heads ? L % full : full;
+      const int head = L < full * heads ? L / full : L - full * heads;
+      attn_item<DT, MODE, NQT>(a, head / a.Hkv, head % a.Hkv, split, s_idx, s_stage, s_m, s_l);
+    } else {
+      attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, s_idx, s_stage, s_m, s_l);
+    }
   }
 }
 
@@ -979,7 +993,16 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
   const long heads = (long)B * Hkv;
   const long per_head = target_wgs / heads;  // splits per (sequence, KV head) that keep the grid within target
   long tpw = max_tpw;
-  if (per_head >= 1) {
+  p.tail_last = 0;
+  if (per_head >= 1 && (long)max_virtual > per_head * max_tpw &&
+      (long)max_virtual - per_head * max_tpw <= max_tpw / 8) {
+    p.tail_last = 1;
+    // one round of full splits and a tail split of at most max_tpw / 8
+    // virtual tokens per (sequence, head): the tails are dispatched last
+    // (short items, run as the first full splits finish), cheaper than two
+    // rounds of half-size splits (a cache allocated a little past its
+    // length: Llama2-7B-128K with 512 spare rows, verify 322 -> 318 us)
+  } else if (per_head >= 1) {
     // whole rounds of per_head splits: one when the splits fit max_tpw, else
     // as few as do (a last round of a few long splits would run on its own)
     const long rounds = ((long)max_virtual + per_head * max_tpw - 1) / (per_head * max_tpw);
@@ -1006,6 +1029,10 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
 template <int DT, int MODE, bool FLAT>
 static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.Hkv, a.B), block(kThreads);
+  if (a.tail_last) {
+    if ((long)a.nsplit * a.Hkv * a.B > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    grid = dim3((unsigned)((long)a.nsplit * a.Hkv * a.B), 1, 1);
+  }
   if (FLAT) {
     const long most = (long)a.B * a.Hkv * a.nsplit;  // items when every sequence is as long as the longest
     grid = dim3((unsigned)min(most, (long)kFlatMaxWgs), 1, 1);

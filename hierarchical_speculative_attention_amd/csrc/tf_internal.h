@@ -38,6 +38,7 @@ struct AttnArgs {
   int32_t tpw;              // virtual tokens per workgroup (multiple of 128)
   int32_t nsplit;           // splits of the longest sequence (partial-buffer stride; the 3-D grid's x)
   int32_t rows_pad;         // 16 * query tiles
+  int32_t tail_last;        // the plan ends with a short split per (sequence, head), dispatched after the rest
   float* out;               // [B][Hq][Qn][d]
   float* lse;               // [B][Hq][Qn] or null
   float* part_o;            // [B][Hkv][nsplit][rows_pad][d]
@@ -51,6 +52,7 @@ struct SplitPlan {
   int32_t tpw;
   int32_t nsplit;
   int32_t rows_pad;
+  int32_t tail_last;  // one round of full splits and a short last split per (sequence, head)
   size_t part_o_bytes, part_ml_bytes, total_bytes;
 };
 

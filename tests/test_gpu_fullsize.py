@@ -211,9 +211,9 @@ def test_llama2_7b_128k_sparse_verify_with_tail():
 
 def test_llama2_7b_128k_verify_in_a_larger_allocation():
     # 512 rows allocated past the sequence (the three-tier loop's cache): the
-    # split plan takes two whole rounds of workgroups (32 splits of 4128 rows)
-    # instead of 16 splits of 8192 plus a second round of one; parity on heads
-    # of the first and last XCD groups
+    # split plan takes one round of 16 splits of 8192 rows and a short 17th
+    # split per head, dispatched after all the others (a 1-D grid); parity on
+    # heads of the first and last XCD groups
     Q = 7
     W = synth.WORKLOADS["llama2-7b-128k-1layer"]
     K, V, qv, qd, lay, _ = synth.make_layer_torch(
