@@ -167,9 +167,14 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
 // bytes): on this chip that pattern streams at about 7.0 TB/s, while loading
 // straight into the MFMA operand layout (16 rows x 64 bytes per instruction)
 // tops out near 6.3 TB/s.  The tile is staged in a wave-private LDS slab with
-// a 272-byte row pitch, so both the contiguous writes and the 16-row operand
-// reads are free of bank conflicts.  One tile is in flight while the staged
-// one is consumed.
+// a 288-byte row pitch: consecutive rows start 8 banks apart, so the
+// contiguous writes, the 16-row operand reads and the transposing value reads
+// (8 bytes from each of four consecutive rows per lane group) are all free
+// of bank conflicts (the chip's conflict counter reads 0; a 272-byte pitch
+// left 24% of the kernel's LDS cycles to conflicts at one query tile and 36%
+// at three, GQA verify 1 us slower; 280 bytes breaks the 16-byte alignment of
+// the operand reads: GQA verify 337 -> 593 us).  One tile is in flight while
+// the staged one is consumed.
 //
 // Staged, two deep (sparse: a few gathered tiles per wave, latency-bound).
 // The same 1 KB-per-instruction loads and slab, but two register stages
@@ -183,7 +188,7 @@ __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, i
 // go straight into the MFMA operand layout (lane (t, g): dims 32 s + 8 g ..
 // +8 of token t) and two tiles are in flight at once; staging measured slower
 // here (8.6 -> 8.9 us).
-constexpr int kPitch = 272;                  // LDS bytes per staged 256-byte row
+constexpr int kPitch = 288;                  // LDS bytes per staged 256-byte row
 constexpr int kStageRows = 2 * kTile;        // 32 key rows, then 32 value rows
 constexpr int kStageBytes = kStageRows * kPitch;
 constexpr int kMergeBytes = 4 * 16 * 132 * 4;  // per-query-tile merge buffer (staged: reuses the slabs)
