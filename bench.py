@@ -77,7 +77,7 @@ def read_traffic():
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        if ":" in line:
+        if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("attn_hip_sha256") != sources_sha(VERIFY_SRCS):
