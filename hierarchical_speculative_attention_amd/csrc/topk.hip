@@ -6,29 +6,39 @@
 // owns the contiguous index range [t * IPT, (t + 1) * IPT) and keeps its keys
 // in registers for the whole kernel.  A most-significant-digit-first radix
 // select over LDS histograms finds the exact k-th largest key T and how many
-// keys equal to T must be taken: the first digit is 11 bits wide, the later
-// ones 8, 8 and 5; as soon as the bin holding the k-th largest key has at most
-// 64 keys, those keys are copied to LDS and one wave ranks them directly
-// instead of running the remaining passes.  One block-wide prefix sum in
+// keys equal to T must be taken: the first digit is 14 bits wide (13 for
+// workgroups of fewer than 16 keys per thread), the later ones 8, 8 and the
+// rest; as soon as the bin holding the k-th largest key has at most 64 keys,
+// those keys are copied to LDS and one wave ranks them directly instead of
+// running the remaining passes.  One block-wide prefix sum in
 // thread order then gives each kept item's output slot (all keys > T, then the
 // lowest-index keys == T), so the output is ascending and bit-exact for a
 // given score array.
 //
 // Costs that shaped it (measured on the chip, 32 rows of 16384 chunks,
-// k = 512; kernel time 12.1 -> 10.8 us with the last four changes):
+// k = 512; kernel time 12.1 -> 10.8 us with four changes, then -0.4 us from
+// the 14-bit first digit):
 //  * the score loads are issued unconditionally (index clamped into the row)
 //    and all at once, with the chunk count, before anything waits for them;
 //    the first histogram is cleared meanwhile and the only barrier before the
 //    first pass follows, so each thread counts as soon as its keys arrive;
 //  * real score rows crowd a few top-byte bins and same-address LDS atomics
-//    within one instruction serialise, so each histogram is kept in kSub
-//    copies indexed by lane % kSub, one bin of different copies in different
-//    banks (8 copies beat 4, 16, 32), and the first digit has 2048 bins (kept
-//    in 4 copies: 0.15 us faster than 8), its bin picked by all sixteen waves;
-//  * after 19 bits the k-th key's bin holds a few keys: copying them to LDS
-//    and ranking them in one wave (broadcast LDS reads, no lane shuffles)
-//    replaces the last two passes; ranking a bin of up to 256 keys with the
-//    whole block instead of the second pass measured slower;
+//    within one instruction serialise.  The first digit (sign, exponent and
+//    five mantissa bits) spreads the keys over 16384 bins, one histogram
+//    copy (64 KB), its bin picked by all sixteen waves; the k-th key's bin
+//    then holds a few dozen keys of a real score row, so the one-wave rank
+//    follows the first pass directly.  Measured per launch (32 rows of
+//    16384 / GQA: 8 rows in 8 slices + merge / 256 ragged rows): 11 bits in 4
+//    copies 11.9 / 14.5 / 12.6 us; 14 bits 11.4 / 15.2 / 12.0 (slices of
+//    four keys per thread do not repay clearing and scanning 64 KB); 13 bits
+//    11.6 / 13.8 / 12.2; 15 bits 13.0 (128 KB).  Hence 14 bits at 16 or more
+//    keys per thread, 13 below.  The later 8-bit digits keep kSub copies
+//    indexed by lane % kSub, one bin of different copies in different banks
+//    (8 copies beat 4, 16, 32);
+//  * a bin of at most 64 keys is ranked by one wave after copying its keys
+//    to LDS (broadcast LDS reads, no lane shuffles) in place of the
+//    remaining passes; ranking a bin of up to 256 keys with the whole block
+//    instead of an 8-bit pass measured slower;
 //  * histograms are double-buffered (the next pass's copy is cleared while
 //    this one fills), so a pass needs two barriers; the output prefix sum
 //    needs one; both output counts share it.
@@ -49,18 +59,20 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kSub = 8;            // histogram copies, one per lane % kSub
 constexpr int kHistStride = 257;   // words between copies (different LDS banks for one bin)
 constexpr int kHistWords = kSub * kHistStride;
-// The first digit is 11 bits wide (sign, exponent, two mantissa bits): real
-// score rows crowd a handful of 8-bit top digits, and same-address LDS
-// atomics serialise; 2048 bins spread them.  Later digits: 8, 8 and 5 bits.
-constexpr int kWide = 11;
-constexpr int kWideBins = 1 << kWide;
-constexpr int kWideSub = 4;  // copies of the wide histogram (its 2048 bins already spread the keys; 8 copies
-                             // measured 0.15 us slower, from clearing and summing twice the words)
-constexpr int kWideStride = kWideBins + 1;  // one bin of different copies in different banks
-constexpr int kWideWords = (kWideSub * kWideStride + 3) / 4 * 4;
-static_assert(kWideWords % 4 == 0, "the wide histogram is cleared in 16-byte stores");
+// Width of the first digit: 14 bits (sign, exponent, five mantissa bits) for
+// workgroups of 16 or more keys per thread, 13 below.  Later digits: 8, 8 and
+// the remaining 2 or 3 bits.
+template <int IPT>
+constexpr int wide_bits() { return IPT >= 16 ? 14 : 13; }
+template <int W>
+struct Wide {
+  static_assert(W >= 12 && W <= 15, "first digit of 12-15 bits");
+  static constexpr int kBins = 1 << W;
+  static constexpr int kPerLane = kBins / kTopkThreads;  // bins per thread in the pick (4-32)
+};
 // lowest bit of the digit of pass p (0 .. 3)
-__device__ __forceinline__ constexpr int digit_shift(int p) { return p == 0 ? 32 - kWide : p == 3 ? 0 : 32 - kWide - 8 * p; }
+template <int W>
+__device__ __forceinline__ constexpr int digit_shift(int p) { return p == 0 ? 32 - W : p == 3 ? 0 : 32 - W - 8 * p; }
 #ifndef TF_TOPK_SMALL
 #define TF_TOPK_SMALL kSmall
 #endif
@@ -136,22 +148,30 @@ __device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int widt
   }
 }
 
-// The same choice over the 2048 bins of the first digit, by all sixteen
-// waves: wave w sums bins 2047 - 128 w down to 1920 - 128 w (two per lane,
-// kWideSub copies each) and scans them, the wave totals meet in LDS, and the one
-// lane whose bins hold the krem-th largest key writes the result.  Every
-// thread of the block calls it; it ends with a barrier.
+// The same choice over the 2^W bins of the first digit, by all sixteen waves:
+// thread t reads P = 2^W / 1024 consecutive bins with 16-byte LDS reads (wave
+// 0 lane 0 the highest P), each wave scans its lanes' sums, the wave totals
+// meet in LDS, and the one lane whose bins hold the krem-th largest key writes
+// the result.  Every thread of the block calls it; it ends with a barrier.
+template <int W>
 __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_tot, unsigned* s_prefix, int* s_krem,
                                           int* s_cnt) {
+  constexpr int P = Wide<W>::kPerLane;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b0 = kWideBins - 1 - 128 * w - 2 * lane;  // this lane's bins: b0, then b0 - 1
-  int c0 = 0, c1 = 0;
+  // this lane's bins, ascending: lo .. lo + P - 1 (lane 0 of wave 0 holds the highest)
+  const int lo = Wide<W>::kBins - P * (64 * w + lane + 1);
+  int c[P];
 #pragma unroll
-  for (int x = 0; x < kWideSub; ++x) {
-    c0 += h[x * kWideStride + b0];
-    c1 += h[x * kWideStride + b0 - 1];
+  for (int i = 0; i < P; i += 4) {
+    const int4 t = *(const int4*)(h + lo + i);
+    c[i] = t.x;
+    c[i + 1] = t.y;
+    c[i + 2] = t.z;
+    c[i + 3] = t.w;
   }
-  const int sum = c0 + c1;
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) sum += c[i];
   int incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -168,10 +188,15 @@ __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_to
                    (4 * q + 3 < w ? t.w : 0u));
   }
   if (above < krem && krem <= above + sum) {
-    const bool first = krem <= above + c0;
-    *s_prefix = (unsigned)(first ? b0 : b0 - 1);
-    *s_krem = first ? krem - above : krem - above - c0;
-    *s_cnt = first ? c0 : c1;
+#pragma unroll
+    for (int i = P - 1; i >= 0; --i) {  // highest bin first
+      if (above < krem && krem <= above + c[i]) {
+        *s_prefix = (unsigned)(lo + i);
+        *s_krem = krem - above;
+        *s_cnt = c[i];
+      }
+      above += c[i];
+    }
   }
   __syncthreads();
 }
@@ -217,7 +242,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                              int32_t c_max, const int32_t* __restrict__ n_chunks,
                                                              int32_t k, int32_t* __restrict__ idx,
                                                              uint2* __restrict__ cand, int32_t L) {
-  __shared__ __attribute__((aligned(16))) int s_wide[kWideWords];
+  constexpr int W = wide_bits<IPT>();
+  __shared__ __attribute__((aligned(16))) int s_wide[Wide<W>::kBins];
   __shared__ int s_hist[2][kHistWords];
   __shared__ __attribute__((aligned(16))) unsigned s_warp[2 * kTopkWaves];
   __shared__ __attribute__((aligned(16))) unsigned s_tot[kTopkWaves];
@@ -289,7 +315,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // The first histogram is cleared while the loads are in flight; the
   // barrier after it is the last one before the first pass, so each thread
   // starts counting as soon as its own keys arrive.
-  for (int j = tid; j < kWideWords / 4; j += kTopkThreads) ((uint4*)s_wide)[j] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = tid; j < Wide<W>::kBins / 4; j += kTopkThreads) ((uint4*)s_wide)[j] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const int C = min(max(n_chunks_b, 0), c_max);
 
@@ -320,22 +346,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
   unsigned prefix = 0;
   int krem = k;
-  // First pass: the 11-bit top digit of every key.
+  // First pass: the W-bit top digit of every key.
   {
-    const int sub = (lane & (kWideSub - 1)) * kWideStride;
     for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;  // the next pass's histogram
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      if (key[j] != 0u) atomicAdd(&s_wide[sub + (key[j] >> digit_shift(0))], 1);
+      if (key[j] != 0u) atomicAdd(&s_wide[key[j] >> digit_shift<W>(0)], 1);
     __syncthreads();
-    pick_wide(s_wide, krem, s_tot, &s_prefix, &s_krem, &s_cnt);
+    pick_wide<W>(s_wide, krem, s_tot, &s_prefix, &s_krem, &s_cnt);
     prefix = s_prefix;
     krem = s_krem;
   }
   // Later passes: the next 8 (last: 5) bits of the keys still in the running,
   // then the bin holding the krem-th largest.
   auto radix_pass = [&](const int pass) {
-    const int shift = digit_shift(pass), width = digit_shift(pass - 1) - digit_shift(pass);
+    const int shift = digit_shift<W>(pass), width = digit_shift<W>(pass - 1) - digit_shift<W>(pass);
     int* h = s_hist[(pass - 1) & 1];
     int* hn = s_hist[pass & 1];
     if (pass < 3)
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const unsigned kk = key[j];
-      if (kk != 0u && (kk >> digit_shift(pass - 1)) == prefix) atomicAdd(&h[sub + ((kk >> shift) & ((1u << width) - 1u))], 1);
+      if (kk != 0u && (kk >> digit_shift<W>(pass - 1)) == prefix) atomicAdd(&h[sub + ((kk >> shift) & ((1u << width) - 1u))], 1);
     }
     __syncthreads();
     if (tid < 64) pick_bin(h, prefix, width, krem, &s_prefix, &s_krem, &s_cnt);
@@ -352,12 +377,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     prefix = s_prefix;
     krem = s_krem;
   };
-  // A bin of at most kSmall keys (after 19 bits, real score rows leave one
-  // or a few there): its keys are copied to LDS and ranked by one wave in
-  // place of the remaining passes (each pass costs two block barriers and a
-  // bin pick).
+  // A bin of at most kSmall keys (after the first digit, real score rows
+  // leave a few dozen there): its keys are copied to LDS and ranked by one
+  // wave in place of the remaining passes (each pass costs two block barriers
+  // and a bin pick).
   auto finish_small = [&](const int pass) {
-    const int shift = digit_shift(pass);
+    const int shift = digit_shift<W>(pass);
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const unsigned kk = key[j];
