@@ -16,8 +16,8 @@
 // given score array.
 //
 // Costs that shaped it (measured on the chip, 32 rows of 16384 chunks,
-// k = 512; kernel time 12.1 -> 10.8 us with four changes, then -0.4 us from
-// the 14-bit first digit):
+// k = 512; kernel time 12.1 -> 10.8 us with four changes, then 10.5 us per
+// call with the 14-bit first digit and 9.7 us with the DPP scans):
 //  * the score loads are issued unconditionally (index clamped into the row)
 //    and all at once, with the chunk count, before anything waits for them;
 //    the first histogram is cleared meanwhile and the only barrier before the
@@ -36,9 +36,16 @@
 //    indexed by lane % kSub, one bin of different copies in different banks
 //    (8 copies beat 4, 16, 32);
 //  * a bin of at most 64 keys is ranked by one wave after copying its keys
-//    to LDS (broadcast LDS reads, no lane shuffles) in place of the
-//    remaining passes; ranking a bin of up to 256 keys with the whole block
-//    instead of an 8-bit pass measured slower;
+//    to LDS (broadcast LDS reads, all sixteen issued before any comparison)
+//    in place of the remaining passes; ranking a bin of up to 256 keys with
+//    the whole block instead of an 8-bit pass measured slower;
+//  * wave prefix sums (the bin picks, the copy of the small bin, the output
+//    slots) run on DPP row shifts and row broadcasts: lane shuffles compiled
+//    to six dependent LDS permutes per scan.  With the rank's reads issued
+//    together and the small bin copied through one wave scan and one LDS
+//    atomic per wave (instead of one returning atomic per key slot), 11.4 ->
+//    10.65 us per launch at 32 rows of 16384, 13.7 -> 12.5 us for the GQA
+//    slices + merge;
 //  * histograms are double-buffered (the next pass's copy is cleared while
 //    this one fills), so a pass needs two barriers; the output prefix sum
 //    needs one; both output counts share it.
@@ -51,6 +58,8 @@
 // order, then over the row's 8 k candidates (8 rows of 32768 chunks, k = 512:
 // 22.0 -> 14.1 us per call; 4 or 16 slices: 15.3 and 15.0 us).
 #include "tf_internal.h"
+
+#include <type_traits>
 
 namespace tfk {
 
@@ -86,18 +95,29 @@ __device__ __forceinline__ unsigned order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (modulo 2^32), every lane
+// active: shifts by 1, 2, 4 and 8 lanes within each row of 16, then row 15's
+// and row 31's lane broadcast into the rows after them (DPP row_shr and
+// row_bcast operands; a lane without a source adds 0).  The values stay in
+// registers: lane shuffles compile to six dependent LDS permutes instead.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (unsigned)v;
+}
+
 // Exclusive prefix sum over the 1024 threads in thread order (modulo 2^32).
 // One barrier: each wave publishes its total, then every wave reads all
 // sixteen totals (broadcast reads) and adds those of the waves before it.
 // s_warp is written once per call, so a second call needs its own array.
 __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* s_warp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  unsigned incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const unsigned incl = wave_incl_scan(x);
   if (lane == 63) s_warp[w] = incl;
   __syncthreads();
   unsigned before = 0u;
@@ -128,12 +148,7 @@ __device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int widt
     c[j] = t;
     sum += t;
   }
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = (int)wave_incl_scan((unsigned)sum);
   int above = incl - sum;  // keys in higher digits than this lane's bins
   if (above < krem && krem <= incl) {
 #pragma unroll
@@ -172,12 +187,7 @@ __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_to
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < P; ++i) sum += c[i];
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = (int)wave_incl_scan((unsigned)sum);
   if (lane == 63) s_tot[w] = (unsigned)incl;
   __syncthreads();
   int above = incl - sum;  // keys in higher bins of this wave, then of the waves before it
@@ -211,13 +221,17 @@ __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_to
 constexpr int kSmall = 64;
 __device__ __forceinline__ void rank_small(const unsigned* s_key, int n, int krem, unsigned* s_T, int* s_krem) {
   const int lane = threadIdx.x;
-  const unsigned mine = lane < n ? s_key[lane] : 0u;
+  const unsigned mine = s_key[lane];  // (slots n .. kSmall - 1 hold 0)
+  // all sixteen reads are issued before any comparison (one round trip)
+  uint4 o[kSmall / 4];
+#pragma unroll
+  for (int q = 0; q < kSmall / 4; ++q) o[q] = ((const uint4*)s_key)[q];  // one address for every lane: a broadcast
+  __builtin_amdgcn_sched_barrier(0);
   int gt = 0, eq = 0;
 #pragma unroll
   for (int q = 0; q < kSmall / 4; ++q) {
-    const uint4 o = ((const uint4*)s_key)[q];  // one address for every lane: a broadcast
-    gt += (int)(o.x > mine) + (int)(o.y > mine) + (int)(o.z > mine) + (int)(o.w > mine);
-    eq += (int)(o.x == mine) + (int)(o.y == mine) + (int)(o.z == mine) + (int)(o.w == mine);
+    gt += (int)(o[q].x > mine) + (int)(o[q].y > mine) + (int)(o[q].z > mine) + (int)(o[q].w > mine);
+    eq += (int)(o[q].x == mine) + (int)(o[q].y == mine) + (int)(o[q].z == mine) + (int)(o[q].w == mine);
   }
   if (lane < n && gt < krem && krem <= gt + eq) {
     *s_T = mine;
@@ -383,11 +397,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // and a bin pick).
   auto finish_small = [&](const int pass) {
     const int shift = digit_shift<W>(pass);
+    // this thread's keys in the bin (bit j: key j), their slots from one wave
+    // scan of the counts and one LDS atomic per wave
+    using Mask = typename std::conditional<(IPT > 32), unsigned long long, unsigned>::type;
+    Mask m = 0;
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const unsigned kk = key[j];
-      if (kk != 0u && (kk >> shift) == prefix) s_small[atomicAdd(&s_n, 1)] = kk;
+    for (int j = 0; j < IPT; ++j) m |= (key[j] != 0u && (key[j] >> shift) == prefix) ? ((Mask)1 << j) : (Mask)0;
+    const unsigned cnt = (unsigned)__builtin_popcountll((unsigned long long)m);
+    const unsigned incl = wave_incl_scan(cnt);
+    const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+    unsigned base = 0u;
+    if (total != 0u) {
+      if (lane == 63) base = (unsigned)atomicAdd(&s_n, (int)total);
+      base = (unsigned)__builtin_amdgcn_readlane((int)base, 63);
     }
+    unsigned pos = base + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if ((m >> j) & 1u) s_small[pos++] = key[j];
     __syncthreads();
     if (tid < 64) rank_small(s_small, s_n, krem, &s_prefix, &s_krem);
     __syncthreads();
