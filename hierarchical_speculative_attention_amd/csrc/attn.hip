@@ -131,6 +131,26 @@ __device__ __forceinline__ Geo make_geo(const AttnArgs& a, const SeqDesc& d) {
   return g;
 }
 
+// A value combined over the four 16-lane rows of a wave (lanes l, l ^ 16,
+// l ^ 32, l ^ 48: one column of the MFMA output), first with the row beside
+// it, then with the other half.  v_permlane16_swap / v_permlane32_swap with
+// one register as both operands leave every lane holding its own value and
+// its partner's, so the exchange stays in registers (lane shuffles compile to
+// LDS permutes); the partner pairs and their order match x op shfl_xor(x, 16)
+// then op shfl_xor(x, 32), so the results are the same bits.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Virtual token -> cache row, or -1 when nothing valid lives there.
 template <int MODE>
 __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, int v_end,
@@ -351,8 +371,7 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows4_max(mx);
     const float m_new = fmaxf(m_run[qt], mx);
     // Rescale only when some row's running max moved (rare once it settles).
     if (__ballot(m_new != m_run[qt]) != 0ull) {
@@ -526,8 +545,7 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   // each owning wave's rows are complete for this split
   float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
   float lsum = l_run[0];
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows4_sum(lsum);
   if (owner) {
     if (lg == 0) {
       s_m[w][lq] = m_run[0];
@@ -755,8 +773,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     float lsum = l_run[qt];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = rows4_sum(lsum);
     if (lg == 0) {
       s_m[w][lq] = m_run[qt];
       s_l[w][lq] = lsum;

@@ -107,6 +107,19 @@ hipError_t launch_chunk_keys(const uint16_t* K, const tf_kv_desc& kv, int32_t cs
   return hipGetLastError();
 }
 
+// Sum over each row of 16 lanes, every lane ending with its row's total:
+// rotations of the row by 8, 4, 2 and 1 lanes (DPP row_ror operands, in
+// registers; lane shuffles compile to LDS permutes).  At each step a lane's
+// rotation partner holds the same value as its xor partner would, so the
+// result is the same bits as the xor butterfly.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // a2, 16-bit chunk keys: workgroups of four waves; wave j of the grid scores
 // blocks j, j + (waves in the grid), ... of 16 consecutive chunks (4 KB of
@@ -171,10 +184,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc = fmaf(qs[j], f[j], acc);
-      acc += __shfl_xor(acc, 8, 16);
-      acc += __shfl_xor(acc, 4, 16);
-      acc += __shfl_xor(acc, 2, 16);
-      acc += __shfl_xor(acc, 1, 16);
+      acc = row16_sum(acc);
       dot[i] = acc;
     }
     // lane `part` of key group `grp` writes chunk blk * kScoreBlock + 4 part + grp
@@ -252,10 +262,7 @@ __global__ __launch_bounds__(256) void score_kernel_f32(
       acc = qs[0] * x0[0] + qs[1] * x0[1] + qs[2] * x0[2] + qs[3] * x0[3];
       acc = fmaf(qs[4], x1[0], fmaf(qs[5], x1[1], fmaf(qs[6], x1[2], fmaf(qs[7], x1[3], acc))));
     }
-    acc += __shfl_xor(acc, 8, 16);
-    acc += __shfl_xor(acc, 4, 16);
-    acc += __shfl_xor(acc, 2, 16);
-    acc += __shfl_xor(acc, 1, 16);
+    acc = row16_sum(acc);
     dot[i] = acc;
   }
   if (part < 4) {
