@@ -39,13 +39,14 @@
 //    to LDS (broadcast LDS reads, all sixteen issued before any comparison)
 //    in place of the remaining passes; ranking a bin of up to 256 keys with
 //    the whole block instead of an 8-bit pass measured slower;
-//  * wave prefix sums (the bin picks, the copy of the small bin, the output
-//    slots) run on DPP row shifts and row broadcasts: lane shuffles compiled
-//    to six dependent LDS permutes per scan.  With the rank's reads issued
-//    together and the small bin copied through one wave scan and one LDS
-//    atomic per wave (instead of one returning atomic per key slot), 11.4 ->
-//    10.65 us per launch at 32 rows of 16384, 13.7 -> 12.5 us for the GQA
-//    slices + merge;
+//  * wave prefix sums (the bin picks, the output slots) run on DPP row
+//    shifts and row broadcasts: lane shuffles compiled to six dependent LDS
+//    permutes per scan.  With the rank's reads issued together: 11.4 ->
+//    10.55 us per launch at 32 rows of 16384, 13.7 -> 12.3 us for the GQA
+//    slices + merge.  The small bin is copied with one returning LDS atomic
+//    per key in it: a copy through a per-thread match mask, one wave scan and
+//    one atomic per wave measured 0.1-0.2 us slower (every wave then waits
+//    for an atomic; here only those holding one of the few keys do);
 //  * histograms are double-buffered (the next pass's copy is cleared while
 //    this one fills), so a pass needs two barriers; the output prefix sum
 //    needs one; both output counts share it.
@@ -59,7 +60,6 @@
 // 22.0 -> 14.1 us per call; 4 or 16 slices: 15.3 and 15.0 us).
 #include "tf_internal.h"
 
-#include <type_traits>
 
 namespace tfk {
 
@@ -78,6 +78,15 @@ struct Wide {
   static_assert(W >= 12 && W <= 15, "first digit of 12-15 bits");
   static constexpr int kBins = 1 << W;
   static constexpr int kPerLane = kBins / kTopkThreads;  // bins per thread in the pick (4-32)
+  static constexpr int kShift = W - 10;                   // log2(kPerLane)
+  // LDS word of a bin.  At 16 or more bins per lane, four pad words follow
+  // every kPerLane bins, so the pick's 16-byte reads (lane stride kPerLane + 4
+  // words) fall in distinct banks (without: four-way conflicts); 32 rows of
+  // 16384: 10.58 -> 10.42 us.  At 8 bins per lane the conflict is two-way and
+  // the larger clear costs more (GQA slices 12.4 -> 12.7 us), so no pad.
+  static constexpr int kPad = kPerLane >= 16 ? 4 : 0;
+  static constexpr int kWords = kBins + kPad * kTopkThreads;
+  __device__ static __forceinline__ int word(unsigned bin) { return (int)(bin + (bin >> kShift) * kPad); }
 };
 // lowest bit of the digit of pass p (0 .. 3)
 template <int W>
@@ -165,9 +174,11 @@ __device__ __forceinline__ void pick_bin(const int* h, unsigned prefix, int widt
 
 // The same choice over the 2^W bins of the first digit, by all sixteen waves:
 // thread t reads P = 2^W / 1024 consecutive bins with 16-byte LDS reads (wave
-// 0 lane 0 the highest P), each wave scans its lanes' sums, the wave totals
-// meet in LDS, and the one lane whose bins hold the krem-th largest key writes
-// the result.  Every thread of the block calls it; it ends with a barrier.
+// 0 lane 0 the highest P; at 16 bins per lane the histogram's pad words keep
+// these reads free of bank conflicts), each wave scans its lanes' sums, the
+// wave totals meet in LDS, and the one lane whose bins hold the krem-th
+// largest key writes the result.  Every thread of the block calls it; it ends
+// with a barrier.
 template <int W>
 __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_tot, unsigned* s_prefix, int* s_krem,
                                           int* s_cnt) {
@@ -175,10 +186,11 @@ __device__ __forceinline__ void pick_wide(const int* h, int krem, unsigned* s_to
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // this lane's bins, ascending: lo .. lo + P - 1 (lane 0 of wave 0 holds the highest)
   const int lo = Wide<W>::kBins - P * (64 * w + lane + 1);
+  const int lo_word = Wide<W>::word((unsigned)lo);  // (a lane's bins are contiguous words)
   int c[P];
 #pragma unroll
   for (int i = 0; i < P; i += 4) {
-    const int4 t = *(const int4*)(h + lo + i);
+    const int4 t = *(const int4*)(h + lo_word + i);
     c[i] = t.x;
     c[i + 1] = t.y;
     c[i + 2] = t.z;
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                              int32_t k, int32_t* __restrict__ idx,
                                                              uint2* __restrict__ cand, int32_t L) {
   constexpr int W = wide_bits<IPT>();
-  __shared__ __attribute__((aligned(16))) int s_wide[Wide<W>::kBins];
+  __shared__ __attribute__((aligned(16))) int s_wide[Wide<W>::kWords];
   __shared__ int s_hist[2][kHistWords];
   __shared__ __attribute__((aligned(16))) unsigned s_warp[2 * kTopkWaves];
   __shared__ __attribute__((aligned(16))) unsigned s_tot[kTopkWaves];
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // The first histogram is cleared while the loads are in flight; the
   // barrier after it is the last one before the first pass, so each thread
   // starts counting as soon as its own keys arrive.
-  for (int j = tid; j < Wide<W>::kBins / 4; j += kTopkThreads) ((uint4*)s_wide)[j] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = tid; j < Wide<W>::kWords / 4; j += kTopkThreads) ((uint4*)s_wide)[j] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const int C = min(max(n_chunks_b, 0), c_max);
 
@@ -365,7 +377,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     for (int j = tid; j < kHistWords; j += kTopkThreads) s_hist[0][j] = 0;  // the next pass's histogram
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      if (key[j] != 0u) atomicAdd(&s_wide[key[j] >> digit_shift<W>(0)], 1);
+      if (key[j] != 0u) atomicAdd(&s_wide[Wide<W>::word(key[j] >> digit_shift<W>(0))], 1);
     __syncthreads();
     pick_wide<W>(s_wide, krem, s_tot, &s_prefix, &s_krem, &s_cnt);
     prefix = s_prefix;
@@ -397,24 +409,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // and a bin pick).
   auto finish_small = [&](const int pass) {
     const int shift = digit_shift<W>(pass);
-    // this thread's keys in the bin (bit j: key j), their slots from one wave
-    // scan of the counts and one LDS atomic per wave
-    using Mask = typename std::conditional<(IPT > 32), unsigned long long, unsigned>::type;
-    Mask m = 0;
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) m |= (key[j] != 0u && (key[j] >> shift) == prefix) ? ((Mask)1 << j) : (Mask)0;
-    const unsigned cnt = (unsigned)__builtin_popcountll((unsigned long long)m);
-    const unsigned incl = wave_incl_scan(cnt);
-    const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
-    unsigned base = 0u;
-    if (total != 0u) {
-      if (lane == 63) base = (unsigned)atomicAdd(&s_n, (int)total);
-      base = (unsigned)__builtin_amdgcn_readlane((int)base, 63);
+    for (int j = 0; j < IPT; ++j) {
+      const unsigned kk = key[j];
+      if (kk != 0u && (kk >> shift) == prefix) s_small[atomicAdd(&s_n, 1)] = kk;
     }
-    unsigned pos = base + incl - cnt;
-#pragma unroll
-    for (int j = 0; j < IPT; ++j)
-      if ((m >> j) & 1u) s_small[pos++] = key[j];
     __syncthreads();
     if (tid < 64) rank_small(s_small, s_n, krem, &s_prefix, &s_krem);
     __syncthreads();
