@@ -60,7 +60,6 @@
 // 22.0 -> 14.1 us per call; 4 or 16 slices: 15.3 and 15.0 us).
 #include "tf_internal.h"
 
-
 namespace tfk {
 
 constexpr int kTopkThreads = 1024;
@@ -91,9 +90,6 @@ struct Wide {
 // lowest bit of the digit of pass p (0 .. 3)
 template <int W>
 __device__ __forceinline__ constexpr int digit_shift(int p) { return p == 0 ? 32 - W : p == 3 ? 0 : 32 - W - 8 * p; }
-#ifndef TF_TOPK_SMALL
-#define TF_TOPK_SMALL kSmall
-#endif
 
 // Keys of real scores are >= 0x007FFFFF (the key of -inf), so 0 marks
 // "no item".
@@ -420,15 +416,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     prefix = s_prefix;
     krem = s_krem;
   };
-  if (s_cnt <= TF_TOPK_SMALL) {
+  if (s_cnt <= kSmall) {
     finish_small(0);
   } else {
     radix_pass(1);
-    if (s_cnt <= TF_TOPK_SMALL) {
+    if (s_cnt <= kSmall) {
       finish_small(1);
     } else {
       radix_pass(2);
-      if (s_cnt <= TF_TOPK_SMALL) finish_small(2); else radix_pass(3);
+      if (s_cnt <= kSmall) finish_small(2); else radix_pass(3);
     }
   }
   const unsigned T = prefix;
