@@ -176,7 +176,7 @@ def test_topk_adversarial_rows():
                 assert np.array_equal(idx[0, g], ref), (k, n, g)
 
 
-@pytest.mark.parametrize("C,k", [(16384, 512), (32768, 512), (70000, 3000)])
+@pytest.mark.parametrize("C,k", [(16384, 512), (16448, 512), (32768, 512), (70000, 3000)])
 def test_topk_large_rows(C, k):
     rng = np.random.default_rng(C)
     s = (rng.standard_normal((2, 3, C)) * 5).astype(np.float32)
@@ -187,13 +187,14 @@ def test_topk_large_rows(C, k):
             assert np.array_equal(idx[b, g], oracle.select_topk(s[b, g, :n].astype(np.float64), k))
 
 
-@pytest.mark.parametrize("C", [1500, 3001, 4096, 5003, 16384, 40000, 50001])
+@pytest.mark.parametrize("C", [1500, 3001, 4096, 5003, 16384, 16448, 20001, 24576, 30000, 40000, 50001])
 def test_topk_value_spreads(C):
     """Rows whose k-th key sits in bins of every size: exponents spread so the
-    first 8-bit digit already isolates a small bin, quantised values whose
-    16-bit bins hold exact duplicates, a narrow band that needs all four
-    digits.  Row lengths cover every keys-per-thread instantiation (2 to 64
-    keys per thread) with lengths that are and are not a multiple of 4."""
+    first digit already isolates a small bin, quantised values whose 16-bit
+    bins hold exact duplicates, a narrow band that needs all four digits.
+    Row lengths cover every keys-per-thread instantiation of the one-launch
+    path (2, 4, 8, 16, 20, 24, 32, 48 and 64 keys per thread) with lengths
+    that are and are not a multiple of 4."""
     rng = np.random.default_rng(C + 1)
     rows = [
         np.sign(rng.standard_normal(C)) * np.exp2(rng.uniform(-60, 60, C)),     # spread exponents
