@@ -245,7 +245,7 @@ TF_EXPORT size_t tf_sparse_attn_workspace_size(int32_t B, int32_t Hq, int32_t H,
   if (B < 1 || H < 1 || Hq < 1 || k < 1 || chunk_size < 1) return 0;
   const long virt = (long)k * chunk_size;
   if (virt > 0x7fffffffL) return 0;
-  return tfk::plan_splits(B, H, Hq / H, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw).total_bytes;
+  return tfk::plan_splits(B, H, Hq / H, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw, tfk::kSparseMinTpw).total_bytes;
 }
 
 TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const void* V, const tf_kv_desc* kv,
@@ -264,7 +264,7 @@ TF_EXPORT int tf_sparse_attn(const void* q, int32_t Hq, const void* K, const voi
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, Hq / kv->H, k * chunk_size, kSparseTargetWgs, tfk::kSparseMaxTpw);
+      tfk::plan_splits(kv->B, kv->H, Hq / kv->H, k * chunk_size, kSparseTargetWgs, tfk::kSparseMaxTpw, tfk::kSparseMinTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, 1, out, lse);
@@ -283,7 +283,7 @@ TF_EXPORT size_t tf_sparse_verify_attn_workspace_size(int32_t B, int32_t Hq, int
   if (B < 1 || H < 1 || Hq < 1 || Q < 1 || k < 1 || chunk_size < 1 || tail < 1) return 0;
   const long virt = (long)k * chunk_size + tail;
   if (virt > 0x7fffffffL) return 0;
-  return tfk::plan_splits(B, H, (Hq / H) * Q, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw).total_bytes;
+  return tfk::plan_splits(B, H, (Hq / H) * Q, (int32_t)virt, kSparseTargetWgs, tfk::kSparseMaxTpw, tfk::kSparseMinTpw).total_bytes;
 }
 
 TF_EXPORT int tf_sparse_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
@@ -307,7 +307,7 @@ TF_EXPORT int tf_sparse_verify_attn(const void* q, int32_t Hq, int32_t Q, const 
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan = tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, k * chunk_size + tail,
-                                               kSparseTargetWgs, tfk::kSparseMaxTpw);
+                                               kSparseTargetWgs, tfk::kSparseMaxTpw, tfk::kSparseMinTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
@@ -356,7 +356,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
 // ---------------------------------------------------------------------------
 TF_EXPORT size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len) {
   if (B < 1 || H < 1 || Hq < 1 || Q < 1 || max_len < 0) return 0;
-  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw).total_bytes;
+  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw).total_bytes;
 }
 
 TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
@@ -375,7 +375,7 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
@@ -444,7 +444,7 @@ TF_EXPORT int tf_verify_attn_noalloc(const void* q, int32_t Hq, int32_t Q, const
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
   if (plan.total_bytes > kNoAllocScratchBytes)
     return fail(TF_ERR_WORKSPACE, "this call needs %zu bytes of split partials; the built-in scratch holds %zu "
                 "(use tf_verify_attn with a workspace)", plan.total_bytes, kNoAllocScratchBytes);
@@ -473,7 +473,7 @@ TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const vo
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw);
+      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);

@@ -1010,7 +1010,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
 }
 
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
-                      int32_t max_tpw) {
+                      int32_t max_tpw, int32_t min_tpw) {
   SplitPlan p;
   const long heads = (long)B * Hkv;
   const long per_head = target_wgs / heads;  // splits per (sequence, KV head) that keep the grid within target
@@ -1030,7 +1030,7 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
     const long rounds = ((long)max_virtual + per_head * max_tpw - 1) / (per_head * max_tpw);
     const long n = per_head * max(1L, rounds);
     long fit = ((long)max_virtual + n - 1) / n;
-    fit = max(128L, (fit + kTile - 1) / kTile * kTile);
+    fit = max((long)min_tpw, (fit + kTile - 1) / kTile * kTile);
     if (fit < tpw) tpw = fit;
   }
   p.tpw = (int32_t)tpw;

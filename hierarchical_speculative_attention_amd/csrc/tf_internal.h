@@ -57,14 +57,20 @@ struct SplitPlan {
 };
 
 // Virtual tokens per workgroup: the fewest (a multiple of the tile, at least
-// 128, at most max_tpw) that give the grid a whole number of rounds of
+// min_tpw, at most max_tpw) that give the grid a whole number of rounds of
 // target_wgs workgroups, the number resident at once -- one round when
 // max_tpw allows.  A grid a little past a whole round would leave its last
 // workgroups to start only when the first ones finish.
 constexpr int32_t kVerifyMaxTpw = 8192;
 constexpr int32_t kSparseMaxTpw = 1024;
+// At least 256 gathered tokens (128 KB of K and V) per workgroup: GQA 512K
+// (8 KV heads x 8192 tokens) in 64 splits of 128 took 16.8 us, in 32 of 256
+// 15.2 us (one group of partials to merge), in 16 of 512 18.0 us; the
+// Llama2-7B-128K layer already takes 256 per split.
+constexpr int32_t kVerifyMinTpw = 128;
+constexpr int32_t kSparseMinTpw = 256;
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
-                      int32_t max_tpw);
+                      int32_t max_tpw, int32_t min_tpw);
 
 hipError_t launch_attn(int dtype, int mode, const AttnArgs& a, hipStream_t stream);
 
