@@ -151,6 +151,16 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Maximum over the 64 lanes of a wave, every lane active: each row of 16
+// rotated by 8, 4, 2 and 1 lanes (DPP row_ror), then the four rows combined.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
+  return rows4_max(x);
+}
+
 // Virtual token -> cache row, or -1 when nothing valid lives there.
 template <int MODE>
 __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, int v_end,
@@ -929,17 +939,17 @@ void attn_kernel(const AttnArgs a) {
 // sequence geometry is known: every split index below the planned split count
 // lies inside the workspace, and splits past this sequence's own count are
 // dropped by selection (their contents are never combined arithmetically).
-// Lane s of the wave holds split s's (max, sum); every other lane reads them
-// with readlane (a scalar operand, no LDS round trip: shuffles through LDS
-// made the merge's arithmetic cost more than its loads), and the group's
-// max, weighted sum and accumulators are folded in split order.
-__device__ __forceinline__ float lane_f(float x, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
+// Lane s of the wave holds split s's (max, sum): the group's max is a
+// register reduction, lane s computes split s's weight (one exponential per
+// lane), and the (weight, sum) pairs reach every lane through 16 broadcast LDS
+// reads; the weighted sum and the accumulators are then folded in split
+// order.  (This replaced ~128 readlane broadcasts per group, each followed
+// by hazard waits: bit-identical results, the sparse call 19.92 -> 19.82 us.)
 
 template <int MODE>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   constexpr int kGroup = 32;
+  __shared__ __attribute__((aligned(16))) float2 s_el[kGroup];
   const int row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const float c2 = a.scale_log2;
@@ -977,29 +987,40 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
 
   float Mx = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += kGroup) {
-    if (s0 > 0) load_group(s0, nsp);
+    if (s0 > 0) {
+      __syncthreads();  // (the previous group's reads of s_el are done)
+      load_group(s0, nsp);
+    }
     if (s0 + (lane & (kGroup - 1)) >= nsp) mlv = make_float2(kNegInf, 0.f);
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
       if (s0 + u >= nsp) v[u] = make_float2(0.f, 0.f);
-    float gm = kNegInf;
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, lane_f(mlv.x, u));
+    const float gm = wave_max(mlv.x);  // (lanes 32-63 repeat lanes 0-31)
     const float Mn = fmaxf(Mx, gm);
     if (Mn == kNegInf) continue;  // nothing seen yet
     const float r = (Mx == kNegInf) ? 0.f : fast_exp2((Mx - Mn) * c2);
     const float e = (mlv.x == kNegInf) ? 0.f : fast_exp2((mlv.x - Mn) * c2);
+    // every lane needs every split's (weight, sum): lane s publishes split
+    // s's, and all lanes read them back with broadcast LDS reads
+    if (lane < kGroup) s_el[lane] = make_float2(e, mlv.y);
+    __syncthreads();
+    float2 el[kGroup];
+#pragma unroll
+    for (int q = 0; q < kGroup / 2; ++q) {
+      const float4 t = ((const float4*)s_el)[q];
+      el[2 * q] = make_float2(t.x, t.y);
+      el[2 * q + 1] = make_float2(t.z, t.w);
+    }
     float le = 0.f;
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) le += lane_f(e, u) * lane_f(mlv.y, u);
+    for (int u = 0; u < kGroup; ++u) le += el[u].x * el[u].y;
     Ls = Ls * r + le;
     o0 *= r;
     o1 *= r;
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      const float eu = lane_f(e, u);
-      o0 += eu * v[u].x;
-      o1 += eu * v[u].y;
+      o0 += el[u].x * v[u].x;
+      o1 += el[u].x * v[u].y;
     }
     Mx = Mn;
   }
