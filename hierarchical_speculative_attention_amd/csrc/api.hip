@@ -100,6 +100,14 @@ int check_ws(void* ws, size_t have, size_t need) {
 constexpr int kVerifyTargetWgs = 512;
 constexpr int kSparseTargetWgs = 512;
 
+// Split plan of a verification call (chain or tree): a batch of several
+// sequences takes equal work per workgroup over its tiles, one sequence the
+// split grid.
+static tfk::SplitPlan verify_plan(int32_t B, int32_t H, int32_t rows, int32_t max_len) {
+  if (tfk::flat_eligible(B, H, max_len)) return tfk::plan_flat(B, H, rows, kVerifyTargetWgs);
+  return tfk::plan_splits(B, H, rows, max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
+}
+
 void fill_common(tfk::AttnArgs& a, const void* q, const void* K, const void* V, const tf_kv_desc* kv, int Hq, int Qn,
                  float* out, float* lse) {
   a.q = (const uint16_t*)q;
@@ -135,10 +143,13 @@ void fill_plan(tfk::AttnArgs& a, const tfk::SplitPlan& p, void* ws) {
   a.nsplit = p.nsplit;
   a.rows_pad = p.rows_pad;
   a.tail_last = p.tail_last;
+  a.flat_wgs = p.flat_wgs;
+  a.flat_prefix = nullptr;
   if (p.total_bytes) {
     char* w = (char*)ws;
     a.part_ml = (float*)w;
     a.part_o = (float*)(w + p.part_ml_bytes);
+    if (p.flat_wgs > 0) a.flat_prefix = (int32_t*)(w + p.part_ml_bytes + p.part_o_bytes);
   }
 }
 
@@ -155,8 +166,12 @@ const char* status_name(int status) {
 
 // Launch of an attention call (after its checks passed), logged when TF_LOG is set.
 int attn_call(const char* fn, int dtype, int mode, const tfk::AttnArgs& a, hipStream_t stream) {
-  log_line("%s: B=%d Hq=%d H=%d rows/head=%d max_len=%d tokens/workgroup=%d splits=%d%s", fn, a.B, a.Hq, a.Hkv,
-           a.rows, a.max_len, a.tpw, a.nsplit, a.nsplit > 1 ? " (+ split merge)" : "");
+  if (a.flat_wgs > 0)
+    log_line("%s: B=%d Hq=%d H=%d rows/head=%d max_len=%d equal work on %d workgroups, %d partial slots "
+             "(+ split merge)", fn, a.B, a.Hq, a.Hkv, a.rows, a.max_len, a.flat_wgs, a.nsplit);
+  else
+    log_line("%s: B=%d Hq=%d H=%d rows/head=%d max_len=%d tokens/workgroup=%d splits=%d%s", fn, a.B, a.Hq, a.Hkv,
+             a.rows, a.max_len, a.tpw, a.nsplit, a.nsplit > 1 ? " (+ split merge)" : "");
   return check_hip(tfk::launch_attn(dtype, mode, a, stream), fn);
 }
 
@@ -356,7 +371,7 @@ TF_EXPORT int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const vo
 // ---------------------------------------------------------------------------
 TF_EXPORT size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q, int32_t max_len) {
   if (B < 1 || H < 1 || Hq < 1 || Q < 1 || max_len < 0) return 0;
-  return tfk::plan_splits(B, H, (Hq / H) * Q, max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw).total_bytes;
+  return verify_plan(B, H, (Hq / H) * Q, max_len).total_bytes;
 }
 
 TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
@@ -375,7 +390,7 @@ TF_EXPORT int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
+      verify_plan(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);
@@ -444,7 +459,7 @@ TF_EXPORT int tf_verify_attn_noalloc(const void* q, int32_t Hq, int32_t Q, const
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
+      verify_plan(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len);
   if (plan.total_bytes > kNoAllocScratchBytes)
     return fail(TF_ERR_WORKSPACE, "this call needs %zu bytes of split partials; the built-in scratch holds %zu "
                 "(use tf_verify_attn with a workspace)", plan.total_bytes, kNoAllocScratchBytes);
@@ -473,7 +488,7 @@ TF_EXPORT int tf_verify_tree_attn(const void* q, int32_t Hq, int32_t Q, const vo
   TRY(check_ptr(out, "out", 16));
   if (lse) TRY(check_ptr(lse, "lse", 4));
   const tfk::SplitPlan plan =
-      tfk::plan_splits(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len, kVerifyTargetWgs, tfk::kVerifyMaxTpw, tfk::kVerifyMinTpw);
+      verify_plan(kv->B, kv->H, (Hq / kv->H) * Q, kv->max_len);
   TRY(check_ws(ws, ws_bytes, plan.total_bytes));
   tfk::AttnArgs a;
   fill_common(a, q, K, V, kv, Hq, Q, out, lse);

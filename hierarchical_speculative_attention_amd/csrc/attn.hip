@@ -61,8 +61,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxSparseTpw = kSparseMaxTpw;      // virtual tokens per sparse workgroup (host-capped)
 constexpr int kMaxSparseIdx = kMaxSparseTpw + 2;  // chunk slots one sparse workgroup can touch
-constexpr int kMaxFlatSeqs = 1024;  // ragged verification batches up to this size use the flat grid
-constexpr int kFlatMaxWgs = 2048;   // flat grid: workgroups (each takes every 2048th item)
 
 // Sequence geometry of one (b) for a mode: virtual length and what a
 // virtual token maps to.
@@ -159,6 +157,20 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
   return rows4_max(x);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (modulo 2^32), every lane
+// active: DPP shifts by 1, 2, 4 and 8 lanes within each row of 16, then the
+// last lane of rows 0 and 2, and of row 1, broadcast into the rows after them.
+__device__ __forceinline__ unsigned wave_incl_scan_u32(unsigned x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (unsigned)v;
 }
 
 // Virtual token -> cache row, or -1 when nothing valid lives there.
@@ -446,6 +458,15 @@ __device__ __forceinline__ void process_tile(const Src& src, unsigned mask, int 
   }
 }
 
+// A work item given explicitly (the equal-work plan of a batch's
+// verification): tokens [v0, v1) of one (sequence, KV head); part >= 0 is the
+// partial slot its result goes to, part < 0 means the span is the head's
+// whole range and its result is the output itself.
+struct Span {
+  int v0, v1;
+  long part;
+};
+
 // Verification with 3-4 query tiles, rows split over the waves: wave w < NQT
 // owns query tile w over the item's whole token range and holds the register
 // state of one tile (~180 registers: two waves per SIMD; all tiles in one wave
@@ -462,7 +483,8 @@ constexpr int kRowRing = 4;
 
 template <int DT, int MODE, int NQT>
 __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, const int hk, const int split,
-                                               unsigned char* s_stage, float (*s_m)[16], float (*s_l)[16]) {
+                                               const Span* span, unsigned char* s_stage, float (*s_m)[16],
+                                               float (*s_l)[16]) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
@@ -471,7 +493,7 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   const int lq = lane & 15, lg = lane >> 4;
   const bool owner = w < NQT;  // (with fewer query tiles than waves, the rest would only fetch)
   const int qt = owner ? w : 0;
-  const int v0 = split * a.tpw;
+  const int v0 = span ? span->v0 : split * a.tpw;
   const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
   const int row = qt * 16 + lq;
   V8 qreg[1][4];
@@ -487,9 +509,19 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   const SeqDesc sd = load_seq(a, b);
   const Geo geo = make_geo<MODE>(a, sd);
   const int tbase = geo.n - a.Qn;  // tree: cache row of node 0
-  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
-  if (split >= nsp) return;
-  const int v1 = min(geo.L, v0 + a.tpw);
+  const size_t bh = (size_t)b * a.Hkv + hk;
+  int nsp, v1;
+  long part;  // partial slot (when nsp > 1)
+  if (span) {
+    nsp = span->part < 0 ? 1 : 2;
+    v1 = min(geo.L, span->v1);
+    part = span->part;
+  } else {
+    nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+    if (split >= nsp) return;
+    v1 = min(geo.L, v0 + a.tpw);
+    part = (long)(bh * a.nsplit + split);
+  }
   const size_t base = (size_t)sd.base + (size_t)hk * (size_t)geo.cap * kHeadDim;
   const uint16_t* __restrict__ Kb = a.K + base;
   const uint16_t* __restrict__ Vb = a.V + base;
@@ -565,7 +597,6 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
     for (int bb = 0; bb < 8; ++bb) *(f32x4*)&s_o[w][lq][16 * bb + 4 * lg] = acc[0][bb];
   }
   __syncthreads();
-  const size_t bh = (size_t)b * a.Hkv + hk;
   const int q = tid >> 4;          // 0..15
   const int dc = (tid & 15) * 8;   // 8 dims per thread
 #pragma unroll
@@ -583,7 +614,7 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
         *(f32x4*)(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
         if (a.lse && dc == 0) a.lse[qrow0 + r2] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
       } else {
-        const size_t pr = (bh * a.nsplit + split) * a.rows_pad + r2;
+        const size_t pr = (size_t)part * a.rows_pad + r2;
         float* dst = a.part_o + pr * kHeadDim + dc;
         *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
         *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
@@ -600,14 +631,15 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
 // One work item: split `split` of KV head hk of sequence b, by the whole
 // workgroup (the LDS arrays are the kernel's).
 template <int DT, int MODE, int NQT>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const int hk, const int split, int* s_idx,
-                                          unsigned char* s_stage, float (*s_m)[16], float (*s_l)[16]) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const int hk, const int split,
+                                          const Span* span, int* s_idx, unsigned char* s_stage, float (*s_m)[16],
+                                          float (*s_l)[16]) {
   using M = MT<DT>;
   using V8 = typename M::V8;
   using S = typename M::S;
   constexpr bool kStaged = MODE == kVerify || MODE == kVerifyTree;
   if constexpr (kStaged && NQT >= 3) {
-    attn_item_rows<DT, MODE, NQT>(a, b, hk, split, s_stage, s_m, s_l);
+    attn_item_rows<DT, MODE, NQT>(a, b, hk, split, span, s_stage, s_m, s_l);
     return;
   }
   float (*s_o)[16][132] = reinterpret_cast<float (*)[16][132]>(s_stage);
@@ -615,7 +647,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
-  const int v0 = split * a.tpw;
+  const int v0 = span ? span->v0 : split * a.tpw;
 
   // Loads that need only the arguments (chunk slots, query rows) are issued
   // before the sequence geometry is read, so their round trips overlap it.
@@ -661,9 +693,19 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   const SeqDesc sd = load_seq(a, b);
   const Geo geo = make_geo<MODE>(a, sd);
   const int tbase = geo.n - a.Qn;  // tree: cache row of node 0
-  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
-  if (split >= nsp) return;
-  const int v1 = min(geo.L, v0 + a.tpw);
+  const size_t bh = (size_t)b * a.Hkv + hk;
+  int nsp, v1;
+  long part;  // partial slot (when nsp > 1)
+  if (span) {
+    nsp = span->part < 0 ? 1 : 2;
+    v1 = min(geo.L, span->v1);
+    part = span->part;
+  } else {
+    nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+    if (split >= nsp) return;
+    v1 = min(geo.L, v0 + a.tpw);
+    part = (long)(bh * a.nsplit + split);
+  }
 
   const size_t base = (size_t)sd.base + (size_t)hk * (size_t)geo.cap * kHeadDim;
   const uint16_t* __restrict__ Kb = a.K + base;
@@ -779,7 +821,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   if (kStaged || kStaged2) __syncthreads();  // every slab consumed: the merge reuses them
 
   // ---- merge the four waves (per query tile) -------------------------------
-  const size_t bh = (size_t)b * a.Hkv + hk;
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     float lsum = l_run[qt];
@@ -825,7 +866,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
           *(f32x4*)(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
           if (a.lse && dc == 0) a.lse[qrow0 + row] = Ls > 0.f ? Mx * a.scale_ln + logf(Ls) : kNegInf;
         } else {
-          const size_t pr = (bh * a.nsplit + split) * a.rows_pad + row;
+          const size_t pr = (size_t)part * a.rows_pad + row;
           float* dst = a.part_o + pr * kHeadDim + dc;
           *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
           *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
@@ -840,9 +881,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   }
 }
 
-// Items of a ragged batch: sequence b has Hkv * max(1, ceil(L_b / tpw)) of
-// them (L_b its virtual length), head-major then split; s_pre[b] = the items
-// of sequences 0 .. b-1.  Computed by wave 0 from the device-resident lengths.
+// Tiles of a batch's verification: sequence b has Hkv * ceil(L_b / 32)
+// 32-token tiles (L_b its virtual length), head-major; s_pre[b] = the tiles
+// of sequences 0 .. b-1.  Computed by wave 0 from the device-resident lengths
+// (the host checks that the total fits an int).
 template <int MODE>
 __device__ __forceinline__ void flat_prefix(const AttnArgs& a, int* s_pre) {
   const int lane = threadIdx.x & 63;
@@ -850,26 +892,35 @@ __device__ __forceinline__ void flat_prefix(const AttnArgs& a, int* s_pre) {
   int carry = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
-    int items = 0;
+    int tiles = 0;
     if (b < a.B) {
       SeqDesc sd;
       sd.base = 0;
       sd.cap = a.seq_cap[b];
       sd.len = a.seq_len[b];
       const Geo g = make_geo<MODE>(a, sd);
-      items = a.Hkv * max(1, (g.L + a.tpw - 1) / a.tpw);
+      tiles = a.Hkv * ((g.L + kTile - 1) / kTile);
     }
-    int incl = items;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int incl = (int)wave_incl_scan_u32((unsigned)tiles);
     if (b < a.B) s_pre[b + 1] = carry + incl;
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
   if (lane == 0) s_pre[0] = 0;
 }
+
+// Equal work per workgroup: of a batch's TT tiles (in sequence, head, tile
+// order) workgroup g of G = min(grid, TT) takes tiles [floor(g TT / G),
+// floor((g + 1) TT / G)), at least one each (the rest of the grid idles),
+// so all G finish together whatever the lengths (items of one split size
+// filled 3.7 rounds of the 512 resident workgroups on the 8-sequence batch,
+// the last one 69% full).  The workgroup holding tile x is
+// floor(((x + 1) G - 1) / TT).  A workgroup's range crosses (sequence, head)
+// segments; its part of segment s is written to partial slot g + s (unique:
+// along the tile order each cut advances g, s or both), so a segment's parts
+// are consecutive slots, merged in order by combine_kernel; a segment inside
+// one workgroup is written as output directly.
+__device__ __forceinline__ long flat_wg_of(long x, long TT, long G) { return ((x + 1) * G - 1) / TT; }
+
 
 // One query tile fits two waves per SIMD (<= 256 registers, no spills);
 // more query tiles run one wave per SIMD.  Either one work item per
@@ -899,16 +950,31 @@ void attn_kernel(const AttnArgs a) {
   if (FLAT) {
     flat_prefix<MODE>(a, s_pre);
     __syncthreads();
-    const int total = s_pre[a.B];
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-      int lo = 0, hi = a.B;  // the sequence: largest b with s_pre[b] <= item
+    if (blockIdx.x == 0)  // for the merge kernel
+      for (int j = threadIdx.x; j <= a.B; j += kThreads) a.flat_prefix[j] = s_pre[j];
+    // (G <= TT: with more workgroups than tiles some would get none, and the
+    // merge's consecutive slots would skip theirs)
+    const long TT = s_pre[a.B], G = min((long)gridDim.x, TT);
+    long x = (long)blockIdx.x * TT / max(G, 1L);
+    const long xe = blockIdx.x < G ? ((long)blockIdx.x + 1) * TT / G : x;
+    while (x < xe) {
+      int lo = 0, hi = a.B;  // the sequence: largest b with s_pre[b] <= x (its tiles are not empty)
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_pre[mid] <= item) lo = mid; else hi = mid;
+        if (s_pre[mid] <= x) lo = mid; else hi = mid;
       }
-      const int per = (s_pre[lo + 1] - s_pre[lo]) / a.Hkv;  // splits of sequence lo
-      const int r = item - s_pre[lo];
-      attn_item<DT, MODE, NQT>(a, lo, r / per, r % per, s_idx, s_stage, s_m, s_l);
+      const long T = (s_pre[lo + 1] - s_pre[lo]) / a.Hkv;  // tiles per head of sequence lo
+      const long rel = x - s_pre[lo];
+      const int hk = (int)(rel / T);
+      const long seg0 = s_pre[lo] + (long)hk * T, seg1 = seg0 + T;
+      const long x1 = min(xe, seg1);
+      Span sp;
+      sp.v0 = (int)((x - seg0) * kTile);
+      sp.v1 = (int)((x1 - seg0) * kTile);
+      sp.part = flat_wg_of(seg0, TT, G) == flat_wg_of(seg1 - 1, TT, G) ? -1L
+                                                                           : (long)blockIdx.x + (long)lo * a.Hkv + hk;
+      attn_item<DT, MODE, NQT>(a, lo, hk, 0, &sp, s_idx, s_stage, s_m, s_l);
+      x = x1;
     }
   } else {
     // One item per workgroup: grid (splits, KV heads, sequences), or, when
@@ -922,9 +988,9 @@ void attn_kernel(const AttnArgs a) {
       const int L = blockIdx.x;
       const int split = L < full * heads ? L % full : full;
       const int head = L < full * heads ? L / full : L - full * heads;
-      attn_item<DT, MODE, NQT>(a, head / a.Hkv, head % a.Hkv, split, s_idx, s_stage, s_m, s_l);
+      attn_item<DT, MODE, NQT>(a, head / a.Hkv, head % a.Hkv, split, nullptr, s_idx, s_stage, s_m, s_l);
     } else {
-      attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, s_idx, s_stage, s_m, s_l);
+      attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, nullptr, s_idx, s_stage, s_m, s_l);
     }
   }
 }
@@ -946,7 +1012,7 @@ void attn_kernel(const AttnArgs a) {
 // order.  (This replaced ~128 readlane broadcasts per group, each followed
 // by hazard waits: bit-identical results, the sparse call 19.92 -> 19.82 us.)
 
-template <int MODE>
+template <int MODE, bool FLAT>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   constexpr int kGroup = 32;
   __shared__ __attribute__((aligned(16))) float2 s_el[kGroup];
@@ -954,12 +1020,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
   const int lane = threadIdx.x;
   const float c2 = a.scale_log2;
   const size_t bh = (size_t)b * a.Hkv + hk;
-  const size_t pbase = bh * a.nsplit * a.rows_pad + row;
   const float2* ml = (const float2*)a.part_ml;
-  SeqDesc sd;
-  sd.base = 0;  // not used by the geometry
-  sd.cap = a.seq_cap[b];
-  sd.len = a.seq_len[b];
+  size_t pbase = bh * a.nsplit * a.rows_pad + row;  // (the equal-work plan sets it below)
 
   float2 mlv;
   float2 v[kGroup];
@@ -972,18 +1034,42 @@ __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
     for (int u = 0; u < kGroup; ++u)
       v[u] = *(const float2*)(a.part_o + (pbase + (size_t)min(s0 + u, bound - 1) * a.rows_pad) * kHeadDim + 2 * lane);
   };
-  load_group(0, a.nsplit);
-  // Every load above is consumed here, before the geometry decides whether
-  // this row merges at all: otherwise the compiler sinks the group's loads
-  // past that branch and the descriptor read and the group become two
-  // serial round trips instead of one.
-  asm volatile("" : : "v"(sd.cap), "v"(sd.len), "v"(mlv.x), "v"(mlv.y));
+  int nsp;
+  if constexpr (FLAT) {
+    // the segment's parts: consecutive slots from (its first workgroup) + s,
+    // located from the tile prefix the attention kernel stored
+    if (row >= a.rows) return;
+    const long p0 = a.flat_prefix[b], p1 = a.flat_prefix[b + 1], TT = a.flat_prefix[a.B];
+    const long T = (p1 - p0) / a.Hkv;
+    if (T == 0) {  // no rows: nothing attended
+      const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
+      *(float2*)(a.out + (qrow0 + row) * kHeadDim + 2 * lane) = make_float2(0.f, 0.f);
+      if (a.lse && lane == 0) a.lse[qrow0 + row] = kNegInf;
+      return;
+    }
+    const long seg0 = p0 + (long)hk * T, G = min((long)a.flat_wgs, TT);
+    const long g0 = flat_wg_of(seg0, TT, G);
+    nsp = (int)(flat_wg_of(seg0 + T - 1, TT, G) - g0 + 1);
+    if (nsp == 1) return;  // written directly by the attention kernel
+    pbase = (size_t)(g0 + (long)bh) * a.rows_pad + row;
+    load_group(0, nsp);
+  } else {
+    SeqDesc sd;
+    sd.base = 0;  // not used by the geometry
+    sd.cap = a.seq_cap[b];
+    sd.len = a.seq_len[b];
+    load_group(0, a.nsplit);
+    // Every load above is consumed here, before the geometry decides whether
+    // this row merges at all: otherwise the compiler sinks the group's loads
+    // past that branch and the descriptor read and the group become two
+    // serial round trips instead of one.
+    asm volatile("" : : "v"(sd.cap), "v"(sd.len), "v"(mlv.x), "v"(mlv.y));
 #pragma unroll
-  for (int u = 0; u < kGroup; ++u) asm volatile("" : : "v"(v[u].x), "v"(v[u].y));
-
-  const Geo geo = make_geo<MODE>(a, sd);
-  const int nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
-  if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
+    for (int u = 0; u < kGroup; ++u) asm volatile("" : : "v"(v[u].x), "v"(v[u].y));
+    const Geo geo = make_geo<MODE>(a, sd);
+    nsp = max(1, (geo.L + a.tpw - 1) / a.tpw);
+    if (nsp == 1 || row >= a.rows) return;  // written directly by the attention kernel
+  }
 
   float Mx = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += kGroup) {
@@ -1054,6 +1140,8 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
     fit = max((long)min_tpw, (fit + kTile - 1) / kTile * kTile);
     if (fit < tpw) tpw = fit;
   }
+  p.flat_wgs = 0;
+  p.flat_prefix_bytes = 0;
   p.tpw = (int32_t)tpw;
   p.nsplit = (int32_t)(((long)max_virtual + tpw - 1) / tpw);
   if (p.nsplit < 1) p.nsplit = 1;
@@ -1069,6 +1157,26 @@ SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual,
   return p;
 }
 
+bool flat_eligible(int32_t B, int32_t Hkv, int32_t max_len) {
+  const long tiles = (long)B * Hkv * (((long)max_len + kTile - 1) / kTile);
+  return B > 1 && B <= kMaxFlatSeqs && tiles < 0x7fffffffL;
+}
+
+SplitPlan plan_flat(int32_t B, int32_t Hkv, int32_t rows, int32_t G) {
+  SplitPlan p;
+  p.tail_last = 0;
+  p.flat_wgs = G;
+  p.tpw = 0;  // (spans come from the tile ranges)
+  p.nsplit = G + B * Hkv;
+  p.rows_pad = ((rows + 15) / 16) * 16;
+  const size_t parts = (size_t)p.nsplit * p.rows_pad;
+  p.part_ml_bytes = (parts * 2 * sizeof(float) + 255) & ~(size_t)255;
+  p.part_o_bytes = parts * kHeadDim * sizeof(float);
+  p.flat_prefix_bytes = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  p.total_bytes = p.part_ml_bytes + p.part_o_bytes + p.flat_prefix_bytes;
+  return p;
+}
+
 template <int DT, int MODE, bool FLAT>
 static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.Hkv, a.B), block(kThreads);
@@ -1076,10 +1184,7 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
     if ((long)a.nsplit * a.Hkv * a.B > 0x7fffffffL) return hipErrorInvalidConfiguration;
     grid = dim3((unsigned)((long)a.nsplit * a.Hkv * a.B), 1, 1);
   }
-  if (FLAT) {
-    const long most = (long)a.B * a.Hkv * a.nsplit;  // items when every sequence is as long as the longest
-    grid = dim3((unsigned)min(most, (long)kFlatMaxWgs), 1, 1);
-  }
+  if (FLAT) grid = dim3((unsigned)a.flat_wgs, 1, 1);
   const int nqt = (a.rows + 15) / 16;
   switch (nqt) {
     case 1: hipLaunchKernelGGL((attn_kernel<DT, MODE, 1, FLAT>), grid, block, 0, stream, a); break;
@@ -1089,17 +1194,17 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<MODE>), dim3(a.rows, a.Hkv, a.B), dim3(64), 0, stream, a);
+  if (e != hipSuccess || (!FLAT && a.nsplit == 1)) return e;
+  hipLaunchKernelGGL((combine_kernel<MODE, FLAT>), dim3(a.rows, a.Hkv, a.B), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
-// Verification of a ragged batch takes the flat grid; everything else one
-// item per workgroup.
+// Verification of a batch takes the equal-work grid when its plan says so;
+// everything else one item per workgroup.
 template <int DT, int MODE>
 static hipError_t launch_nqt(const AttnArgs& a, hipStream_t stream) {
   if constexpr (MODE == kVerify || MODE == kVerifyTree) {
-    if (a.B > 1 && a.B <= kMaxFlatSeqs) return launch_tiles<DT, MODE, true>(a, stream);
+    if (a.flat_wgs > 0) return launch_tiles<DT, MODE, true>(a, stream);
   }
   return launch_tiles<DT, MODE, false>(a, stream);
 }

@@ -39,6 +39,8 @@ struct AttnArgs {
   int32_t nsplit;           // splits of the longest sequence (partial-buffer stride; the 3-D grid's x)
   int32_t rows_pad;         // 16 * query tiles
   int32_t tail_last;        // the plan ends with a short split per (sequence, head), dispatched after the rest
+  int32_t flat_wgs;         // > 0: a batch's verification with equal work per workgroup, on this many
+  int32_t* flat_prefix;     // [B + 1] tiles before each sequence, stored by the attention kernel for the merge
   float* out;               // [B][Hq][Qn][d]
   float* lse;               // [B][Hq][Qn] or null
   float* part_o;            // [B][Hkv][nsplit][rows_pad][d]
@@ -53,7 +55,8 @@ struct SplitPlan {
   int32_t nsplit;
   int32_t rows_pad;
   int32_t tail_last;  // one round of full splits and a short last split per (sequence, head)
-  size_t part_o_bytes, part_ml_bytes, total_bytes;
+  int32_t flat_wgs;   // > 0: equal work per workgroup over a batch's tiles (nsplit = partial slots)
+  size_t part_o_bytes, part_ml_bytes, flat_prefix_bytes, total_bytes;
 };
 
 // Virtual tokens per workgroup: the fewest (a multiple of the tile, at least
@@ -71,6 +74,12 @@ constexpr int32_t kVerifyMinTpw = 128;
 constexpr int32_t kSparseMinTpw = 256;
 SplitPlan plan_splits(int32_t B, int32_t Hkv, int32_t rows, int32_t max_virtual, int32_t target_wgs,
                       int32_t max_tpw, int32_t min_tpw);
+// Verification of a batch of 2 .. kMaxFlatSeqs sequences whose tiles
+// (B * Hkv * ceil(max_len / 32)) fit an int: every one of G workgroups takes
+// an equal share of the batch's tiles, with G + B * Hkv partial slots.
+constexpr int kMaxFlatSeqs = 1024;
+bool flat_eligible(int32_t B, int32_t Hkv, int32_t max_len);
+SplitPlan plan_flat(int32_t B, int32_t Hkv, int32_t rows, int32_t G);
 
 hipError_t launch_attn(int dtype, int mode, const AttnArgs& a, hipStream_t stream);
 

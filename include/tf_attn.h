@@ -34,7 +34,8 @@
  *    implies (seq_base[b] and seq_cap[b] * d) a multiple of 8 elements.
  *  - Calls that share one workspace must not overlap in time (same stream or
  *    explicitly ordered).  A workspace needs no initialisation: it only holds
- *    per-split partial results that each call writes before reading.
+ *    per-split partial results (and, for the verification of a batch, each
+ *    sequence's tile count) that each call writes before reading.
  *  - Caches must hold finite values.
  *  - With TF_LOG set to anything but "0" in the environment, every rejected
  *    call prints its status and detail, and every attention call its launch
@@ -204,7 +205,11 @@ int tf_stream_attn(const void* q, int32_t Hq, const void* Ks, const void* Vs,
  * (a row that sees nothing gets out = 0, lse = -inf).
  *   q  : device [B][Hq][Q][d] in kv->dtype.  out: device fp32 [B][Hq][Q][d].
  *   lse: device fp32 [B][Hq][Q] or NULL.     G * Q <= 64.
- *   ws : tf_verify_attn_workspace_size(kv->B, Hq, kv->H, Q, kv->max_len) bytes.
+ *   ws : tf_verify_attn_workspace_size(kv->B, Hq, kv->H, Q, kv->max_len) bytes
+ *        (for a batch of 2 to 1024 sequences: (512 + B * H) partial slots of
+ *        the query rows, whatever max_len, work being shared equally by 512
+ *        workgroups; for one sequence: its splits' partials, which grow with
+ *        max_len).
  */
 int tf_verify_attn(const void* q, int32_t Hq, int32_t Q, const void* K, const void* V,
                    const tf_kv_desc* kv, float* out, float* lse,
@@ -219,8 +224,9 @@ size_t tf_verify_attn_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t Q
  * go to a scratch array built into the library: every GPU the library runs
  * on holds tf_verify_attn_noalloc_max_bytes() = 48 MiB of it until the process
  * ends, and a call whose partials need more (tf_verify_attn_workspace_size
- * above that; e.g. 8 sequences of 128K rows and G * Q = 36) is refused with
- * TF_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing.
+ * above that; e.g. one sequence of 32 KV heads, G * Q = 7 and room for 4M
+ * rows) is refused with TF_ERR_WORKSPACE before anything is enqueued.  The
+ * call allocates nothing.
  * The scratch is shared by every call on that GPU: calls that overlap on one
  * GPU (other streams, other host threads) race and must be serialised by
  * the caller.  stream must belong to the current device (TF_ERR_INVALID_ARG

@@ -247,8 +247,8 @@ def test_verify_noalloc_validates_before_any_device_call():
     L = T.lib()
     cap = L.tf_verify_attn_noalloc_max_bytes()
     assert cap == 48 << 20
-    big = desc(B=8, H=32, max_len=1 << 20)
-    assert T.lib().tf_verify_attn_workspace_size(8, 32, 32, 7, 1 << 20) > cap
+    big = desc(B=1, H=32, max_len=1 << 22)  # 512 splits per head
+    assert T.lib().tf_verify_attn_workspace_size(1, 32, 32, 7, 1 << 22) > cap
     st = L.tf_verify_attn_noalloc(FAKE, 32, 7, FAKE, FAKE, ctypes.byref(big), FAKE, None, None)
     assert st == T.TF_ERR_WORKSPACE
     assert b"scratch" in L.tf_last_error_detail()

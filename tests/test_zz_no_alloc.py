@@ -49,14 +49,14 @@ def test_noalloc_matches_oracle_small():
 def test_noalloc_refuses_a_call_beyond_the_scratch():
     cap = tf.verify_attn_noalloc_max_bytes()
     assert cap == 48 << 20
-    lens = [1 << 20] * 2
-    need = tf.verify_attn_workspace_size(2, 32, 32, 7, lens[0])
+    max_len = 1 << 22   # one sequence: 512 splits per head
+    need = tf.verify_attn_workspace_size(1, 32, 32, 7, max_len)
     assert need > cap
-    lay = synth.KVLayout.build([64, 64], 32, 128, caps=[64, 64])   # small buffers; max_len sizes the plan
-    kv = desc(lay, "bf16", max_len=lens[0])
-    q = torch.zeros((2, 32, 7, 128), dtype=torch.bfloat16, device="cuda")
+    lay = synth.KVLayout.build([64], 32, 128, caps=[64])   # small buffers; max_len sizes the plan
+    kv = desc(lay, "bf16", max_len=max_len)
+    q = torch.zeros((1, 32, 7, 128), dtype=torch.bfloat16, device="cuda")
     K = torch.zeros(lay.total_elems, dtype=torch.bfloat16, device="cuda")
-    out = torch.zeros((2, 32, 7, 128), dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, 32, 7, 128), dtype=torch.float32, device="cuda")
     with pytest.raises(tf.TfError) as e:
         tf.verify_attn_noalloc(q, K, K, kv, out)
     assert e.value.status == tf.TF_ERR_WORKSPACE
