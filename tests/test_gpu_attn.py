@@ -44,6 +44,22 @@ def test_verify_ragged_gqa_short_sequences(dtype):
     compare_attn(out, lse, *oracle_verify(inp, 5))
 
 
+def test_verify_batch_equal_work_segments():
+    """A batch's verification shares its tiles equally over the workgroups:
+    64 short sequences (some empty) over 4 KV heads put several whole
+    (sequence, head) segments inside one workgroup (written directly), split
+    others over two or three (merged from consecutive partial slots), and
+    leave empty ones to the merge (0 and -inf)."""
+    rng = np.random.default_rng(70)
+    lens = [int(x) for x in rng.integers(0, 3000, 64)]
+    for i in (3, 17, 40, 63):
+        lens[i] = 0
+    print(f"batch verify: B=64 Hq=8 Hkv=4 Q=5 lens[:8]={lens[:8]}", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=8, Hkv=4, dtype="bf16", Q=5, seed=70, cap_extra=9)
+    out, lse = run_verify(inp, 5)
+    compare_attn(out, lse, *oracle_verify(inp, 5))
+
+
 @pytest.mark.parametrize("Hq,Hkv,Q,n", [(32, 8, 9, 2000), (16, 2, 8, 777), (4, 4, 1, 5000), (6, 3, 7, 129)])
 def test_verify_query_tiles(Hq, Hkv, Q, n):
     # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14
