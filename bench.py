@@ -91,11 +91,12 @@ def read_traffic():
 TRACE_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama2-7b-128k_kernel_trace.txt")
 
 
-def read_kernel_trace(verify_bytes):
+def read_kernel_trace(verify_bytes, sparse_bytes=None):
     """Each verify kernel's own average duration from the committed rocprofv3
     kernel-trace summary (if it was taken on the current kernel source), and
     the fractions of the HBM peak they give: the attention kernel alone, and
-    the attention kernel plus the split merge."""
+    the attention kernel plus the split merge; with sparse_bytes, the same for
+    the gathered sparse pass (its own key lines) under "sparse"."""
     if not os.path.exists(TRACE_FILE):
         return None
     kv = {}
@@ -109,10 +110,19 @@ def read_kernel_trace(verify_bytes):
         a, m = float(kv["attention_kernel_avg_us"]), float(kv["split_merge_kernel_avg_us"])
     except (KeyError, ValueError):
         return None
-    return {"attention_kernel_us": a, "split_merge_kernel_us": m,
-            "frac_attention_kernel": round(verify_bytes / (a * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "frac_both_kernels": round(verify_bytes / ((a + m) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "source": os.path.relpath(TRACE_FILE, ROOT)}
+    out = {"attention_kernel_us": a, "split_merge_kernel_us": m,
+           "frac_attention_kernel": round(verify_bytes / (a * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "frac_both_kernels": round(verify_bytes / ((a + m) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "source": os.path.relpath(TRACE_FILE, ROOT)}
+    if sparse_bytes is not None and "sparse_kernel_avg_us" in kv:
+        try:
+            g, sm = float(kv["sparse_kernel_avg_us"]), float(kv["sparse_split_merge_kernel_avg_us"])
+        except (KeyError, ValueError):
+            return out
+        out["sparse"] = {"gather_kernel_us": g, "split_merge_kernel_us": sm,
+                         "frac_gather_kernel": round(sparse_bytes / (g * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "frac_both_kernels": round(sparse_bytes / ((g + sm) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return out
 
 
 class Layer:
@@ -470,7 +480,11 @@ def main():
     default_shape = args.workload == DEFAULT_WORKLOAD and gamma == W["gamma"] and budget == W["budget"]
     # (the counters and the kernel trace are of the verify launch at the default workload's shape)
     traffic = read_traffic() if default_shape else None
-    trace = read_kernel_trace(verify_bytes) if default_shape else None
+    trace = read_kernel_trace(verify_bytes, by["sparse"]) if default_shape else None
+    if trace and "sparse" in trace:
+        # the sparse pass: the call level above (gather kernel + split merge, timed
+        # together), each kernel's own traced duration here
+        kernels["sparse"]["kernel_trace"] = trace.pop("sparse")
     ms_per_step = elapsed / args.steps * 1e3
 
     result = {
