@@ -60,6 +60,20 @@ def test_verify_batch_equal_work_segments():
     compare_attn(out, lse, *oracle_verify(inp, 5))
 
 
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_verify_batch_at_the_equal_work_limit(B):
+    """1024 sequences is the largest batch the equal-work grid takes (its tile
+    prefix, built 64 sequences per pass, fills the workgroup's table); 1025
+    go back to one workgroup per (sequence, head) split."""
+    rng = np.random.default_rng(71)
+    lens = [int(x) for x in rng.integers(0, 90, B)]
+    lens[0], lens[B - 1] = 0, 89
+    print(f"batch verify: B={B} Hq=4 Hkv=2 Q=3", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=4, Hkv=2, dtype="bf16", Q=3, seed=71, cap_extra=4)
+    out, lse = run_verify(inp, 3)
+    compare_attn(out, lse, *oracle_verify(inp, 3))
+
+
 @pytest.mark.parametrize("Hq,Hkv,Q,n", [(32, 8, 9, 2000), (16, 2, 8, 777), (4, 4, 1, 5000), (6, 3, 7, 129)])
 def test_verify_query_tiles(Hq, Hkv, Q, n):
     # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14
