@@ -173,22 +173,41 @@ __device__ __forceinline__ unsigned wave_incl_scan_u32(unsigned x) {
   return (unsigned)v;
 }
 
-// Virtual token -> cache row, or -1 when nothing valid lives there.
+// Sparse modes: virtual token v -> cache row, given the chunk index c held by
+// v's slot (v / cs), or -1 when nothing valid lives there.  Written without
+// branches (every value computed, the invalid ones dropped by selection), so
+// that the rows of a tile are mapped together: with a branch per row, each
+// row's slot read became a round trip of its own, nine in a row before a
+// tile's loads could be issued.  Unsigned arithmetic: v >= 0, and a slot
+// holding anything (padding, an index out of range) cannot overflow.
+template <int MODE>
+__device__ __forceinline__ int sparse_row(const AttnArgs& a, const Geo& g, int v, int v_end, int c) {
+  const unsigned cs = (unsigned)a.cs;
+  const unsigned slot = (unsigned)v / cs;
+  const int row = (int)((unsigned)c * cs + ((unsigned)v - slot * cs));
+  // padding or an index out of range reads nothing; with a tail, chunk rows
+  // from the tail on are attended as tail rows
+  int r = (v < v_end && c >= 0 && c < g.nchunks && row < (MODE == kSparseTail ? g.lo : g.n)) ? row : -1;
+  if (MODE == kSparseTail) {
+    const int kcs = a.k * a.cs;
+    if (v >= kcs) r = v < v_end ? g.lo + (v - kcs) : -1;  // tail row (< n since v < L)
+  }
+  return r;
+}
+
+// Virtual token -> cache row, or -1 when nothing valid lives there.  A sparse
+// row's slot is read from the workgroup's slot table, clamped into it: for a
+// token inside the workgroup's range it is a slot the workgroup fetched, and
+// any other token's row is dropped.
 template <int MODE>
 __device__ __forceinline__ int map_row(const AttnArgs& a, const Geo& g, int v, int v_end,
                                        const int* s_idx, int chunk_lo) {
+  if (MODE == kSparse || MODE == kSparseTail) {
+    const unsigned slot = (unsigned)v / (unsigned)a.cs;
+    return sparse_row<MODE>(a, g, v, v_end, s_idx[min(slot - (unsigned)chunk_lo, (unsigned)(kMaxSparseIdx - 1))]);
+  }
   if (v >= v_end) return -1;
   if (MODE == kVerify || MODE == kVerifyTree) return v;
-  if (MODE == kSparse || MODE == kSparseTail) {
-    const int kcs = a.k * a.cs;
-    if (MODE == kSparseTail && v >= kcs) return g.lo + (v - kcs);  // tail row (< n since v < L)
-    int slot = v / a.cs;
-    const int c = s_idx[slot - chunk_lo];
-    if (c < 0 || c >= g.nchunks) return -1;  // padding or out of range: nothing read
-    const int row = c * a.cs + (v - slot * a.cs);
-    // with a tail, chunk rows from the tail on are attended as tail rows
-    return row < (MODE == kSparseTail ? g.lo : g.n) ? row : -1;
-  }
   // stream
   int slot;
   if (v < g.s_eff) {
@@ -241,23 +260,50 @@ struct Stage {
   unsigned mask;   // bit j: token j of the tile is a valid row
 };
 
-template <int MODE>
-__device__ __forceinline__ void load_stage(Stage& st, const AttnArgs& a, const Geo& geo, int t0, int v1,
-                                           const int* s_idx, int chunk_lo, const uint16_t* Kb,
-                                           const uint16_t* Vb, int lane) {
-  const int rv = map_row<MODE>(a, geo, t0 + (lane & 31), v1, s_idx, chunk_lo);
+// The 16 loads of staged tile t0; rowmap(v, i) gives the cache row of
+// virtual token v, for row group i = 0..7 of the lane, or 8 for its
+// token-mask row.
+template <class RowMap>
+__device__ __forceinline__ void load_stage_rows(Stage& st, int t0, const RowMap& rowmap, const uint16_t* Kb,
+                                                const uint16_t* Vb, int lane) {
+  const int rv = rowmap(t0 + (lane & 31), 8);
   st.mask = (unsigned)(__ballot(rv >= 0) & 0xFFFFFFFFull);
   size_t off[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     // Rows that hold nothing read row 0 (in bounds) and are masked later.
-    const int r = map_row<MODE>(a, geo, t0 + 4 * i + (lane >> 4), v1, s_idx, chunk_lo);
+    const int r = rowmap(t0 + 4 * i + (lane >> 4), i);
     off[i] = (size_t)(r < 0 ? 0 : r) * kHeadDim + 8 * (lane & 15);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.v[i] = __builtin_nontemporal_load((const u32x4*)(Kb + off[i]));
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.v[8 + i] = __builtin_nontemporal_load((const u32x4*)(Vb + off[i]));
+}
+
+template <int MODE>
+__device__ __forceinline__ void load_stage(Stage& st, const AttnArgs& a, const Geo& geo, int t0, int v1,
+                                           const int* s_idx, int chunk_lo, const uint16_t* Kb,
+                                           const uint16_t* Vb, int lane) {
+  load_stage_rows(st, t0, [&](int v, int) { return map_row<MODE>(a, geo, v, v1, s_idx, chunk_lo); }, Kb, Vb, lane);
+}
+
+// The chunk indices one lane needs for staged tile t0 of a sparse workgroup
+// (its 8 row groups, then its token-mask row), read straight from the
+// (sequence, head)'s k slots, each slot clamped into them: for a token inside
+// the workgroup's range the slot is the token's own, any other token's row is
+// dropped.
+struct TileIdx {
+  int c[9];
+};
+
+__device__ __forceinline__ void fetch_tile_idx(TileIdx& ti, const AttnArgs& a, const int32_t* slots, int t0,
+                                               int lane) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int v = i < 8 ? t0 + 4 * i + (lane >> 4) : t0 + (lane & 31);
+    ti.c[i] = slots[min((unsigned)v / (unsigned)a.cs, (unsigned)(a.k - 1))];
+  }
 }
 
 __device__ __forceinline__ void write_stage(const Stage& st, unsigned char* slab, int lane) {
@@ -651,22 +697,31 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
 
   // Loads that need only the arguments (chunk slots, query rows) are issued
   // before the sequence geometry is read, so their round trips overlap it.
-  // The slots fetched cover every chunk virtual tokens [v0, v0 + tpw) can
-  // touch, clamped to the k slots of the row, so they stay in bounds whatever
-  // the sequence length turns out to be.
+  // The workgroup's slot table (LDS) covers every chunk virtual tokens
+  // [v0, v0 + tpw) can touch, clamped to the k slots of the row, so its loads
+  // stay in bounds whatever the sequence length turns out to be.  A staged
+  // sparse wave also reads the slots of its first two tiles itself, into
+  // registers, so that those tiles' loads need no LDS read and no barrier:
+  // they follow the slots' one round trip, and the table (used from a wave's
+  // third tile on) is waited for after them.
   constexpr bool kSparseIdx = MODE == kSparse || MODE == kSparseTail;
+  constexpr bool kStaged2 = kSparseIdx && NQT <= 2;
   constexpr int kIdxPerThread = kSparseIdx ? (kMaxSparseIdx + kThreads - 1) / kThreads : 1;
+  TileIdx ci0, ci1;
   int chunk_lo = 0, n_idx = 0;
   int idx_reg[kIdxPerThread];
   if (kSparseIdx) {
+    const int32_t* slots = a.idx + ((size_t)b * a.Hkv + hk) * a.k;
+    if (kStaged2) {
+      fetch_tile_idx(ci0, a, slots, v0 + kTile * w, lane);
+      fetch_tile_idx(ci1, a, slots, v0 + kTile * w + 4 * kTile, lane);
+    }
     chunk_lo = v0 / a.cs;
     n_idx = min(a.k, (v0 + a.tpw + a.cs - 1) / a.cs) - chunk_lo;
-    const int32_t* src = a.idx + ((size_t)b * a.Hkv + hk) * a.k + chunk_lo;
+    // (unconditional loads, each slot clamped into the row: a load under a
+    // branch makes the compiler's later waits for it waits for every load)
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
-      const int j = tid + u * kThreads;
-      idx_reg[u] = j < n_idx ? src[j] : -1;
-    }
+    for (int u = 0; u < kIdxPerThread; ++u) idx_reg[u] = slots[min(chunk_lo + tid + u * kThreads, a.k - 1)];
   }
 
   // Query rows of this KV head: heads hk*G .. hk*G+G-1, Qn rows each, contiguous.
@@ -711,13 +766,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   const uint16_t* __restrict__ Kb = a.K + base;
   const uint16_t* __restrict__ Vb = a.V + base;
 
+  // the slot table: written now, waited for (a barrier) before its first
+  // use -- here, or after a staged wave's first loads
   if (kSparseIdx) {
 #pragma unroll
     for (int u = 0; u < kIdxPerThread; ++u) {
       const int j = tid + u * kThreads;
       if (j < n_idx) s_idx[j] = idx_reg[u];
     }
-    __syncthreads();
+    if (!kStaged2) __syncthreads();
   }
 
   int lim[NQT];
@@ -758,30 +815,47 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   // outstanding.  LDS operations of one wave complete in order, so a slab is
   // rewritten only after the previous tile's operand reads.
   int t = v0 + kTile * w;
-  constexpr bool kStaged2 = (MODE == kSparse || MODE == kSparseTail) && NQT <= 2;
-  if (kStaged2 && t < v1) {
+  if constexpr (kStaged2) {
     // two register stages alternate into the slab; the next-but-one tile's
     // loads are issued while the staged one is consumed
+    // (issued by every wave, also one with no tile in the range -- its rows
+    // are all row 0, masked: a branch around the loads would make the
+    // compiler's waits after it count these loads too)
+    // (the scheduling barrier keeps the first tile's loads ahead of the
+    // second's, so that waiting for them does not wait for both)
+    Stage sa, sb;
+    load_stage_rows(sa, t, [&](int v, int i) { return sparse_row<MODE>(a, geo, v, v1, ci0.c[i]); }, Kb, Vb, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage_rows(sb, t + 4 * kTile, [&](int v, int i) { return sparse_row<MODE>(a, geo, v, v1, ci1.c[i]); }, Kb,
+                    Vb, lane);
+    __syncthreads();  // the slot table (every wave)
     unsigned char* slab = s_stage + w * kStageBytes;
     const SlabSource<DT> src(slab, lane);
-    Stage sa, sb;
-    load_stage<MODE>(sa, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
-    load_stage<MODE>(sb, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
-    while (true) {
-      unsigned mask = sa.mask;
+    if (t < v1) {
+      // The first tile is consumed outside the loop, where the compiler's
+      // waits cover only its own loads (at the loop's head they cover every
+      // load in flight, here both tiles').
       write_stage(sa, slab, lane);
       if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
+      process_tile<DT, MODE, NQT>(src, sa.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq,
+                                  lg);
       t += 4 * kTile;
-      if (t >= v1) break;
-      mask = sb.mask;
-      write_stage(sb, slab, lane);
-      if (t + 8 * kTile < v1) load_stage<MODE>(sb, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
-      t += 4 * kTile;
-      if (t >= v1) break;
+      while (t < v1) {
+        unsigned mask = sb.mask;
+        write_stage(sb, slab, lane);
+        if (t + 8 * kTile < v1) load_stage<MODE>(sb, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
+        t += 4 * kTile;
+        if (t >= v1) break;
+        mask = sa.mask;
+        write_stage(sa, slab, lane);
+        if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
+        t += 4 * kTile;
+      }
     }
   } else if (kStaged && t < v1) {
     unsigned char* slab = s_stage + w * kStageBytes;
