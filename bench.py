@@ -343,6 +343,54 @@ def read_ceiling(L, stream):
                     "in a HIP graph; the best grid"}
 
 
+GATHER_TPW = (128, 256, 512)
+
+
+def gather_ceiling(L, c, stream, sparse_bytes):
+    """How fast one launch can gather the sparse pass's bytes: a kernel that
+    only reads the K and V rows of the selected chunks (the measurement aid
+    libtfbench.so: chunk indices first, two 32-row tiles per wave in flight, 1
+    KB per wave instruction; no attention, no split merge), on the sparse
+    call's buffers and indices, timed like the per-kernel graphs (one launch
+    per layer), for a few workgroup sizes.  GB/s are over the sparse call's
+    algorithmic bytes, so they compare with its figure directly."""
+    import ctypes
+    import torch
+    if not os.path.exists(BENCH_LIB) or c.cs % 4 != 0:
+        return None
+    lib = ctypes.CDLL(BENCH_LIB)
+    if not hasattr(lib, "tfb_gather_kv"):
+        return None
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.tfb_gather_kv.restype = i32
+    lib.tfb_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    cyc = -(-MIN_LAUNCHES // len(L))
+    Lc = L * cyc
+    splits = -(-(c.k * c.cs) // min(GATHER_TPW))
+    sink = torch.empty(splits * c.Hkv * c.B * 4, dtype=torch.int32, device=L[0].K.device)
+    out = {}
+    with torch.cuda.stream(stream):
+        for tpw in GATHER_TPW:
+            def launches():
+                for x in Lc:
+                    st = lib.tfb_gather_kv(vp(x.K.data_ptr()), vp(x.V.data_ptr()), vp(x.kv.seq_base.data_ptr()),
+                                           vp(x.kv.seq_cap.data_ptr()), vp(x.kv.seq_len.data_ptr()),
+                                           vp(c.idx.data_ptr()), c.B, c.Hkv, c.k, c.cs, tpw, vp(sink.data_ptr()),
+                                           vp(stream.cuda_stream))
+                    if st != 0:
+                        raise RuntimeError(f"tfb_gather_kv: hip error {st}")
+            out[tpw] = time_graph(launches, stream, len(Lc))
+    best = min(out, key=lambda t: out[t]["us"])
+    return {"us": out[best]["us"], "tpw": best,
+            "GB_s": round(sparse_bytes / (out[best]["us"] * 1e-6) / 1e9, 1),
+            "frac": round(sparse_bytes / (out[best]["us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_by_tpw": {str(t): v["us"] for t, v in out.items()},
+            "what": "a kernel that only gathers the selected chunks' K and V rows (chunk indices read first, two "
+                    "32-row tiles per wave in flight, 1 KB per wave instruction), one launch per layer in a HIP "
+                    "graph, on the sparse call's buffers and indices; the best workgroup size; GB/s over the "
+                    "sparse call's algorithmic bytes"}
+
+
 def kernel_table(us, dist, by, names):
     out = {}
     for n in names:
@@ -481,6 +529,11 @@ def main():
     # (the counters and the kernel trace are of the verify launch at the default workload's shape)
     traffic = read_traffic() if default_shape else None
     trace = read_kernel_trace(verify_bytes, by["sparse"]) if default_shape else None
+    gather = gather_ceiling(L, c, stream, by["sparse"])
+    if gather:
+        # the sparse call against a bare gather of its bytes in one launch
+        kernels["sparse"]["gather_ceiling"] = gather
+        kernels["sparse"]["frac_of_gather_ceiling"] = round(gather["us"] / kernels["sparse"]["us"], 4)
     if trace and "sparse" in trace:
         # the sparse pass: the call level above (gather kernel + split merge, timed
         # together), each kernel's own traced duration here
