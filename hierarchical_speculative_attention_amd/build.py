@@ -4,7 +4,8 @@
 
 libtfattn.so, the C-ABI library of the decode path, from every .hip file
 under csrc/; libtfbench.so, a measurement aid the benchmark loads (a kernel
-that only reads, for the HBM ceiling of the verification pass), from
+that only reads, for the HBM ceiling of the verification pass, and one that
+only gathers the sparse pass's rows, for the ceiling of that call), from
 bench_kernels/.  Each source is compiled to an object in parallel, then the
 objects are linked.  Packed-fp32 instruction selection is disabled for the
 device code (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass
