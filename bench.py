@@ -307,11 +307,12 @@ BENCH_LIB = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "libtfb
 CEILING_GRIDS = (256, 512, 1024)
 
 
-def read_ceiling(L, stream):
-    """How fast HBM serves the verification pass's bytes when nothing else is
-    done with them: a kernel that only reads each layer's K and V (the
-    measurement aid libtfbench.so, verify's access shape), timed like the
-    per-kernel graphs (one launch per layer), for a few grid sizes."""
+def read_ceiling(L, stream, what="kv"):
+    """How fast HBM serves a pass's bytes when nothing else is done with them:
+    a kernel that only reads them (the measurement aid libtfbench.so, verify's
+    access shape), timed like the per-kernel graphs (one launch per layer), for
+    a few grid sizes.  what = "kv": each layer's K and V (the verification
+    pass); "ck": each layer's chunk keys (the score pass), read as two halves."""
     import ctypes
     import torch
     if not os.path.exists(BENCH_LIB):
@@ -322,25 +323,31 @@ def read_ceiling(L, stream):
                                 ctypes.c_void_p]
     cyc = -(-MIN_LAUNCHES // len(L))
     Lc = L * cyc
-    nbytes = L[0].K.numel() * L[0].K.element_size()
+    if what == "kv":
+        nbytes = L[0].K.numel() * L[0].K.element_size()
+        pairs = [(x.K.data_ptr(), x.V.data_ptr()) for x in Lc]
+    else:
+        nbytes = L[0].ck.numel() * L[0].ck.element_size() // 2 // 16 * 16
+        pairs = [(x.ck.data_ptr(), x.ck.data_ptr() + nbytes) for x in Lc]
     sink = torch.empty(max(CEILING_GRIDS) * 4, dtype=torch.int32, device=L[0].K.device)
-    out = {}
+    out, us = {}, {}
     with torch.cuda.stream(stream):
         for grid in CEILING_GRIDS:
             def launches():
-                for x in Lc:
-                    st = lib.tfb_read_kv(ctypes.c_void_p(x.K.data_ptr()), ctypes.c_void_p(x.V.data_ptr()), nbytes,
-                                         grid, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                for k_ptr, v_ptr in pairs:
+                    st = lib.tfb_read_kv(ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), nbytes, grid,
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
                     if st != 0:
                         raise RuntimeError(f"tfb_read_kv: hip error {st}")
             r = time_graph(launches, stream, len(Lc))
+            us[grid] = r["us"]
             out[grid] = 2 * nbytes / (r["us"] * 1e-6) / 1e9
     best = max(out, key=out.get)
-    return {"GB_s": round(out[best], 1), "grid": best, "bytes_per_launch": 2 * nbytes,
+    return {"GB_s": round(out[best], 1), "us": us[best], "grid": best, "bytes_per_launch": 2 * nbytes,
             "GB_s_by_grid": {str(g): round(v, 1) for g, v in out.items()},
-            "what": "a kernel that only reads each layer's K and V (verify's access shape: 1 KB per wave "
-                    "instruction, nontemporal 16-byte loads, 4 per tensor in flight per lane), one launch per layer "
-                    "in a HIP graph; the best grid"}
+            "what": ("a kernel that only reads each layer's " + ("K and V" if what == "kv" else "chunk keys") +
+                     " (verify's access shape: 1 KB per wave instruction, nontemporal 16-byte loads, 4 per tensor "
+                     "in flight per lane), one launch per layer in a HIP graph; the best grid")}
 
 
 GATHER_TPW = (128, 256, 512)
@@ -529,6 +536,11 @@ def main():
     # (the counters and the kernel trace are of the verify launch at the default workload's shape)
     traffic = read_traffic() if default_shape else None
     trace = read_kernel_trace(verify_bytes, by["sparse"]) if default_shape else None
+    ck_ceiling = read_ceiling(L, stream, "ck")
+    if ck_ceiling:
+        # the score pass against a plain read of the chunk keys it streams
+        kernels["score"]["read_ceiling"] = ck_ceiling
+        kernels["score"]["frac_of_read_ceiling"] = round(ck_ceiling["us"] / kernels["score"]["us"], 4)
     gather = gather_ceiling(L, c, stream, by["sparse"])
     if gather:
         # the sparse call against a bare gather of its bytes in one launch
