@@ -307,12 +307,15 @@ BENCH_LIB = os.path.join(ROOT, "hierarchical_speculative_attention_amd", "libtfb
 CEILING_GRIDS = (256, 512, 1024)
 
 
-def read_ceiling(L, stream, what="kv"):
+def read_ceiling(L, stream, what="kv", grids=None):
     """How fast HBM serves a pass's bytes when nothing else is done with them:
     a kernel that only reads them (the measurement aid libtfbench.so, verify's
     access shape), timed like the per-kernel graphs (one launch per layer), for
     a few grid sizes.  what = "kv": each layer's K and V (the verification
-    pass); "ck": each layer's chunk keys (the score pass), read as two halves."""
+    pass); "ck": each layer's chunk keys (the score pass), read as two halves;
+    "ring": each layer's streaming ring (K and V), where a grid of one
+    workgroup per KV head gives each workgroup one head's rows, as the
+    streaming kernel does."""
     import ctypes
     import torch
     if not os.path.exists(BENCH_LIB):
@@ -323,16 +326,20 @@ def read_ceiling(L, stream, what="kv"):
                                 ctypes.c_void_p]
     cyc = -(-MIN_LAUNCHES // len(L))
     Lc = L * cyc
+    grids = grids or CEILING_GRIDS
     if what == "kv":
         nbytes = L[0].K.numel() * L[0].K.element_size()
         pairs = [(x.K.data_ptr(), x.V.data_ptr()) for x in Lc]
+    elif what == "ring":
+        nbytes = L[0].Ks.numel() * L[0].Ks.element_size()
+        pairs = [(x.Ks.data_ptr(), x.Vs.data_ptr()) for x in Lc]
     else:
         nbytes = L[0].ck.numel() * L[0].ck.element_size() // 2 // 16 * 16
         pairs = [(x.ck.data_ptr(), x.ck.data_ptr() + nbytes) for x in Lc]
-    sink = torch.empty(max(CEILING_GRIDS) * 4, dtype=torch.int32, device=L[0].K.device)
+    sink = torch.empty(max(grids) * 4, dtype=torch.int32, device=L[0].K.device)
     out, us = {}, {}
     with torch.cuda.stream(stream):
-        for grid in CEILING_GRIDS:
+        for grid in grids:
             def launches():
                 for k_ptr, v_ptr in pairs:
                     st = lib.tfb_read_kv(ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), nbytes, grid,
@@ -345,7 +352,9 @@ def read_ceiling(L, stream, what="kv"):
     best = max(out, key=out.get)
     return {"GB_s": round(out[best], 1), "us": us[best], "grid": best, "bytes_per_launch": 2 * nbytes,
             "GB_s_by_grid": {str(g): round(v, 1) for g, v in out.items()},
-            "what": ("a kernel that only reads each layer's " + ("K and V" if what == "kv" else "chunk keys") +
+            "us_by_grid": {str(g): v for g, v in us.items()},
+            "what": ("a kernel that only reads each layer's " +
+                     {"kv": "K and V", "ck": "chunk keys", "ring": "streaming ring (K and V)"}[what] +
                      " (verify's access shape: 1 KB per wave instruction, nontemporal 16-byte loads, 4 per tensor "
                      "in flight per lane), one launch per layer in a HIP graph; the best grid")}
 
@@ -541,6 +550,13 @@ def main():
         # the score pass against a plain read of the chunk keys it streams
         kernels["score"]["read_ceiling"] = ck_ceiling
         kernels["score"]["frac_of_read_ceiling"] = round(ck_ceiling["us"] / kernels["score"]["us"], 4)
+    ring_ceiling = read_ceiling(L, stream, "ring", grids=(Hkv * B, 4 * Hkv * B, 16 * Hkv * B))
+    if ring_ceiling:
+        # streaming attention against a plain read of its ring: with one
+        # workgroup per KV head (its own grid) and spread over 4 and 16
+        kernels["stream"]["read_ceiling"] = ring_ceiling
+        kernels["stream"]["frac_of_one_workgroup_per_head_read"] = round(
+            ring_ceiling["us_by_grid"][str(Hkv * B)] / kernels["stream"]["us"], 4)
     gather = gather_ceiling(L, c, stream, by["sparse"])
     if gather:
         # the sparse call against a bare gather of its bytes in one launch
