@@ -659,7 +659,7 @@ def main():
 
 
 # The other workloads measured beside the default one: (name, budget, gamma).
-OTHER_WORKLOADS = [("gqa-hq32-hkv8-512k-16layers", 8192, 8, False), ("ragged-b8-16k-128k", 4096, 6, True),
+OTHER_WORKLOADS = [("gqa-hq32-hkv8-512k-16layers", 8192, 8, True), ("ragged-b8-16k-128k", 4096, 6, True),
                    ("ragged-b8-16k-128k", 2048, 4, False)]   # (name, budget, gamma, time the oracle too)
 
 
@@ -1087,18 +1087,23 @@ def cpu_baseline(sample_layers, lens, Hq, Hkv, d, cs, k, S, Wn, Q, layers, acc_i
            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
            "sample": f"fp64 numpy oracle on {nl} of the {layers} layers (all {Hkv} KV heads x {Hq} query heads, "
                      f"{len(lens)} sequence(s)) + 1 accept, {t_layers + t_acc:.1f} s timed, scaled to "
-                     f"{layers} layers ({t_layers / nl:.2f} s per layer); chunk-key prefill untimed"}
+                     f"{layers} layers ({t_layers / nl:.2f} s per layer); chunk-key prefill untimed",
+           "s_per_layer": round(t_layers / nl, 4)}
     # the same oracle on one thread, over a few heads of one layer
     try:
         from threadpoolctl import threadpool_limits
-        few = every[:4]
+        # four pairs spread over the sequences, scaled by their share of the
+        # layer's rows (the work of a pair grows with its sequence's length)
+        few = every[::max(1, len(every) // 4)][:4]
         with threadpool_limits(limits=1):
             t1 = heads_of(sample_layers[0], few)
             t1a = accepts()
-        t1_step = t1 / len(few) * len(every) * layers + t1a
+        rows_all = sum(lens[b] for b, _ in every)
+        rows_few = max(1, sum(lens[b] for b, _ in few))
+        t1_step = t1 * rows_all / rows_few * layers + t1a
         out["single_thread"] = {"value": round(1.0 / t1_step, 6), "unit": "steps/s", "cores": 1,
                                 "sample": f"{len(few)} (sequence, KV head) pairs of one layer + 1 accept on one "
-                                          f"thread, {t1 + t1a:.1f} s timed, scaled to the step"}
+                                          f"thread, {t1 + t1a:.1f} s timed, scaled to the step by rows"}
     except ImportError:
         pass
     return out
