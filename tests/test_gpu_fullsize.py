@@ -69,11 +69,25 @@ def new_acc():
     return {"o_abs": 0.0, "o_rel": 0.0, "o_max": 0.0, "lse_abs": 0.0, "lse_rel": 0.0}
 
 
+# A check of the arithmetic tighter than the 2e-3 bar, which at 128K context
+# is loose (|o| is 1e-2 to 3e-1 here): the kernels keep each probability to
+# about 16 significant bits (a 16-bit high part and a 16-bit remainder) and
+# accumulate in fp32, so on these inputs, whose rounding errors are
+# independent, an output is off by about 2^-16 |v| sqrt(sum p^2), some 1e-7
+# (observed 2e-8 to 7e-7).  The guards sit 60x (lse) and 300x (o, relative)
+# above what is seen.
+O_REL_GUARD = 1e-3   # max |do| / max |o| over the checked rows
+LSE_GUARD = 1e-4     # max |dlse|
+
+
 def report(name, errs_by_kind):
-    """Print the observed error margins under the 2e-3 bar (shown with -s / -rP)."""
+    """Print the observed error margins under the 2e-3 bar (shown with -s / -rP)
+    and hold them to the tighter guards above."""
     for kind, a in errs_by_kind.items():
         print(f"{name} {kind}: max|do| {a['o_abs']:.2e} (rel {a['o_rel']:.2e}, max|o| {a['o_max']:.2e}), "
               f"max|dlse| {a['lse_abs']:.2e} (rel {a['lse_rel']:.2e}); bar {ATOL:.0e}")
+        assert a["o_rel"] <= O_REL_GUARD, (name, kind, a)
+        assert a["lse_abs"] <= LSE_GUARD, (name, kind, a)
 
 
 def check_head(W, lay, b, g, Kh, Vh, ck_h, scores_h, idx_h, qd_h, qv_h, o_sp, l_sp, o_v, l_v, Q, budget, acc):
