@@ -521,11 +521,10 @@ struct Span {
 // wave (with the transposing V reads): 3 tiles 379 -> 363 us, 4 tiles faster
 // too; 2 tiles about equal, so they keep the per-wave path.  Each 32-token K/V
 // tile is fetched by all four
-// waves together, 16 rows each (1 KB per instruction), kRowRing tiles in
+// waves together, 16 rows each (1 KB per instruction), two to four tiles in
 // flight per workgroup, staged in two shared slabs and consumed after a
 // barrier by every owning wave.  A slab is rewritten two tiles later, after
 // the barrier that follows its last reads.
-constexpr int kRowRing = 4;
 
 template <int DT, int MODE, int NQT>
 __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, const int hk, const int split,
@@ -537,7 +536,9 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
-  const bool owner = w < NQT;  // (with fewer query tiles than waves, the rest would only fetch)
+  // (with fewer query tiles than waves, the rest would only fetch; a scalar,
+  // so that the branch on it is uniform)
+  const bool owner = __builtin_amdgcn_readfirstlane(w) < NQT;
   const int qt = owner ? w : 0;
   const int v0 = span ? span->v0 : split * a.tpw;
   const size_t qrow0 = ((size_t)b * a.Hq + (size_t)hk * a.G) * a.Qn;
@@ -604,28 +605,44 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   };
   // (an item with no rows fetches nothing: the sequence may have no row 0)
   const int ntiles = v1 > v0 ? (v1 - v0 + kTile - 1) / kTile : 0;
-  u32x4 R[kRowRing][4];
+  auto consume = [&](const u32x4 (&r)[4], int i) {
+    const int t = v0 + kTile * i;
+    unsigned char* slab = s_stage + (i & 1) * kStageBytes;
+    stage(r, slab);
+    const unsigned mask =
+        (unsigned)(__ballot(map_row<MODE>(a, geo, t + (lane & 31), v1, nullptr, 0) >= 0) & 0xFFFFFFFFull);
+    __syncthreads();
+    if (owner) {
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, 1>(SlabSource<DT>(slab, lane), mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run,
+                                l_run, c2, lq, lg);
+    }
+  };
+  // Two groups of two tiles alternate: while one group's tiles are consumed
+  // the other's are in flight, and the group after next is requested before
+  // the first of them is staged.  At the loop's head exactly one group is in
+  // flight, so the compiler's waits there (which cover every load in flight)
+  // cover just that group; with a ring of four tiles they drained the ring
+  // every fourth tile.  Fetches past the range read row 0, masked.
   if (ntiles > 0) {
-#pragma unroll
-    for (int j = 0; j < kRowRing; ++j) fetch(R[j], v0 + kTile * j);
-  }
-  for (int i0 = 0; i0 < ntiles; i0 += kRowRing) {
-#pragma unroll
-    for (int j = 0; j < kRowRing; ++j) {
-      const int i = i0 + j;
-      if (i >= ntiles) break;
-      const int t = v0 + kTile * i;
-      unsigned char* slab = s_stage + (j & 1) * kStageBytes;  // i and j have the same parity
-      stage(R[j], slab);
-      fetch(R[j], t + kTile * kRowRing);
-      const unsigned mask =
-          (unsigned)(__ballot(map_row<MODE>(a, geo, t + (lane & 31), v1, nullptr, 0) >= 0) & 0xFFFFFFFFull);
-      __syncthreads();
-      if (owner) {
-        __builtin_amdgcn_sched_barrier(0);
-        process_tile<DT, MODE, 1>(SlabSource<DT>(slab, lane), mask, t, qreg, sel, lim, lim_min, tm,
-                                  tbase, acc, m_run, l_run, c2, lq, lg);
-      }
+    u32x4 A[2][4], B[2][4];
+    fetch(A[0], v0);
+    fetch(A[1], v0 + kTile);
+    for (int i = 0;; i += 4) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(B[0], v0 + kTile * (i + 2));
+      fetch(B[1], v0 + kTile * (i + 3));
+      consume(A[0], i);
+      if (i + 1 >= ntiles) break;
+      consume(A[1], i + 1);
+      if (i + 2 >= ntiles) break;
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(A[0], v0 + kTile * (i + 4));
+      fetch(A[1], v0 + kTile * (i + 5));
+      consume(B[0], i + 2);
+      if (i + 3 >= ntiles) break;
+      consume(B[1], i + 3);
+      if (i + 4 >= ntiles) break;
     }
   }
   __syncthreads();  // every slab consumed: the results reuse them
