@@ -620,10 +620,12 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
   };
   // Two groups of two tiles alternate: while one group's tiles are consumed
   // the other's are in flight, and the group after next is requested before
-  // the first of them is staged.  At the loop's head exactly one group is in
-  // flight, so the compiler's waits there (which cover every load in flight)
-  // cover just that group; with a ring of four tiles they drained the ring
-  // every fourth tile.  Fetches past the range read row 0, masked.
+  // the first of them is staged.  At the loop's head only one group is in
+  // flight, so the compiler's waits there (which, with the loop's exits
+  // leading back to its head, cover the loads in flight as if any were
+  // still pending) hold at most that group; with a ring of four tiles they
+  // drained the whole ring every fourth tile.  Fetches past the range read
+  // row 0, masked.
   if (ntiles > 0) {
     u32x4 A[2][4], B[2][4];
     fetch(A[0], v0);
