@@ -74,6 +74,19 @@ def test_verify_batch_at_the_equal_work_limit(B):
     compare_attn(out, lse, *oracle_verify(inp, 3))
 
 
+@pytest.mark.parametrize("Q", [9, 16])
+def test_verify_batch_rows_split_over_waves(Q):
+    """A batch on the equal-work grid with 36 and 64 rows per KV head (query
+    rows split over the waves, tiles fetched in alternating groups of two):
+    1904 tiles over 512 workgroups give items of one to four tiles, and the
+    batch holds an empty sequence and ones shorter than the rows."""
+    lens = [0, 5, 32, 95, 128, 161, 3000, 4099]
+    print(f"batch verify: lens={lens} Hq=32 Hkv=8 Q={Q}", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=32, Hkv=8, dtype="bf16", Q=Q, seed=72, cap_extra=6)
+    out, lse = run_verify(inp, Q)
+    compare_attn(out, lse, *oracle_verify(inp, Q))
+
+
 @pytest.mark.parametrize("Hq,Hkv,Q,n", [(32, 8, 9, 2000), (16, 2, 8, 777), (4, 4, 1, 5000), (6, 3, 7, 129)])
 def test_verify_query_tiles(Hq, Hkv, Q, n):
     # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14
