@@ -853,12 +853,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
     if (t < v1) {
       // The first tile is consumed outside the loop, where the compiler's
       // waits cover only its own loads (at the loop's head they cover every
-      // load in flight, here both tiles').
+      // load in flight, here both tiles').  Its mask is taken before the
+      // stage is refilled with the wave's third tile.
+      const unsigned mask0 = sa.mask;
       write_stage(sa, slab, lane);
       if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
       __builtin_amdgcn_sched_barrier(0);
-      process_tile<DT, MODE, NQT>(src, sa.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq,
-                                  lg);
+      process_tile<DT, MODE, NQT>(src, mask0, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
       t += 4 * kTile;
       while (t < v1) {
         unsigned mask = sb.mask;

@@ -200,6 +200,71 @@ def test_sparse_chunk_sizes(cs, k):
     compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
 
 
+def sparse_plan_tpw(B, Hkv, virtual):
+    """Gathered tokens per workgroup of the sparse split plan: splits that
+    fill one round of 512 workgroups, a multiple of 32 between 256 and 1024
+    (the C ABI's plan, restated so that the test can say which regime a
+    shape falls in; the plan's short last split, which these shapes do not
+    reach, is left out)."""
+    per_head = 512 // (B * Hkv)
+    if per_head < 1:
+        return 1024
+    rounds = max(1, -(-virtual // (per_head * 1024)))
+    fit = -(-virtual // (per_head * rounds))
+    return min(1024, max(256, -(-fit // 32) * 32))
+
+
+def random_selection(rng, lens, Hkv, k, cs):
+    """k chunk slots per (sequence, KV head): distinct chunks in ascending
+    order, then the partial last chunk, a chunk past the end and -1 padding."""
+    idx = np.full((len(lens), Hkv, k), -1, np.int64)
+    for b, n in enumerate(lens):
+        C = -(-n // cs)
+        for g in range(Hkv):
+            m = min(k - 2, C)
+            idx[b, g, :m] = np.sort(rng.choice(C, size=m, replace=False)) if m > 0 else []
+            idx[b, g, m] = max(C - 1, 0) if C > 0 else -1
+            idx[b, g, m + 1] = C + 2
+    return idx
+
+
+@pytest.mark.parametrize("mode", ["sparse", "sparse_verify"])
+@pytest.mark.parametrize("shape", ["two_tiles_per_wave", "long_items", "many_heads"])
+def test_sparse_items_with_and_without_a_slot_table(mode, shape):
+    """Workgroups of at most 256 gathered tokens (no wave takes more than two
+    32-row tiles) take every chunk slot they use from registers; in longer
+    items a wave's third tile on is mapped through the workgroup's slot
+    table in LDS, and its first tile keeps its own row mask while its stage
+    is refilled with the third (padded and past-the-end slots make the two
+    masks differ).  Both regimes, for both sparse modes: one sequence of 16
+    KV heads with 1500 selected chunks (384 tokens per workgroup), 80 short
+    ragged sequences of 8 KV heads (more heads than the grid's round: 1024
+    tokens per workgroup, one item each), and a shape of 256 per workgroup."""
+    cs, Q = 8, (3 if mode == "sparse_verify" else 1)
+    rng = np.random.default_rng(90)
+    if shape == "long_items":
+        lens, Hq, Hkv, k = [12500], 16, 16, 1500
+    elif shape == "many_heads":
+        lens = [int(x) for x in rng.integers(0, 1500, 80)]
+        lens[0], lens[1] = 0, 1
+        Hq, Hkv, k = 16, 8, 40
+    else:
+        lens, Hq, Hkv, k = [5000, 3333], 8, 4, 300
+    tail = 40 if mode == "sparse_verify" else 0
+    tpw = sparse_plan_tpw(len(lens), Hkv, k * cs + tail)
+    assert (tpw <= 256) == (shape == "two_tiles_per_wave"), tpw
+    print(f"sparse items: mode={mode} shape={shape} B={len(lens)} Hkv={Hkv} k={k} tokens/workgroup={tpw}",
+          flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=91, cap_extra=5)
+    idx = random_selection(rng, lens, Hkv, k, cs)
+    if mode == "sparse":
+        out, lse = run_sparse(inp, idx, cs)
+        compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
+    else:
+        out, lse = run_sparse_verify(inp, idx, cs, tail)
+        compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
+
+
 # ---------------------------------------------------------------------------
 # stream (Force 1)
 # ---------------------------------------------------------------------------
