@@ -694,8 +694,9 @@ __device__ __forceinline__ void attn_item_rows(const AttnArgs& a, const int b, c
 }
 
 // One work item: split `split` of KV head hk of sequence b, by the whole
-// workgroup (the LDS arrays are the kernel's).
-template <int DT, int MODE, int NQT>
+// workgroup (the LDS arrays are the kernel's).  SHORT: a sparse item of at
+// most 8 tiles (tpw <= 256), so that no wave takes more than two.
+template <int DT, int MODE, int NQT, bool SHORT>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const int hk, const int split,
                                           const Span* span, int* s_idx, unsigned char* s_stage, float (*s_m)[16],
                                           float (*s_l)[16]) {
@@ -722,10 +723,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   // sparse wave also reads the slots of its first two tiles itself, into
   // registers, so that those tiles' loads need no LDS read and no barrier:
   // they follow the slots' one round trip, and the table (used from a wave's
-  // third tile on) is waited for after them.
+  // third tile on) is waited for after them.  Where no wave has a third
+  // tile (SHORT) there is no table, and so no barrier before the first tile.
   constexpr bool kSparseIdx = MODE == kSparse || MODE == kSparseTail;
   constexpr bool kStaged2 = kSparseIdx && NQT <= 2;
-  constexpr int kIdxPerThread = kSparseIdx ? (kMaxSparseIdx + kThreads - 1) / kThreads : 1;
+  constexpr bool kTable = kSparseIdx && !(kStaged2 && SHORT);
+  static_assert(!SHORT || kStaged2, "two tiles per wave: staged sparse items only");
+  constexpr int kIdxPerThread = kTable ? (kMaxSparseIdx + kThreads - 1) / kThreads : 1;
   TileIdx ci0, ci1;
   int chunk_lo = 0, n_idx = 0;
   int idx_reg[kIdxPerThread];
@@ -739,8 +743,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
     n_idx = min(a.k, (v0 + a.tpw + a.cs - 1) / a.cs) - chunk_lo;
     // (unconditional loads, each slot clamped into the row: a load under a
     // branch makes the compiler's later waits for it waits for every load)
+    if constexpr (kTable) {
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) idx_reg[u] = slots[min(chunk_lo + tid + u * kThreads, a.k - 1)];
+      for (int u = 0; u < kIdxPerThread; ++u) idx_reg[u] = slots[min(chunk_lo + tid + u * kThreads, a.k - 1)];
+    }
   }
 
   // Query rows of this KV head: heads hk*G .. hk*G+G-1, Qn rows each, contiguous.
@@ -787,7 +793,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
 
   // the slot table: written now, waited for (a barrier) before its first
   // use -- here, or after a staged wave's first loads
-  if (kSparseIdx) {
+  if (kTable) {
 #pragma unroll
     for (int u = 0; u < kIdxPerThread; ++u) {
       const int j = tid + u * kThreads;
@@ -847,7 +853,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
     __builtin_amdgcn_sched_barrier(0);
     load_stage_rows(sb, t + 4 * kTile, [&](int v, int i) { return sparse_row<MODE>(a, geo, v, v1, ci1.c[i]); }, Kb,
                     Vb, lane);
-    __syncthreads();  // the slot table (every wave)
+    if (kTable) __syncthreads();  // the slot table (every wave)
     unsigned char* slab = s_stage + w * kStageBytes;
     const SlabSource<DT> src(slab, lane);
     if (t < v1) {
@@ -857,21 +863,21 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
       // stage is refilled with the wave's third tile.
       const unsigned mask0 = sa.mask;
       write_stage(sa, slab, lane);
-      if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+      if (kTable && t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
       __builtin_amdgcn_sched_barrier(0);
       process_tile<DT, MODE, NQT>(src, mask0, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
       t += 4 * kTile;
       while (t < v1) {
         unsigned mask = sb.mask;
         write_stage(sb, slab, lane);
-        if (t + 8 * kTile < v1) load_stage<MODE>(sb, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+        if (kTable && t + 8 * kTile < v1) load_stage<MODE>(sb, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
         __builtin_amdgcn_sched_barrier(0);
         process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
         t += 4 * kTile;
         if (t >= v1) break;
         mask = sa.mask;
         write_stage(sa, slab, lane);
-        if (t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+        if (kTable && t + 8 * kTile < v1) load_stage<MODE>(sa, a, geo, t + 8 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
         __builtin_amdgcn_sched_barrier(0);
         process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
         t += 4 * kTile;
@@ -1023,8 +1029,9 @@ __device__ __forceinline__ long flat_wg_of(long x, long TT, long G) { return ((x
 // items i, i + gridDim.x, ... of the batch's actual items: with a grid sized
 // for the longest sequence, the items of short sequences would leave most
 // workgroups empty and, since workgroups go to the XCDs in index order, load
-// the XCDs unevenly.
-template <int DT, int MODE, int NQT, bool FLAT>
+// the XCDs unevenly.  SHORT: sparse items of at most 8 tiles (see attn_item),
+// which keep no slot table.
+template <int DT, int MODE, int NQT, bool FLAT, bool SHORT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT >= 3)) ? 2 : 1,
     (NQT == 1 || ((MODE == kVerify || MODE == kVerifyTree) && NQT >= 3)) ? 2 : 1)))
@@ -1036,7 +1043,7 @@ void attn_kernel(const AttnArgs a) {
   constexpr bool kSlabs4 = (kStaged && NQT <= 2) || ((MODE == kSparse || MODE == kSparseTail) && NQT <= 2);
   constexpr int kStageLds = kSlabs4 ? 4 * kStageBytes : (kStaged ? 2 * kStageBytes : kMergeBytes);
   static_assert(kMergeBytes <= 2 * kStageBytes, "results must fit in two slabs");
-  __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) ? kMaxSparseIdx : 1];
+  __shared__ int s_idx[(MODE == kSparse || MODE == kSparseTail) && !SHORT ? kMaxSparseIdx : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[kStageLds];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
@@ -1067,7 +1074,7 @@ void attn_kernel(const AttnArgs a) {
       sp.v1 = (int)((x1 - seg0) * kTile);
       sp.part = flat_wg_of(seg0, TT, G) == flat_wg_of(seg1 - 1, TT, G) ? -1L
                                                                            : (long)blockIdx.x + (long)lo * a.Hkv + hk;
-      attn_item<DT, MODE, NQT>(a, lo, hk, 0, &sp, s_idx, s_stage, s_m, s_l);
+      attn_item<DT, MODE, NQT, SHORT>(a, lo, hk, 0, &sp, s_idx, s_stage, s_m, s_l);
       x = x1;
     }
   } else {
@@ -1082,9 +1089,9 @@ void attn_kernel(const AttnArgs a) {
       const int L = blockIdx.x;
       const int split = L < full * heads ? L % full : full;
       const int head = L < full * heads ? L / full : L - full * heads;
-      attn_item<DT, MODE, NQT>(a, head / a.Hkv, head % a.Hkv, split, nullptr, s_idx, s_stage, s_m, s_l);
+      attn_item<DT, MODE, NQT, SHORT>(a, head / a.Hkv, head % a.Hkv, split, nullptr, s_idx, s_stage, s_m, s_l);
     } else {
-      attn_item<DT, MODE, NQT>(a, blockIdx.z, blockIdx.y, blockIdx.x, nullptr, s_idx, s_stage, s_m, s_l);
+      attn_item<DT, MODE, NQT, SHORT>(a, blockIdx.z, blockIdx.y, blockIdx.x, nullptr, s_idx, s_stage, s_m, s_l);
     }
   }
 }
@@ -1271,6 +1278,17 @@ SplitPlan plan_flat(int32_t B, int32_t Hkv, int32_t rows, int32_t G) {
   return p;
 }
 
+template <int DT, int MODE, int NQT, bool FLAT, bool MAY_SHORT>
+static void launch_kernel(bool short_items, dim3 grid, dim3 block, hipStream_t stream, const AttnArgs& a) {
+  if constexpr (MAY_SHORT) {
+    if (short_items) {
+      hipLaunchKernelGGL((attn_kernel<DT, MODE, NQT, FLAT, true>), grid, block, 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((attn_kernel<DT, MODE, NQT, FLAT, false>), grid, block, 0, stream, a);
+}
+
 template <int DT, int MODE, bool FLAT>
 static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.Hkv, a.B), block(kThreads);
@@ -1280,11 +1298,14 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
   }
   if (FLAT) grid = dim3((unsigned)a.flat_wgs, 1, 1);
   const int nqt = (a.rows + 15) / 16;
+  // sparse items of at most 8 tiles (two per wave) keep no slot table
+  constexpr bool kMayShort = (MODE == kSparse || MODE == kSparseTail) && !FLAT;
+  const bool short_items = kMayShort && a.tpw <= 8 * kTile;
   switch (nqt) {
-    case 1: hipLaunchKernelGGL((attn_kernel<DT, MODE, 1, FLAT>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<DT, MODE, 2, FLAT>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((attn_kernel<DT, MODE, 3, FLAT>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<DT, MODE, 4, FLAT>), grid, block, 0, stream, a); break;
+    case 1: launch_kernel<DT, MODE, 1, FLAT, kMayShort>(short_items, grid, block, stream, a); break;
+    case 2: launch_kernel<DT, MODE, 2, FLAT, kMayShort>(short_items, grid, block, stream, a); break;
+    case 3: launch_kernel<DT, MODE, 3, FLAT, false>(false, grid, block, stream, a); break;
+    case 4: launch_kernel<DT, MODE, 4, FLAT, false>(false, grid, block, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
