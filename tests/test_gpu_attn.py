@@ -265,6 +265,40 @@ def test_sparse_items_with_and_without_a_slot_table(mode, shape):
         compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
 
 
+@pytest.mark.parametrize("mode,Hq,Hkv,Q,shape", [
+    ("sparse", 40, 2, 1, "few_heads"),           # 20 rows per KV head: 2 query tiles, two tiles per wave
+    ("sparse", 160, 8, 1, "many_heads"),         # 20 rows, 1024 tokens per workgroup (slot table)
+    ("sparse", 80, 2, 1, "few_heads"),           # 40 rows: 3 query tiles (direct loads)
+    ("sparse", 64, 1, 1, "few_heads"),           # 64 rows: 4 query tiles
+    ("sparse_verify", 32, 8, 5, "many_heads"),   # 20 rows, 1024 tokens per workgroup
+    ("sparse_verify", 16, 2, 5, "few_heads"),    # 40 rows: 3 query tiles
+    ("sparse_verify", 8, 1, 8, "few_heads"),     # 64 rows: 4 query tiles
+])
+def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape):
+    """More than 16 query rows per KV head (many query heads per KV head,
+    or several drafted rows each): two to four 16-row query tiles, staged
+    (two) or loaded straight into the operand layout (three and four)."""
+    cs, k = 8, 40
+    rng = np.random.default_rng(Hq * 7 + Q)
+    if shape == "many_heads":
+        lens = [int(x) for x in rng.integers(0, 1200, 70)]
+        lens[0], lens[1] = 0, 1
+    else:
+        lens = [3, 50, 1001, 4099]
+    tail = 16 if mode == "sparse_verify" else 0
+    tpw = sparse_plan_tpw(len(lens), Hkv, k * cs + tail)
+    print(f"sparse query tiles: mode={mode} Hq={Hq} Hkv={Hkv} Q={Q} rows={Hq // Hkv * Q} B={len(lens)} "
+          f"tokens/workgroup={tpw}", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=92, cap_extra=5)
+    idx = random_selection(rng, lens, Hkv, k, cs)
+    if mode == "sparse":
+        out, lse = run_sparse(inp, idx, cs)
+        compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
+    else:
+        out, lse = run_sparse_verify(inp, idx, cs, tail)
+        compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
+
+
 # ---------------------------------------------------------------------------
 # stream (Force 1)
 # ---------------------------------------------------------------------------
@@ -284,6 +318,30 @@ def test_stream_parity(dtype, S, W):
             q = oracle.widen(s.q[b, h, 0], dtype)
             o_ref[b, h], l_ref[b, h] = oracle.stream_attn_masked(
                 q, oracle.widen(s.K_logical[b][g], dtype), oracle.widen(s.V_logical[b][g], dtype), n, S, W)
+    compare_attn(out, lse, o_ref, l_ref)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(40, 2), (80, 2), (64, 1)])
+def test_stream_with_more_query_tiles(Hq, Hkv):
+    """20, 40 and 64 query heads per KV head: two to four query tiles over
+    the ring."""
+    S, W = 4, 252
+    lens = [4096, 1000, 100, 3, 256, 257, 1]
+    print(f"stream query tiles: Hq={Hq} Hkv={Hkv}", flush=True)
+    s = synth.make_stream_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", n_sink=S, window=W, seed=93)
+    sd = desc(s.layout, "bf16")
+    out, lse = tf.stream_attn(dev(s.q, "bf16").view(len(lens), Hq, 128), dev(s.Ks, "bf16"), dev(s.Vs, "bf16"), sd,
+                              S, W)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    o_ref = np.zeros((len(lens), Hq, 128))
+    l_ref = np.zeros((len(lens), Hq))
+    for b, n in enumerate(lens):
+        for h in range(Hq):
+            g = h // G
+            o_ref[b, h], l_ref[b, h] = oracle.stream_attn_masked(
+                oracle.widen(s.q[b, h, 0], "bf16"), oracle.widen(s.K_logical[b][g], "bf16"),
+                oracle.widen(s.V_logical[b][g], "bf16"), n, S, W)
     compare_attn(out, lse, o_ref, l_ref)
 
 
