@@ -74,23 +74,26 @@ def test_verify_batch_at_the_equal_work_limit(B):
     compare_attn(out, lse, *oracle_verify(inp, 3))
 
 
-@pytest.mark.parametrize("Q", [9, 16])
-def test_verify_batch_rows_split_over_waves(Q):
+@pytest.mark.parametrize("Q,dtype", [(9, "bf16"), (16, "bf16"), (7, "bf16"), (9, "fp16")])
+def test_verify_batch_rows_split_over_waves(Q, dtype):
     """A batch on the equal-work grid with 36 and 64 rows per KV head (query
-    rows split over the waves, tiles fetched in alternating groups of two):
-    1904 tiles over 512 workgroups give items of one to four tiles, and the
-    batch holds an empty sequence and ones shorter than the rows."""
+    rows split over the waves, tiles fetched in alternating groups of two),
+    and with 28 (two query tiles, wave-private slabs): 1904 tiles over 512
+    workgroups give items of one to four tiles, and the batch holds an empty
+    sequence and ones shorter than the rows."""
     lens = [0, 5, 32, 95, 128, 161, 3000, 4099]
-    print(f"batch verify: lens={lens} Hq=32 Hkv=8 Q={Q}", flush=True)
-    inp = synth.make_attn_inputs(lens=lens, Hq=32, Hkv=8, dtype="bf16", Q=Q, seed=72, cap_extra=6)
+    print(f"batch verify: lens={lens} Hq=32 Hkv=8 Q={Q} {dtype}", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=32, Hkv=8, dtype=dtype, Q=Q, seed=72, cap_extra=6)
     out, lse = run_verify(inp, Q)
     compare_attn(out, lse, *oracle_verify(inp, Q))
 
 
-@pytest.mark.parametrize("Hq,Hkv,Q,n", [(32, 8, 9, 2000), (16, 2, 8, 777), (4, 4, 1, 5000), (6, 3, 7, 129)])
-def test_verify_query_tiles(Hq, Hkv, Q, n):
-    # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14
-    inp = synth.make_attn_inputs(lens=[n], Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=2, cap_extra=3)
+@pytest.mark.parametrize("Hq,Hkv,Q,n,dtype", [(32, 8, 9, 2000, "bf16"), (16, 2, 8, 777, "bf16"), (4, 4, 1, 5000, "bf16"),
+                                              (6, 3, 7, 129, "bf16"), (32, 8, 9, 2000, "fp16"), (16, 2, 8, 777, "fp16"),
+                                              (32, 8, 7, 3001, "fp16")])
+def test_verify_query_tiles(Hq, Hkv, Q, n, dtype):
+    # rows per KV head G*Q = 36 (3 MFMA query tiles), 64 (4 tiles), 1, 14, and 28 (2 tiles)
+    inp = synth.make_attn_inputs(lens=[n], Hq=Hq, Hkv=Hkv, dtype=dtype, Q=Q, seed=2, cap_extra=3)
     out, lse = run_verify(inp, Q)
     compare_attn(out, lse, *oracle_verify(inp, Q))
 
@@ -265,16 +268,18 @@ def test_sparse_items_with_and_without_a_slot_table(mode, shape):
         compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
 
 
-@pytest.mark.parametrize("mode,Hq,Hkv,Q,shape", [
-    ("sparse", 40, 2, 1, "few_heads"),           # 20 rows per KV head: 2 query tiles, two tiles per wave
-    ("sparse", 160, 8, 1, "many_heads"),         # 20 rows, 1024 tokens per workgroup (slot table)
-    ("sparse", 80, 2, 1, "few_heads"),           # 40 rows: 3 query tiles (direct loads)
-    ("sparse", 64, 1, 1, "few_heads"),           # 64 rows: 4 query tiles
-    ("sparse_verify", 32, 8, 5, "many_heads"),   # 20 rows, 1024 tokens per workgroup
-    ("sparse_verify", 16, 2, 5, "few_heads"),    # 40 rows: 3 query tiles
-    ("sparse_verify", 8, 1, 8, "few_heads"),     # 64 rows: 4 query tiles
+@pytest.mark.parametrize("mode,Hq,Hkv,Q,shape,dtype", [
+    ("sparse", 40, 2, 1, "few_heads", "bf16"),           # 20 rows per KV head: 2 query tiles, two tiles per wave
+    ("sparse", 160, 8, 1, "many_heads", "bf16"),         # 20 rows, 1024 tokens per workgroup (slot table)
+    ("sparse", 80, 2, 1, "few_heads", "bf16"),           # 40 rows: 3 query tiles (direct loads)
+    ("sparse", 64, 1, 1, "few_heads", "bf16"),           # 64 rows: 4 query tiles
+    ("sparse", 80, 2, 1, "few_heads", "fp16"),
+    ("sparse_verify", 32, 8, 5, "many_heads", "bf16"),   # 20 rows, 1024 tokens per workgroup
+    ("sparse_verify", 16, 2, 5, "few_heads", "bf16"),    # 40 rows: 3 query tiles
+    ("sparse_verify", 8, 1, 8, "few_heads", "bf16"),     # 64 rows: 4 query tiles
+    ("sparse_verify", 8, 1, 8, "few_heads", "fp16"),
 ])
-def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape):
+def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape, dtype):
     """More than 16 query rows per KV head (many query heads per KV head,
     or several drafted rows each): two to four 16-row query tiles, staged
     (two) or loaded straight into the operand layout (three and four)."""
@@ -288,8 +293,8 @@ def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape):
     tail = 16 if mode == "sparse_verify" else 0
     tpw = sparse_plan_tpw(len(lens), Hkv, k * cs + tail)
     print(f"sparse query tiles: mode={mode} Hq={Hq} Hkv={Hkv} Q={Q} rows={Hq // Hkv * Q} B={len(lens)} "
-          f"tokens/workgroup={tpw}", flush=True)
-    inp = synth.make_attn_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=92, cap_extra=5)
+          f"tokens/workgroup={tpw} {dtype}", flush=True)
+    inp = synth.make_attn_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype=dtype, Q=Q, seed=92, cap_extra=5)
     idx = random_selection(rng, lens, Hkv, k, cs)
     if mode == "sparse":
         out, lse = run_sparse(inp, idx, cs)
@@ -321,16 +326,16 @@ def test_stream_parity(dtype, S, W):
     compare_attn(out, lse, o_ref, l_ref)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(40, 2), (80, 2), (64, 1)])
-def test_stream_with_more_query_tiles(Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(40, 2, "bf16"), (80, 2, "bf16"), (64, 1, "bf16"), (80, 2, "fp16")])
+def test_stream_with_more_query_tiles(Hq, Hkv, dtype):
     """20, 40 and 64 query heads per KV head: two to four query tiles over
     the ring."""
     S, W = 4, 252
     lens = [4096, 1000, 100, 3, 256, 257, 1]
-    print(f"stream query tiles: Hq={Hq} Hkv={Hkv}", flush=True)
-    s = synth.make_stream_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", n_sink=S, window=W, seed=93)
-    sd = desc(s.layout, "bf16")
-    out, lse = tf.stream_attn(dev(s.q, "bf16").view(len(lens), Hq, 128), dev(s.Ks, "bf16"), dev(s.Vs, "bf16"), sd,
+    print(f"stream query tiles: Hq={Hq} Hkv={Hkv} {dtype}", flush=True)
+    s = synth.make_stream_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype=dtype, n_sink=S, window=W, seed=93)
+    sd = desc(s.layout, dtype)
+    out, lse = tf.stream_attn(dev(s.q, dtype).view(len(lens), Hq, 128), dev(s.Ks, dtype), dev(s.Vs, dtype), sd,
                               S, W)
     torch.cuda.synchronize()
     G = Hq // Hkv
@@ -340,8 +345,8 @@ def test_stream_with_more_query_tiles(Hq, Hkv):
         for h in range(Hq):
             g = h // G
             o_ref[b, h], l_ref[b, h] = oracle.stream_attn_masked(
-                oracle.widen(s.q[b, h, 0], "bf16"), oracle.widen(s.K_logical[b][g], "bf16"),
-                oracle.widen(s.V_logical[b][g], "bf16"), n, S, W)
+                oracle.widen(s.q[b, h, 0], dtype), oracle.widen(s.K_logical[b][g], dtype),
+                oracle.widen(s.V_logical[b][g], dtype), n, S, W)
     compare_attn(out, lse, o_ref, l_ref)
 
 
