@@ -231,8 +231,19 @@ def random_selection(rng, lens, Hkv, k, cs):
     return idx
 
 
+# (sequences, query heads, KV heads, selected chunks of 8 rows) per shape;
+# whether its workgroups take at most 256 gathered tokens
+SPARSE_ITEM_SHAPES = {
+    "two_tiles_per_wave": (None, 8, 4, 300, True),
+    "long_items": ([12500], 16, 16, 1500, False),      # 384 tokens per workgroup, 32 splits
+    "many_heads": (None, 16, 8, 40, False),             # 80 short sequences: 1024 per workgroup, one item
+    "many_splits": ([17000], 4, 1, 2000, True),         # 63 splits of 256 per head: two merge groups
+    "many_long_splits": ([133000], 2, 1, 16500, False), # 459 splits of 288: fifteen merge groups
+}
+
+
 @pytest.mark.parametrize("mode", ["sparse", "sparse_verify"])
-@pytest.mark.parametrize("shape", ["two_tiles_per_wave", "long_items", "many_heads"])
+@pytest.mark.parametrize("shape", list(SPARSE_ITEM_SHAPES))
 def test_sparse_items_with_and_without_a_slot_table(mode, shape):
     """Workgroups of at most 256 gathered tokens (no wave takes more than two
     32-row tiles) take every chunk slot they use from registers; in longer
@@ -242,22 +253,22 @@ def test_sparse_items_with_and_without_a_slot_table(mode, shape):
     masks differ).  Both regimes, for both sparse modes: one sequence of 16
     KV heads with 1500 selected chunks (384 tokens per workgroup), 80 short
     ragged sequences of 8 KV heads (more heads than the grid's round: 1024
-    tokens per workgroup, one item each), and a shape of 256 per workgroup."""
+    tokens per workgroup, one item each), a shape of 256 per workgroup, and
+    one KV head split 63 and 459 ways (the split merge takes its partials
+    in groups of 32)."""
     cs, Q = 8, (3 if mode == "sparse_verify" else 1)
     rng = np.random.default_rng(90)
-    if shape == "long_items":
-        lens, Hq, Hkv, k = [12500], 16, 16, 1500
-    elif shape == "many_heads":
+    lens, Hq, Hkv, k, short = SPARSE_ITEM_SHAPES[shape]
+    if shape == "many_heads":
         lens = [int(x) for x in rng.integers(0, 1500, 80)]
         lens[0], lens[1] = 0, 1
-        Hq, Hkv, k = 16, 8, 40
-    else:
-        lens, Hq, Hkv, k = [5000, 3333], 8, 4, 300
+    elif shape == "two_tiles_per_wave":
+        lens = [5000, 3333]
     tail = 40 if mode == "sparse_verify" else 0
     tpw = sparse_plan_tpw(len(lens), Hkv, k * cs + tail)
-    assert (tpw <= 256) == (shape == "two_tiles_per_wave"), tpw
-    print(f"sparse items: mode={mode} shape={shape} B={len(lens)} Hkv={Hkv} k={k} tokens/workgroup={tpw}",
-          flush=True)
+    assert (tpw <= 256) == short, tpw
+    print(f"sparse items: mode={mode} shape={shape} B={len(lens)} Hkv={Hkv} k={k} tokens/workgroup={tpw} "
+          f"splits={-(-(k * cs + tail) // tpw)}", flush=True)
     inp = synth.make_attn_inputs(lens=lens, Hq=Hq, Hkv=Hkv, dtype="bf16", Q=Q, seed=91, cap_extra=5)
     idx = random_selection(rng, lens, Hkv, k, cs)
     if mode == "sparse":
