@@ -247,3 +247,32 @@ def test_llama2_7b_128k_verify_in_a_larger_allocation():
         do, dl = errs(ov[0, g], o, lv[0, g], l, acc)
         assert do <= ATOL and dl <= ATOL
     report("llama2-7b-128k verify, 512 rows allocated past n", {"verify": acc})
+
+
+def test_gqa_512k_verify_in_a_larger_allocation():
+    # GQA 512K (36 rows per KV head: query rows split over the waves) in a
+    # cache allocated 512 rows past the sequence: one round of 64 splits of
+    # 8192 rows per KV head and a short 65th, dispatched after all the others
+    # (a 1-D grid); parity on the first and last KV heads
+    Q = 9
+    W = synth.WORKLOADS["gqa-hq32-hkv8-512k-16layers"]
+    K, V, qv, qd, lay, _ = synth.make_layer_torch(
+        lens=W["lens"], Hq=W["Hq"], Hkv=W["Hkv"], d=128, dtype="bf16", Q=Q, chunk_size=W["chunk_size"],
+        plant=None, seed=4, layer=0, device=DEV, extra_rows=512)
+    n = int(lay.seq_len[0])
+    G = W["Hq"] // W["Hkv"]
+    kv = KVDesc.from_layout(lay, torch.bfloat16, DEV, max_len=n + 512)
+    o_v, l_v = tf.verify_attn(qv, K, V, kv)
+    torch.cuda.synchronize()
+    qv_b = host_bits(qv)
+    ov, lv = o_v.cpu().double().numpy(), l_v.cpu().double().numpy()
+    acc = new_acc()
+    for g in (0, W["Hkv"] - 1):
+        Kh = oracle.widen(head_bits_gpu(K, lay, 0, g).reshape(-1, 128), "bf16")
+        Vh = oracle.widen(head_bits_gpu(V, lay, 0, g).reshape(-1, 128), "bf16")
+        for h in range(g * G, (g + 1) * G):
+            o, l = oracle.verify_attn(oracle.widen(qv_b[0, h], "bf16"), Kh, Vh, n)
+            do, dl = errs(ov[0, h], o, lv[0, h], l, acc)
+            assert do <= ATOL and dl <= ATOL
+        del Kh, Vh
+    report("gqa 512k verify, 512 rows allocated past n", {"verify": acc})
