@@ -903,7 +903,22 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   } else if (!kStaged && !kStaged2 && t < v1) {
     Tile<DT> A, B;
     load_tile<DT, MODE>(A, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
-    while (true) {
+    // A wave with at most two tiles (the 4 + 252 ring: two each) requests
+    // nothing past them: the loop below would request a third, past the end
+    // (row 0, masked), and that tile's 16 KB through the one compute unit's
+    // load path cost 0.45 us of 8.2 (1 or 2 query tiles; with 3-4 the extra
+    // copies of the tile step do not fit the registers).
+    if (NQT <= 2 && t + 8 * kTile >= v1) {
+      load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile<DT, MODE, NQT>(RegSource<DT>{A}, A.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run,
+                                  l_run, c2, lq, lg);
+      if (t + 4 * kTile < v1) {
+        __builtin_amdgcn_sched_barrier(0);
+        process_tile<DT, MODE, NQT>(RegSource<DT>{B}, B.mask, t + 4 * kTile, qreg, sel, lim, lim_min, tm, tbase, acc,
+                                    m_run, l_run, c2, lq, lg);
+      }
+    } else while (true) {
       load_tile<DT, MODE>(B, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lq, lg);
       __builtin_amdgcn_sched_barrier(0);
       process_tile<DT, MODE, NQT>(RegSource<DT>{A}, A.mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run,
