@@ -190,8 +190,10 @@ def test_sparse_full_budget_equals_verify_q1():
     compare_attn(out, lse, *oracle_sparse(inp, idx, 8))
 
 
-@pytest.mark.parametrize("cs,k", [(1, 1), (16, 512), (3, 100)])
+@pytest.mark.parametrize("cs,k", [(1, 1), (16, 512), (3, 100), (33, 60), (64, 40), (1000, 3), (4096, 1)])
 def test_sparse_chunk_sizes(cs, k):
+    # chunks of 33 and 64 rows span tiles and cross workgroups; 1000 and the
+    # largest size (4096) span several workgroups
     inp = synth.make_attn_inputs(lens=[3000], Hq=4, Hkv=2, dtype="bf16", Q=1, seed=7)
     C = -(-3000 // cs)
     rng = np.random.default_rng(cs)

@@ -67,6 +67,16 @@ def test_chunk_keys_parity(dtype, out_dtype):
     check_chunk_keys(inp, ck, cl, 8, out_dtype)
 
 
+@pytest.mark.parametrize("cs", [1, 3, 33, 1000, 4096])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_chunk_keys_chunk_sizes(cs, out_dtype):
+    # one row per chunk, odd sizes, and chunks longer than a sequence (the
+    # only chunk partial); the largest chunk size the C ABI takes
+    inp = synth.make_attn_inputs(lens=[5000, 1003, 1, 17], Hq=2, Hkv=2, dtype="bf16", seed=13, cap_extra=5)
+    ck, cl, _ = run_chunk_keys(inp, cs, out_dtype)
+    check_chunk_keys(inp, ck, cl, cs, out_dtype)
+
+
 def test_chunk_keys_partial_refresh():
     inp = synth.make_attn_inputs(lens=[1000, 64], Hq=2, Hkv=2, dtype="bf16", seed=11)
     ck, cl, _ = run_chunk_keys(inp, 16, "bf16", chunk_begin=[60, 2], max_chunks=3)
