@@ -321,8 +321,10 @@ def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape, dtype):
 # stream (Force 1)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,S,W", [("bf16", 4, 252), ("fp16", 4, 252), ("bf16", 0, 1), ("bf16", 2, 7)])
+@pytest.mark.parametrize("dtype,S,W", [("bf16", 4, 252), ("fp16", 4, 252), ("bf16", 0, 1), ("bf16", 2, 7),
+                                       ("bf16", 4, 1020), ("bf16", 16, 400)])
 def test_stream_parity(dtype, S, W):
+    # windows past 256 rows: three to eight tiles per wave
     lens = [4096, 1000, 100, 3, 256, 257, 1]
     s = synth.make_stream_inputs(lens=lens, Hq=8, Hkv=4, dtype=dtype, n_sink=S, window=W, seed=8)
     sd = desc(s.layout, dtype)
