@@ -886,11 +886,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
   } else if (kStaged && t < v1) {
     unsigned char* slab = s_stage + w * kStageBytes;
     const SlabSource<DT> src(slab, lane);
+    // (one stage in flight, so the wait before staging a tile is exact with or
+    // without a prefetch; none is requested past the range)
     Stage st;
     load_stage<MODE>(st, a, geo, t, v1, s_idx, chunk_lo, Kb, Vb, lane);
     unsigned mask = st.mask;
     write_stage(st, slab, lane);
-    load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+    if (t + 4 * kTile < v1) load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     while (true) {
       __builtin_amdgcn_sched_barrier(0);
       process_tile<DT, MODE, NQT>(src, mask, t, qreg, sel, lim, lim_min, tm, tbase, acc, m_run, l_run, c2, lq, lg);
@@ -898,7 +900,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int b, const 
       if (t >= v1) break;
       mask = st.mask;
       write_stage(st, slab, lane);
-      load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
+      if (t + 4 * kTile < v1) load_stage<MODE>(st, a, geo, t + 4 * kTile, v1, s_idx, chunk_lo, Kb, Vb, lane);
     }
   } else if (!kStaged && !kStaged2 && t < v1) {
     Tile<DT> A, B;
