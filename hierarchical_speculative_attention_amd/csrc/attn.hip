@@ -1116,23 +1116,27 @@ void attn_kernel(const AttnArgs a) {
 // Merge of the split partials of every (sequence, KV head, query row) whose
 // sequence needed more than one split: one wave per row, two dims per lane,
 // splits in order.  Runs as its own launch so that no device-wide fence is
-// needed inside the attention kernel.  Splits are taken in groups of 32: the
-// group's (max, sum) pairs and its 32 accumulator rows are all requested
-// before any is used, so a group costs one memory round trip; groups are
-// folded with an online rescale.  The first group is requested before the
+// needed inside the attention kernel.  Splits are taken in groups of GROUP
+// (4, 8, 16 or 32: the smallest that holds the plan's split count; 32 for a
+// batch on the equal-work grid): the group's (max, sum) pairs and its
+// accumulator rows are all requested before any is used, so a group costs
+// one memory round trip; groups are folded with an online rescale.  (Groups
+// of 32 for 16 splits requested 16 clamped duplicates per lane: the sparse
+// call at the Llama2-7B-128K shape took 0.6 us more, the 8-sequence batch's
+// 1.1 us more, outputs bitwise equal since the extra terms are zeros.)  The first group is requested before the
 // sequence geometry is known: every split index below the planned split count
 // lies inside the workspace, and splits past this sequence's own count are
 // dropped by selection (their contents are never combined arithmetically).
 // Lane s of the wave holds split s's (max, sum): the group's max is a
 // register reduction, lane s computes split s's weight (one exponential per
-// lane), and the (weight, sum) pairs reach every lane through 16 broadcast LDS
-// reads; the weighted sum and the accumulators are then folded in split
+// lane), and the (weight, sum) pairs reach every lane through GROUP / 2
+// broadcast LDS reads; the weighted sum and the accumulators are then folded in split
 // order.  (This replaced ~128 readlane broadcasts per group, each followed
 // by hazard waits: bit-identical results, the sparse call 19.92 -> 19.82 us.)
 
-template <int MODE, bool FLAT>
+template <int MODE, bool FLAT, int GROUP>
 __global__ __launch_bounds__(64) void combine_kernel(const AttnArgs a) {
-  constexpr int kGroup = 32;
+  constexpr int kGroup = GROUP;
   __shared__ __attribute__((aligned(16))) float2 s_el[kGroup];
   const int row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
@@ -1327,7 +1331,15 @@ static hipError_t launch_tiles(const AttnArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (!FLAT && a.nsplit == 1)) return e;
-  hipLaunchKernelGGL((combine_kernel<MODE, FLAT>), dim3(a.rows, a.Hkv, a.B), dim3(64), 0, stream, a);
+  const dim3 cgrid(a.rows, a.Hkv, a.B);
+  if (!FLAT && a.nsplit <= 4)
+    hipLaunchKernelGGL((combine_kernel<MODE, FLAT, 4>), cgrid, dim3(64), 0, stream, a);
+  else if (!FLAT && a.nsplit <= 8)
+    hipLaunchKernelGGL((combine_kernel<MODE, FLAT, 8>), cgrid, dim3(64), 0, stream, a);
+  else if (!FLAT && a.nsplit <= 16)
+    hipLaunchKernelGGL((combine_kernel<MODE, FLAT, 16>), cgrid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<MODE, FLAT, 32>), cgrid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
