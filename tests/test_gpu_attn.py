@@ -317,6 +317,47 @@ def test_sparse_calls_with_more_query_tiles(mode, Hq, Hkv, Q, shape, dtype):
         compare_attn(out, lse, *oracle_sparse_verify(inp, idx, cs, tail, Q))
 
 
+def verify_plan_splits(Hkv, n):
+    """Splits per KV head of one sequence's verification: one round of 512
+    workgroups, between 128 and 8192 rows each (the C ABI's plan, restated
+    without its short-last-split case, which these lengths do not reach)."""
+    per_head = 512 // Hkv
+    rounds = max(1, -(-n // (per_head * 8192)))
+    fit = -(-n // (per_head * rounds))
+    tpw = min(8192, max(128, -(-fit // 32) * 32))
+    return -(-n // tpw)
+
+
+@pytest.mark.parametrize("mode,Hkv,size,splits", [
+    ("verify", 128, 300, 3), ("verify", 128, 400, 4), ("verify", 64, 600, 5), ("verify", 64, 1000, 8),
+    ("verify", 32, 1100, 9), ("verify", 32, 2100, 14), ("verify", 16, 4200, 27),
+    ("sparse", 128, 1000, 4), ("sparse", 64, 1296, 6), ("sparse", 64, 2048, 8), ("sparse", 32, 3000, 12),
+])
+def test_split_merge_group_sizes(mode, Hkv, size, splits):
+    """The split merge takes each head's partials in one group of 4, 8, 16
+    or 32 (the smallest holding the plan's split count): 3 to 27 splits per
+    head, for verification (size = cache rows) and sparse attention (size =
+    gathered rows, chunks of 8)."""
+    if mode == "verify":
+        assert verify_plan_splits(Hkv, size) == splits
+        n = size
+    else:
+        assert -(-size // sparse_plan_tpw(1, Hkv, size)) == splits
+        n = size + 500
+    print(f"split merge: mode={mode} Hkv={Hkv} size={size} splits={splits}", flush=True)
+    inp = synth.make_attn_inputs(lens=[n], Hq=Hkv, Hkv=Hkv, dtype="bf16", Q=3, seed=94, cap_extra=3)
+    if mode == "verify":
+        out, lse = run_verify(inp, 3)
+        compare_attn(out, lse, *oracle_verify(inp, 3))
+    else:
+        cs, k = 8, size // 8
+        C = -(-n // cs)
+        rng = np.random.default_rng(size)
+        idx = np.stack([np.sort(rng.choice(C, size=k, replace=False)) for _ in range(Hkv)])[None]
+        out, lse = run_sparse(inp, idx, cs)
+        compare_attn(out, lse, *oracle_sparse(inp, idx, cs))
+
+
 # ---------------------------------------------------------------------------
 # stream (Force 1)
 # ---------------------------------------------------------------------------
