@@ -197,6 +197,23 @@ def test_topk_large_rows(C, k):
             assert np.array_equal(idx[b, g], oracle.select_topk(s[b, g, :n].astype(np.float64), k))
 
 
+@pytest.mark.parametrize("C,ks", [(1 << 20, [1, 2048, 100000]), (300001, [4096])])
+def test_topk_longest_rows(C, ks):
+    # rows past 65536 chunks up to the largest the C ABI takes (2^20): keys
+    # re-read from memory each pass; ties near the top, NaNs, a shorter row
+    rng = np.random.default_rng(C)
+    s = (rng.standard_normal((1, 2, C)) * 4).astype(np.float32)
+    s[0, :, rng.choice(C, 5000, replace=False)] = 9.0
+    s[0, 1, rng.choice(C, 300, replace=False)] = np.nan
+    print(f"top-k longest rows: C={C} ks={ks}", flush=True)
+    for k in ks:
+        for n in (C, C - 12345):
+            idx = run_topk(s, [n], k)
+            for g in range(2):
+                ref = oracle.select_topk(s[0, g, :n].astype(np.float64), k)
+                assert np.array_equal(idx[0, g], ref), (k, n, g)
+
+
 @pytest.mark.parametrize("C", [1500, 3001, 4096, 5003, 16384, 16448, 20001, 24576, 30000, 40000, 50001])
 def test_topk_value_spreads(C):
     """Rows whose k-th key sits in bins of every size: exponents spread so the
