@@ -180,3 +180,32 @@ def test_chain_lengths_bit_exact(gamma, T):
             continue
         assert (n[b], nxt[b]) == (rn, rnext), b
     assert guarded <= 1
+
+
+@pytest.mark.parametrize("gamma", [64, 1024])
+def test_long_chains_bit_exact(gamma):
+    """Chains of 64 and 1024 drafts (the C ABI's largest): two sequences whose
+    draft distribution equals the target's (every draft kept, the bonus drawn
+    from p at the end of the chain) and two with correlated drafts;
+    bit-exact against the oracle."""
+    B, V, T = 4, 1000, 1.0
+    a = synth.make_accept_inputs(B=B, gamma=gamma, vocab=V, correlated=True, seed=28 + gamma)
+    draft = a.draft.copy()
+    draft[:2] = a.target[:2, :gamma]
+    rng = np.random.default_rng(29)
+    tokens = a.tokens.copy()
+    for b in range(B):
+        for i in range(gamma):
+            q = oracle.distribution(draft[b, i], T)
+            tokens[b, i] = rng.choice(V, p=q / q.sum())
+    print(f"accept: B={B} gamma={gamma} V={V}", flush=True)
+    n, nxt = run(a.target, draft, tokens, a.uniforms, T)
+    guarded = 0
+    for b in range(B):
+        rn, rnext, margin = oracle.accept(a.target[b], draft[b], tokens[b], a.uniforms[b], T)
+        if margin < 1e-12:
+            guarded += 1
+            continue
+        assert (n[b], nxt[b]) == (rn, rnext), b
+    assert n[0] == gamma and n[1] == gamma
+    assert guarded == 0
