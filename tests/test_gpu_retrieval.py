@@ -95,9 +95,12 @@ def run_scores(inp, ck, ckd, c_max):
     return s
 
 
-@pytest.mark.parametrize("Hq,Hkv,ck_dtype", [(8, 8, "bf16"), (8, 2, "bf16"), (8, 2, "fp32"), (4, 4, "fp16")])
-def test_scores_parity(Hq, Hkv, ck_dtype):
-    dtype = "fp16" if ck_dtype == "fp16" else "bf16"
+@pytest.mark.parametrize("Hq,Hkv,ck_dtype,dtype", [(8, 8, "bf16", "bf16"), (8, 2, "bf16", "bf16"), (8, 2, "fp32", "bf16"),
+                                                  (4, 4, "fp16", "fp16"), (8, 2, "fp32", "fp16"), (64, 1, "bf16", "bf16"),
+                                                  (32, 4, "fp32", "bf16")])
+def test_scores_parity(Hq, Hkv, ck_dtype, dtype):
+    # keys and queries in bf16 or fp16, chunk keys in the same dtype or fp32,
+    # 1 to 64 query heads per KV head
     inp = synth.make_attn_inputs(lens=[4096, 777, 9], Hq=Hq, Hkv=Hkv, dtype=dtype, seed=12,
                                  plant="count", plant_count=4)
     ck, cl, ckd = run_chunk_keys(inp, 8, ck_dtype)
