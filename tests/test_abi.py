@@ -259,3 +259,28 @@ def test_verify_noalloc_validates_before_any_device_call():
     assert L.tf_verify_attn_noalloc(FAKE, 4, 5, FAKE, FAKE, None, FAKE, None, None) == T.TF_ERR_INVALID_ARG
     empty = desc(B=0, H=4, max_len=0)
     assert L.tf_verify_attn_noalloc(None, 4, 5, None, None, ctypes.byref(empty), None, None, None) == T.TF_OK
+
+
+def plan_bytes(heads, nsplit, rows):
+    """Workspace of a split plan: (max, sum) pairs (rounded up to 256 bytes)
+    and 128-float accumulator rows per (head, split, padded query row); none
+    with one split."""
+    if nsplit <= 1:
+        return 0
+    parts = heads * nsplit * (-(-rows // 16) * 16)
+    return ((parts * 8 + 255) // 256) * 256 + parts * 512
+
+
+def test_split_counts_of_the_gpu_tests_are_the_librarys():
+    """The GPU tests assert which split-plan regime a shape falls in with a
+    Python restatement of the plan; the library's workspace sizes for those
+    shapes follow from the same split counts."""
+    from tests.test_gpu_attn import sparse_plan_tpw, verify_plan_splits
+    L = T.lib()
+    for Hkv, n in [(128, 300), (128, 400), (64, 600), (64, 1000), (32, 1100), (32, 2100), (16, 4200), (4, 20000)]:
+        ns = verify_plan_splits(Hkv, n)
+        assert L.tf_verify_attn_workspace_size(1, Hkv, Hkv, 3, n) == plan_bytes(Hkv, ns, 3), (Hkv, n)
+    for B, Hkv, G, k, cs in [(1, 128, 1, 125, 8), (1, 64, 1, 162, 8), (1, 32, 1, 375, 8), (2, 4, 2, 300, 8),
+                             (1, 16, 1, 1500, 8), (80, 8, 2, 40, 8), (1, 1, 4, 2000, 8), (1, 1, 2, 16500, 8)]:
+        ns = -(-(k * cs) // sparse_plan_tpw(B, Hkv, k * cs))
+        assert L.tf_sparse_attn_workspace_size(B, G * Hkv, Hkv, k, cs) == plan_bytes(B * Hkv, ns, G), (B, Hkv, k)
